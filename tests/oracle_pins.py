@@ -1,0 +1,476 @@
+"""Pins of the float64 oracle against facts fixed by the mathematics.
+
+Each ``pin_*`` returns True when the oracle (passed in as a module-like
+object, so a test can plant a mistake in a copy of it) agrees with something
+other than itself: brute-force loops, a closed form, an invariant, or a
+library routine that computes the same well-defined quantity.
+"""
+from __future__ import annotations
+
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+
+class Geo:
+    """Minimal layer description the oracle reads."""
+
+    def __init__(self, kind="linear", has_bias=False, k=1, stride=1, pad=0):
+        self.kind, self.has_bias, self.k, self.stride, self.pad = kind, has_bias, k, stride, pad
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester construction: H_1 = [1], H_2m = [[H, H], [H, -H]]; H^T H = n I."""
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+# ---------------------------------------------------------------------------
+# unfold
+
+def pin_unfold_direct_conv(O, seed=0) -> bool:
+    """U . W_flat^T equals a convolution written as explicit loops."""
+    rng = np.random.default_rng(seed)
+    B, C, H, W, Co, k, s, p = 2, 3, 5, 5, 4, 3, 2, 1
+    x = rng.standard_normal((B, C, H, W))
+    w = rng.standard_normal((Co, C, k, k))
+    Ho = (H + 2 * p - k) // s + 1
+    Wo = (W + 2 * p - k) // s + 1
+    ref = np.zeros((B, Co, Ho, Wo))
+    for b, o, ho, wo in itertools.product(range(B), range(Co), range(Ho), range(Wo)):
+        acc = 0.0
+        for c, kh, kw in itertools.product(range(C), range(k), range(k)):
+            hi, wi = ho * s - p + kh, wo * s - p + kw
+            if 0 <= hi < H and 0 <= wi < W:
+                acc += x[b, c, hi, wi] * w[o, c, kh, kw]
+        ref[b, o, ho, wo] = acc
+    U = O.unfold(x, k, s, p)
+    got = (U @ w.reshape(Co, -1).T).reshape(B, Ho, Wo, Co).transpose(0, 3, 1, 2)
+    return U.shape == (B * Ho * Wo, C * k * k) and np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_unfold_library(O, seed=1) -> bool:
+    """Same columns and rows as the library im2col (torch unfold, float64 CPU)."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for (B, C, H, W, k, s, p) in [(2, 3, 7, 6, 3, 2, 1), (1, 2, 9, 9, 7, 2, 3), (3, 4, 5, 5, 1, 2, 0),
+                                  (2, 3, 6, 6, 3, 1, 1)]:
+        x = rng.standard_normal((B, C, H, W))
+        ref = torch.nn.functional.unfold(torch.from_numpy(x), k, padding=p, stride=s)  # [B, Ckk, L]
+        ref = ref.permute(0, 2, 1).reshape(-1, C * k * k).numpy()
+        got = O.unfold(x, k, s, p)
+        ok &= got.shape == ref.shape and np.array_equal(got, ref)
+    return bool(ok)
+
+
+# ---------------------------------------------------------------------------
+# factors
+
+def pin_factor_outer_products(O, seed=2) -> bool:
+    """A-hat = (1/N) sum_n a_n a_n^T by an explicit loop; symmetric, PSD, and
+    trace(A-hat) = mean squared row norm."""
+    rng = np.random.default_rng(seed)
+    N, d = 13, 6
+    a = rng.standard_normal((N, d))
+    ref = np.zeros((d, d))
+    for n in range(N):
+        for i in range(d):
+            for j in range(d):
+                ref[i, j] += a[n, i] * a[n, j]
+    ref /= N
+    got = O.kronecker_factor(a)
+    ev = np.linalg.eigvalsh(got)
+    return (np.allclose(got, ref, rtol=1e-13, atol=1e-13) and np.array_equal(got, got.T)
+            and ev.min() >= -1e-12 * np.abs(ev).max()
+            and np.isclose(np.trace(got), (a * a).sum(axis=1).mean(), rtol=1e-13))
+
+
+def pin_factor_hadamard(O) -> bool:
+    """Rows taken from a Sylvester-Hadamard matrix give A-hat = I exactly; with a
+    bias the appended ones column is column 0 of H, i.e. the activations are
+    columns 1..d_in of H and the factor is still I (a_bar = [a | 1])."""
+    N, d_in = 32, 11
+    H = hadamard(N)
+    geo = Geo("linear", has_bias=True)
+    a = H[:, 1:1 + d_in]
+    g = 0.5 * H[:, 1:6]
+    abar, grows = O.layer_rows(geo, a.astype(np.float32), g.astype(np.float32))
+    A = O.kronecker_factor(abar)
+    G = O.kronecker_factor(grows)
+    return (abar.shape == (N, d_in + 1) and np.array_equal(abar[:, -1], np.ones(N))
+            and np.array_equal(A, np.eye(d_in + 1)) and np.array_equal(G, 0.25 * np.eye(5)))
+
+
+def pin_bias_column(O, seed=3) -> bool:
+    """Last row/column of A-hat with a bias: the column means of a, and 1."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((20, 4)).astype(np.float32)
+    g = rng.standard_normal((20, 3)).astype(np.float32)
+    abar, _ = O.layer_rows(Geo("linear", has_bias=True), a, g)
+    A = O.kronecker_factor(abar)
+    m = a.astype(np.float64).mean(axis=0)
+    return np.allclose(A[-1, :-1], m, rtol=1e-13, atol=1e-15) and np.allclose(A[:-1, -1], m) and A[-1, -1] == 1.0
+
+
+def pin_conv_rows(O, seed=4) -> bool:
+    """Convolution G rows: one row per (sample, output position), channel as
+    column, in the same order as the unfold rows: checked by the gradient
+    identity grad_W = g_rows^T U / N against an explicit loop over the
+    convolution's input/output positions."""
+    rng = np.random.default_rng(seed)
+    B, C, H, W, Co, k, s, p = 2, 2, 5, 4, 3, 3, 2, 1
+    x = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    Ho, Wo = (H + 2 * p - k) // s + 1, (W + 2 * p - k) // s + 1
+    g = rng.standard_normal((B, Co, Ho, Wo)).astype(np.float32)
+    U, grows = O.layer_rows(Geo("conv", False, k, s, p), x, g)
+    gw = grows.T @ U
+    ref = np.zeros((Co, C, k, k))
+    for b, o, ho, wo, c, kh, kw in itertools.product(range(B), range(Co), range(Ho), range(Wo), range(C),
+                                                     range(k), range(k)):
+        hi, wi = ho * s - p + kh, wo * s - p + kw
+        if 0 <= hi < H and 0 <= wi < W:
+            ref[o, c, kh, kw] += float(g[b, o, ho, wo]) * float(x[b, c, hi, wi])
+    return grows.shape == (B * Ho * Wo, Co) and np.allclose(gw, ref.reshape(Co, -1), rtol=1e-12, atol=1e-12)
+
+
+def pin_bf16_widen(O) -> bool:
+    """bf16 patterns widen to the float32 whose upper half they are."""
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x3E00, 0x7F7F], np.uint16)
+    ref = np.array([1.0, -1.0, 3.140625, 0.0, -0.0, 0.125, 3.3895313892515355e38])
+    got = O.widen(bits)
+    return got.dtype == np.float64 and np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# EMA
+
+def pin_ema_closed_form(O) -> bool:
+    """Constant input X: A_t = eps^t A_0 + (1 - eps^t) X; eps = 0 gives X,
+    eps = 1 keeps A_0."""
+    rng = np.random.default_rng(5)
+    A0 = np.eye(4)
+    X = rng.standard_normal((4, 4))
+    X = X @ X.T
+    ok = True
+    for eps in (0.95, 0.5, 0.0, 1.0):
+        A = A0
+        for t in range(1, 8):
+            A = O.ema(A, X, eps)
+            ok &= np.allclose(A, eps ** t * A0 + (1 - eps ** t) * X, rtol=1e-12, atol=1e-14)
+    return bool(ok)
+
+
+# ---------------------------------------------------------------------------
+# damped inverse
+
+def pin_inverse_sherman_morrison(O) -> bool:
+    """N = 1: (a a^T + lam I)^-1 = (1/lam)(I - a a^T / (lam + |a|^2))."""
+    rng = np.random.default_rng(6)
+    ok = True
+    for d, lam in ((5, 1e-3), (9, 0.5), (1, 2.0)):
+        a = rng.standard_normal(d)
+        ref = (np.eye(d) - np.outer(a, a) / (lam + a @ a)) / lam
+        got = O.damped_inverse(O.kronecker_factor(a[None, :]), lam)
+        ok &= np.allclose(got, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+    return bool(ok)
+
+
+def pin_inverse_diagonal_and_residual(O) -> bool:
+    """Diagonal F: 1/(f_ii + lam); general SPD: (F + lam I) X = I and X equals
+    the library's general inverse."""
+    rng = np.random.default_rng(7)
+    f = rng.uniform(0.0, 3.0, 7)
+    ok = np.allclose(O.damped_inverse(np.diag(f), 0.25), np.diag(1.0 / (f + 0.25)), rtol=1e-14)
+    a = rng.standard_normal((40, 12))
+    F = a.T @ a / 40
+    X = O.damped_inverse(F, 1e-3)
+    M = F + 1e-3 * np.eye(12)
+    ok &= np.allclose(M @ X, np.eye(12), atol=1e-10)
+    ok &= np.allclose(X, np.linalg.inv(M), rtol=1e-9, atol=1e-9 * np.abs(X).max())
+    ok &= np.array_equal(X, X.T)
+    return bool(ok)
+
+
+def pin_inverse_not_pd_raises(O) -> bool:
+    F = np.diag([1.0, -1.0, 2.0])
+    try:
+        O.damped_inverse(F, 0.5)
+    except np.linalg.LinAlgError:
+        return True
+    return False
+
+
+# ---------------------------------------------------------------------------
+# preconditioning
+
+def pin_kronecker_identity(O, seed=8) -> bool:
+    """((G + lam I) kron (A + lam I))^-1 vec_r(grad) = vec_r(G_inv grad A_inv),
+    with the explicit Kronecker product and a dense solve (row-major vec)."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for dg, da, lam in ((3, 5, 1e-2), (6, 7, 0.3), (4, 4, 1e-3), (1, 6, 1.0)):
+        a = rng.standard_normal((11, da))
+        g = rng.standard_normal((9, dg))
+        A = O.kronecker_factor(a)
+        G = O.kronecker_factor(g)
+        grad = rng.standard_normal((dg, da))
+        big = np.kron(G + lam * np.eye(dg), A + lam * np.eye(da))
+        ref = np.linalg.solve(big, grad.reshape(-1)).reshape(dg, da)
+        got = O.precondition(O.damped_inverse(G, lam), grad, O.damped_inverse(A, lam))
+        ok &= np.allclose(got, ref, rtol=1e-8, atol=1e-8 * np.abs(ref).max())
+    return bool(ok)
+
+
+def pin_full_step_hadamard(O) -> bool:
+    """Hadamard rows with eps = 0: A-hat = I, G-hat = c I, so the first step's
+    direction is grad / ((1 + lam)(c + lam)), and with V0 = 0 the update is
+    W1 = W0 - lr (P + wd W0)."""
+    N, d_in, d_out, c, lam = 64, 9, 5, 0.25, 0.1
+    H = hadamard(N)
+    geo = Geo("linear", has_bias=True)
+    rng = np.random.default_rng(9)
+    st = {"w": rng.standard_normal((d_out, d_in)), "b": rng.standard_normal(d_out),
+          "mom_w": np.zeros((d_out, d_in)), "mom_b": np.zeros(d_out),
+          "A": np.eye(d_in + 1), "G": np.eye(d_out), "A_inv": np.zeros((d_in + 1,) * 2),
+          "G_inv": np.zeros((d_out,) * 2)}
+    inp = {"a": H[:, 1:1 + d_in], "g": np.sqrt(c) * H[:, 1:1 + d_out],
+           "grad_w": rng.standard_normal((d_out, d_in)), "grad_b": rng.standard_normal(d_out)}
+    hp = {"lr": 0.1, "momentum": 0.9, "weight_decay": 5e-4, "ema_decay": 0.0, "damping": lam}
+    out, flags = O.step_full(geo, st, inp, hp, refresh=True)
+    gaug = np.concatenate([inp["grad_w"], inp["grad_b"][:, None]], 1)
+    waug = np.concatenate([st["w"], st["b"][:, None]], 1)
+    P = gaug / ((1 + lam) * (c + lam))
+    W1 = waug - 0.1 * (P + 5e-4 * waug)
+    got = np.concatenate([out["w"], out["b"][:, None]], 1)
+    return flags == 0 and np.allclose(out["P"], P, rtol=1e-12) and np.allclose(got, W1, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# update
+
+def _sgd_loop(w0, grads, lr, mu, wd):
+    """Plain SGD with heavy-ball momentum and L2 weight decay, element by element."""
+    w = [list(r) for r in w0]
+    v = [[0.0] * len(r) for r in w0]
+    for gr in grads:
+        for i in range(len(w)):
+            for j in range(len(w[i])):
+                d = gr[i][j] + wd * w[i][j]
+                v[i][j] = mu * v[i][j] + d
+                w[i][j] = w[i][j] - lr * v[i][j]
+    return np.array(w)
+
+
+def pin_sgd_reduction(O, seed=10) -> bool:
+    """eps = 0 with identity inverses kept (no refresh): the full step is SGD
+    with momentum and weight decay -- equal to an element-wise loop and to
+    torch.optim.SGD (float64, CPU) over several steps."""
+    rng = np.random.default_rng(seed)
+    d_out, d_in, T = 3, 4, 5
+    geo = Geo("linear", has_bias=True)
+    w0 = rng.standard_normal((d_out, d_in))
+    b0 = rng.standard_normal(d_out)
+    st = {"w": w0, "b": b0, "mom_w": np.zeros_like(w0), "mom_b": np.zeros_like(b0),
+          "A": np.eye(d_in + 1), "G": np.eye(d_out), "A_inv": np.eye(d_in + 1), "G_inv": np.eye(d_out)}
+    hp = {"lr": 0.1, "momentum": 0.9, "weight_decay": 5e-4, "ema_decay": 0.0, "damping": 1e-3}
+    grads = []
+    p = torch.tensor(np.concatenate([w0, b0[:, None]], 1), requires_grad=True)
+    opt = torch.optim.SGD([p], lr=0.1, momentum=0.9, weight_decay=5e-4)
+    for t in range(T):
+        inp = {"a": rng.standard_normal((7, d_in)), "g": rng.standard_normal((7, d_out)),
+               "grad_w": rng.standard_normal((d_out, d_in)), "grad_b": rng.standard_normal(d_out)}
+        gaug = np.concatenate([inp["grad_w"], inp["grad_b"][:, None]], 1)
+        grads.append(gaug.tolist())
+        out, _ = O.step_full(geo, st, inp, hp, refresh=False)
+        st = dict(st, **{k: out[k] for k in ("w", "b", "mom_w", "mom_b", "A", "G")})
+        p.grad = torch.tensor(gaug)
+        opt.step()
+    got = np.concatenate([st["w"], st["b"][:, None]], 1)
+    ref = _sgd_loop(np.concatenate([w0, b0[:, None]], 1).tolist(), grads, 0.1, 0.9, 5e-4)
+    return np.allclose(got, ref, rtol=1e-13, atol=1e-15) and np.allclose(got, p.detach().numpy(), rtol=1e-13)
+
+
+def pin_momentum_constant_direction(O) -> bool:
+    """Constant D and wd = 0: V_t = D (1 - mu^t) / (1 - mu)."""
+    D = np.array([[1.0, -2.0], [0.5, 3.0]])
+    w, v = np.zeros((2, 2)), np.zeros((2, 2))
+    ok = True
+    for t in range(1, 10):
+        w, v = O.momentum_update(w, v, D, 0.1, 0.9, 0.0)
+        ok &= np.allclose(v, D * (1 - 0.9 ** t) / (1 - 0.9), rtol=1e-13)
+    return bool(ok)
+
+
+# ---------------------------------------------------------------------------
+# diagonal variant
+
+def pin_diag_is_factor_diagonal(O, seed=11) -> bool:
+    """dA = diag(A-hat), dG = diag(G-hat) for linear and conv layers; the
+    per-parameter product dG[o] dA[j] is the diagonal of G-hat kron A-hat in
+    row-major [d_out, d_a] order."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    cases = [(Geo("linear", True), rng.standard_normal((15, 6)), rng.standard_normal((15, 4))),
+             (Geo("conv", False, 3, 2, 1), rng.standard_normal((2, 3, 7, 6)), rng.standard_normal((2, 4, 4, 3))),
+             (Geo("conv", True, 1, 1, 0), rng.standard_normal((2, 3, 4, 4)), rng.standard_normal((2, 5, 4, 4)))]
+    for geo, a, g in cases:
+        dA, dG = O.diag_factors(geo, a, g)
+        abar, grows = O.layer_rows(geo, a, g)
+        A, G = O.kronecker_factor(abar), O.kronecker_factor(grows)
+        ok &= np.allclose(dA, np.diag(A), rtol=1e-13) and np.allclose(dG, np.diag(G), rtol=1e-13)
+        ok &= np.allclose(np.diag(np.kron(G, A)).reshape(len(dG), len(dA)), np.outer(dG, dA), rtol=1e-13)
+    return bool(ok)
+
+
+def pin_diag_conv_window_sums(O, seed=12) -> bool:
+    """Conv dA[c, kh, kw] = (1/N) sum over samples and output positions of
+    x[b, c, ho*s - p + kh, wo*s - p + kw]^2 (zero outside), by loops."""
+    rng = np.random.default_rng(seed)
+    B, C, H, W, Co, k, s, p = 2, 2, 7, 5, 3, 3, 2, 1
+    x = rng.standard_normal((B, C, H, W))
+    Ho, Wo = (H + 2 * p - k) // s + 1, (W + 2 * p - k) // s + 1
+    g = rng.standard_normal((B, Co, Ho, Wo))
+    dA, dG = O.diag_factors(Geo("conv", False, k, s, p), x, g)
+    N = B * Ho * Wo
+    ref = np.zeros((C, k, k))
+    for b, c, kh, kw, ho, wo in itertools.product(range(B), range(C), range(k), range(k), range(Ho), range(Wo)):
+        hi, wi = ho * s - p + kh, wo * s - p + kw
+        if 0 <= hi < H and 0 <= wi < W:
+            ref[c, kh, kw] += x[b, c, hi, wi] ** 2
+    refG = np.array([(g[:, o] ** 2).sum() for o in range(Co)]) / N
+    return np.allclose(dA, ref.reshape(-1) / N, rtol=1e-13) and np.allclose(dG, refG, rtol=1e-13)
+
+
+def pin_diag_step_closed_form(O, seed=13) -> bool:
+    """beta = 0: F = dG dA^T, P = grad / (F + lam) element by element; beta = 1
+    with F0 = 1 - lam: P = grad, and steps reduce to the SGD loop."""
+    rng = np.random.default_rng(seed)
+    geo = Geo("linear", True)
+    d_in, d_out, N = 5, 3, 8
+    a = rng.standard_normal((N, d_in))
+    g = rng.standard_normal((N, d_out))
+    w0, b0 = rng.standard_normal((d_out, d_in)), rng.standard_normal(d_out)
+    gw, gb = rng.standard_normal((d_out, d_in)), rng.standard_normal(d_out)
+    st = {"w": w0, "b": b0, "mom_w": np.zeros_like(w0), "mom_b": np.zeros_like(b0),
+          "F_w": np.full_like(w0, 7.0), "F_b": np.full_like(b0, 7.0)}
+    inp = {"a": a, "g": g, "grad_w": gw, "grad_b": gb}
+    lam = 1e-2
+    out, _ = O.step_diag(geo, st, inp, {"lr": 0.1, "momentum": 0.9, "weight_decay": 0.0,
+                                        "ema_decay": 0.0, "damping": lam})
+    ok = True
+    for o in range(d_out):
+        for j in range(d_in + 1):
+            dAj = np.mean(a[:, j] ** 2) if j < d_in else 1.0
+            dGo = np.mean(g[:, o] ** 2)
+            gr = gw[o, j] if j < d_in else gb[o]
+            ok &= np.isclose(out["P"][o, j], gr / (dGo * dAj + lam), rtol=1e-12)
+    # SGD reduction
+    st = dict(st, F_w=np.full_like(w0, 1 - lam), F_b=np.full_like(b0, 1 - lam))
+    hp = {"lr": 0.05, "momentum": 0.9, "weight_decay": 5e-4, "ema_decay": 1.0, "damping": lam}
+    grads = []
+    for t in range(4):
+        gw, gb = rng.standard_normal((d_out, d_in)), rng.standard_normal(d_out)
+        grads.append(np.concatenate([gw, gb[:, None]], 1).tolist())
+        out, _ = O.step_diag(geo, st, {"a": a, "g": g, "grad_w": gw, "grad_b": gb}, hp)
+        st = dict(st, **{k: out[k] for k in ("w", "b", "mom_w", "mom_b", "F_w", "F_b")})
+    ref = _sgd_loop(np.concatenate([w0, b0[:, None]], 1).tolist(), grads, 0.05, 0.9, 5e-4)
+    ok &= np.allclose(np.concatenate([st["w"], st["b"][:, None]], 1), ref, rtol=1e-12, atol=1e-15)
+    return bool(ok)
+
+
+def pin_refresh_keeps_inverses(O) -> bool:
+    """Without a refresh the previous inverses are used unchanged; a factor that
+    is not positive definite keeps its inverse and raises the NOT_PD flag."""
+    rng = np.random.default_rng(14)
+    geo = Geo("linear", False)
+    st = {"w": rng.standard_normal((2, 3)), "mom_w": np.zeros((2, 3)),
+          "A": np.diag([1.0, -5.0, 1.0]), "G": np.eye(2),
+          "A_inv": 2 * np.eye(3), "G_inv": 3 * np.eye(2)}
+    inp = {"a": np.zeros((4, 3)), "g": np.zeros((4, 2)), "grad_w": np.ones((2, 3))}
+    hp = {"lr": 0.1, "momentum": 0.0, "weight_decay": 0.0, "ema_decay": 1.0, "damping": 0.1}
+    out, flags = O.step_full(geo, st, inp, hp, refresh=False)
+    ok = flags == 0 and np.array_equal(out["P"], 6 * np.ones((2, 3)))
+    out, flags = O.step_full(geo, st, inp, hp, refresh=True)
+    ok &= flags == O.FLAG_NOT_PD and np.array_equal(out["A_inv"], 2 * np.eye(3))
+    ok &= np.allclose(out["G_inv"], np.eye(2) / 1.1)
+    return bool(ok)
+
+
+def _gauss_jordan_inverse(M):
+    """Exact inverse of a small rational matrix (Gauss-Jordan with row swaps)."""
+    n = len(M)
+    aug = [list(M[i]) + [Fraction(int(i == j)) for j in range(n)] for i in range(n)]
+    for c in range(n):
+        piv = next(r for r in range(c, n) if aug[r][c] != 0)
+        aug[c], aug[piv] = aug[piv], aug[c]
+        pv = aug[c][c]
+        aug[c] = [x / pv for x in aug[c]]
+        for r in range(n):
+            if r != c and aug[r][c] != 0:
+                f = aug[r][c]
+                aug[r] = [x - f * y for x, y in zip(aug[r], aug[c])]
+    return [row[n:] for row in aug]
+
+
+def _mm(X, Y):
+    return [[sum(X[i][k] * Y[k][j] for k in range(len(Y))) for j in range(len(Y[0]))] for i in range(len(X))]
+
+
+def pin_full_step_exact_rational(O) -> bool:
+    """Two whole steps of a tiny biased linear layer in exact rational
+    arithmetic: outer-product sums, the EMA, damped inverses by Gauss-Jordan
+    elimination (not Cholesky), the two-sided product, weight decay and
+    momentum, in the step order the pages give.  The float64 oracle must agree
+    to rounding."""
+    F = Fraction
+    eps, lam, lr, mu, wd = F(1, 2), F(1, 10), F(1, 4), F(9, 10), F(1, 20)
+    a_steps = [[[1, 2], [3, -1], [0, 1]], [[2, 0], [-1, 1], [1, 1]]]
+    g_steps = [[[1, -1], [2, 0], [0, 3]], [[1, 1], [-2, 1], [1, 0]]]
+    gw_steps = [[[1, 2, -1], [0, 1, 3]], [[-1, 0, 2], [1, 1, 1]]]
+    W = [[F(1), F(-2), F(1, 2)], [F(3), F(0), F(-1)]]
+    V = [[F(0)] * 3 for _ in range(2)]
+    A = [[F(int(i == j)) for j in range(3)] for i in range(3)]
+    G = [[F(int(i == j)) for j in range(2)] for i in range(2)]
+    st = {"w": np.array([[1.0, -2.0], [3.0, 0.0]]), "b": np.array([0.5, -1.0]),
+          "mom_w": np.zeros((2, 2)), "mom_b": np.zeros(2), "A": np.eye(3), "G": np.eye(2),
+          "A_inv": np.zeros((3, 3)), "G_inv": np.zeros((2, 2))}
+    hp = {"lr": 0.25, "momentum": 0.9, "weight_decay": 0.05, "ema_decay": 0.5, "damping": 0.1}
+    ok = True
+    for t in range(2):
+        abar = [[F(x) for x in row] + [F(1)] for row in a_steps[t]]
+        g = [[F(x) for x in row] for row in g_steps[t]]
+        N = len(abar)
+        Ahat = [[sum(abar[n][i] * abar[n][j] for n in range(N)) / N for j in range(3)] for i in range(3)]
+        Ghat = [[sum(g[n][i] * g[n][j] for n in range(N)) / N for j in range(2)] for i in range(2)]
+        A = [[eps * A[i][j] + (1 - eps) * Ahat[i][j] for j in range(3)] for i in range(3)]
+        G = [[eps * G[i][j] + (1 - eps) * Ghat[i][j] for j in range(2)] for i in range(2)]
+        Ai = _gauss_jordan_inverse([[A[i][j] + (lam if i == j else 0) for j in range(3)] for i in range(3)])
+        Gi = _gauss_jordan_inverse([[G[i][j] + (lam if i == j else 0) for j in range(2)] for i in range(2)])
+        Pm = _mm(_mm(Gi, [[F(x) for x in r] for r in gw_steps[t]]), Ai)
+        for i in range(2):
+            for j in range(3):
+                d = Pm[i][j] + wd * W[i][j]
+                V[i][j] = mu * V[i][j] + d
+                W[i][j] = W[i][j] - lr * V[i][j]
+        gw = np.array(gw_steps[t], np.float64)
+        inp = {"a": np.array(a_steps[t], np.float64), "g": np.array(g_steps[t], np.float64),
+               "grad_w": gw[:, :2], "grad_b": gw[:, 2]}
+        out, flags = O.step_full(Geo("linear", True), st, inp, hp, refresh=True)
+        st = dict(st, **{k: out[k] for k in ("w", "b", "mom_w", "mom_b", "A", "G", "A_inv", "G_inv")})
+        Wf = np.array([[float(x) for x in r] for r in W])
+        got = np.concatenate([st["w"], st["b"][:, None]], 1)
+        ok &= flags == 0 and np.allclose(got, Wf, rtol=1e-13, atol=1e-14)
+        ok &= np.allclose(st["A_inv"], np.array([[float(x) for x in r] for r in Ai]), rtol=1e-12, atol=1e-13)
+    return bool(ok)
+
+
+ALL_PINS = [pin_full_step_exact_rational, pin_unfold_direct_conv, pin_unfold_library, pin_factor_outer_products, pin_factor_hadamard,
+            pin_bias_column, pin_conv_rows, pin_bf16_widen, pin_ema_closed_form,
+            pin_inverse_sherman_morrison, pin_inverse_diagonal_and_residual, pin_inverse_not_pd_raises,
+            pin_kronecker_identity, pin_full_step_hadamard, pin_sgd_reduction,
+            pin_momentum_constant_direction, pin_diag_is_factor_diagonal, pin_diag_conv_window_sums,
+            pin_diag_step_closed_form, pin_refresh_keeps_inverses]
