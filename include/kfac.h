@@ -1,0 +1,189 @@
+/*
+ * kfac.h -- C ABI of the MI355X (gfx950) K-FAC optimizer-step library.
+ *
+ * One optimizer step for a stack of layers, run on one GPU by hand-written
+ * HIP kernels.  Two methods are provided:
+ *
+ *   kfac_step_full  K-FAC (Osawa et al., "Large-Scale Distributed
+ *                   Second-Order Optimization Using Kronecker-Factored
+ *                   Approximate Curvature for Deep Convolutional Neural
+ *                   Networks", section 3.2): per layer, Kronecker factors
+ *                   A = a^T a / N from the layer's inputs and G = g^T g / N from
+ *                   its output gradients, an exponential moving average of
+ *                   each, damped inverses (A + lambda I)^-1 and
+ *                   (G + lambda I)^-1 (section 4.2: damping) refreshed when the
+ *                   caller asks (sections 1 and 5.4: refreshed less often than
+ *                   every step), the direction P = G^-1 grad_W A^-1, then
+ *                   momentum, weight decay and the in-place parameter write.
+ *
+ *   kfac_step_diag  the AdaFisher-style diagonal variant (CAFIN briefing,
+ *                   "Introduction" and "Kernel Fusion Strategy"): per-parameter
+ *                   EMA of dG[o] * dA[j] (the diagonal of G kron A), division of
+ *                   the gradient by (F + lambda), momentum, weight decay and the
+ *                   parameter write, fused into one elementwise pass.
+ *
+ * Per step and layer (both methods; W, V, grad are the bias-augmented
+ * [d_out x d_a] matrices [W | b] etc., the bias as the last column):
+ *     D = P + weight_decay * W;   V = momentum * V + D;   W = W - lr * V
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers inside kfac_layer_t are DEVICE pointers to
+ *    contiguous, 16-byte aligned buffers owned by the caller.  The library
+ *    keeps no pointer after a call returns and frees nothing of the caller's.
+ *  - `workspace` is a device buffer of at least kfac_workspace_size() bytes,
+ *    256-byte aligned, owned by the caller.  One workspace must not be used
+ *    by two calls that can run at the same time; its first 256 bytes hold the
+ *    sticky device flag word (see kfac_read_flags) and must be zeroed by the
+ *    caller once before first use (the library never clears it on its own).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  The step entry
+ *    points only enqueue work on it and return; they never synchronise.
+ *  - Arguments are validated on the host before anything is enqueued: on any
+ *    error status no kernel runs and no buffer is touched.
+ *  - Numerical trouble (a damped factor that is not positive definite, a
+ *    non-finite parameter) is reported through device flags, never through a
+ *    return code, because it is only known once the kernels have run.
+ *  - Calls on different workspaces and streams may be made from different
+ *    host threads.
+ */
+#ifndef KFAC_H
+#define KFAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KFAC_ABI_VERSION 1
+
+typedef int32_t kfac_status_t;
+enum {
+  KFAC_OK = 0,
+  KFAC_ERR_ARG = 1,          /* null pointer, bad count, inconsistent shape */
+  KFAC_ERR_DTYPE = 2,        /* dtype code not supported for that operand */
+  KFAC_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned (workspace: 256) */
+  KFAC_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  KFAC_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement */
+  KFAC_ERR_HIP = 6           /* a HIP launch or runtime call failed */
+};
+
+/* layer kinds */
+enum { KFAC_LINEAR = 0, KFAC_CONV2D = 1 };
+/* element types of a / g (every other tensor is float32) */
+enum { KFAC_F32 = 0, KFAC_BF16 = 1 };
+/* kfac_workspace_size modes */
+enum { KFAC_MODE_FULL = 0, KFAC_MODE_DIAG = 1 };
+/* kfac_hparams_t.phase_mask bits; 0 means all phases.
+ *   full: FACTORS = factor construction + EMA, INVERT = damped inverses
+ *         (only when refresh != 0), UPDATE = precondition + momentum/decay/write
+ *   diag: FACTORS = the streaming reduction of a and g (sums of squares) into
+ *         the workspace; UPDATE = dA/dG formed from that reduction (written to
+ *         the descriptor's dA/dG) followed by the fused elementwise step.  An
+ *         UPDATE-only call reads the reduction the last FACTORS call on the
+ *         same workspace and layers left there. */
+enum { KFAC_PHASE_FACTORS = 1, KFAC_PHASE_INVERT = 2, KFAC_PHASE_UPDATE = 4, KFAC_PHASE_ALL = 7 };
+/* sticky device flags */
+enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
+
+/*
+ * One layer.  Shapes (row-major, contiguous):
+ *   linear : a [rows, d_in]           g [rows, d_out]          rows = N
+ *   conv2d : a [batch, c_in, height, width]   g [batch, d_out, h_out, w_out] (NCHW)
+ *            d_in = c_in * kh * kw (weights [d_out, c_in, kh, kw] flattened in
+ *            (c, kh, kw) order), h_out = (height + 2 pad - kh) / stride + 1 (same for
+ *            width), rows = batch * h_out * w_out; dilation 1, groups 1.
+ *   d_a = d_in + (has_bias ? 1 : 0)   (the bias acts as a constant-1 input,
+ *                                      appended as the last column)
+ *   grad_w, w, mom_w, F_w : [d_out, d_in] float32
+ *   grad_b, b, mom_b, F_b : [d_out] float32, NULL iff has_bias == 0
+ * Full method:  A, A_inv : [d_a, d_a]; G, G_inv : [d_out, d_out]  (float32,
+ *               symmetric; the library reads the upper triangle of A and G and
+ *               writes both triangles).  A, G are updated in place every step;
+ *               A_inv, G_inv are written on refresh steps and read every step.
+ * Diag method:  F_w, F_b updated in place; dA [d_a], dG [d_out] are written by
+ *               the FACTORS phase and read by the UPDATE phase.
+ * Pointers a method does not use may be NULL.  w, mom_w, b, mom_b are updated
+ * in place; a, g, grad_w, grad_b are only read.
+ */
+typedef struct kfac_layer {
+  int32_t kind;        /* KFAC_LINEAR | KFAC_CONV2D */
+  int32_t has_bias;    /* 0 | 1 */
+  int32_t act_dtype;   /* KFAC_F32 | KFAC_BF16 (element type of a) */
+  int32_t grad_dtype;  /* KFAC_F32 | KFAC_BF16 (element type of g) */
+  int64_t rows;        /* N */
+  int32_t d_in;
+  int32_t d_out;
+  int32_t batch, c_in, height, width, kh, kw, stride, pad;   /* conv2d only */
+  const void* a;
+  const void* g;
+  const float* grad_w;
+  const float* grad_b;
+  float* w;
+  float* b;
+  float* mom_w;
+  float* mom_b;
+  float* A;
+  float* G;
+  float* A_inv;
+  float* G_inv;
+  float* F_w;
+  float* F_b;
+  float* dA;
+  float* dG;
+} kfac_layer_t;
+
+/* Per-call scalars.  Schedules (warm-up damping, learning-rate decay, the
+ * inverse-refresh policy) live with the caller: it passes this step's values. */
+typedef struct kfac_hparams {
+  float lr;
+  float momentum;
+  float weight_decay;
+  float ema_decay;     /* full: factor EMA decay; diag: F EMA decay */
+  float damping;       /* lambda */
+  int32_t refresh;     /* full: nonzero = recompute the damped inverses this step */
+  int32_t phase_mask;  /* KFAC_PHASE_* bits, 0 = all */
+  int32_t reserved;    /* must be 0 */
+} kfac_hparams_t;
+
+/* Bytes of workspace the given stack needs in `mode` (host only, no GPU
+ * call).  Returns KFAC_ERR_ARG / _DTYPE / _UNSUPPORTED for descriptors the
+ * step would reject; pointers are not inspected. */
+kfac_status_t kfac_workspace_size(const kfac_layer_t* layers, int32_t n_layers, int32_t mode,
+                                  size_t* bytes);
+
+/* Enqueue one full K-FAC step for all layers on `stream`:
+ *   [FACTORS] A <- ema_decay A + (1 - ema_decay) a_bar^T a_bar / N, same for G
+ *   [INVERT]  if refresh: A_inv = (A + damping I)^-1, G_inv = (G + damping I)^-1
+ *             by Cholesky; a factor that is not positive definite keeps its
+ *             previous inverse and sets KFAC_FLAG_NOT_PD
+ *   [UPDATE]  P = G_inv [grad_w | grad_b] A_inv; D = P + wd W; V = mu V + D;
+ *             W = W - lr V  (w, b, mom_w, mom_b in place)
+ * Layers are processed in order; phases are ordered as listed. */
+kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Enqueue one diagonal step for all layers on `stream`:
+ *   [FACTORS] sums of squares of a and g down their rows, into the workspace
+ *   [UPDATE]  dA[j] = mean_n a_bar[n, j]^2 (conv: over the unfolded rows,
+ *             which are never materialised), dG[o] = mean_n g[n, o]^2; then in
+ *             one pass F = beta F + (1 - beta) dG[o] dA[j];
+ *             P = grad / (F + damping); D = P + wd W; V = mu V + D; W = W - lr V */
+kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Copy the workspace's sticky flag word to *flags (waits for `stream`), and
+ * clear it on the device afterwards when `clear` is nonzero. */
+kfac_status_t kfac_read_flags(void* workspace, void* stream, uint32_t* flags, int32_t clear);
+
+/* Static description of a status code. */
+const char* kfac_status_string(kfac_status_t status);
+
+/* KFAC_ABI_VERSION of the built library. */
+int32_t kfac_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KFAC_H */

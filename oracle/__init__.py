@@ -12,6 +12,9 @@ from .kfac import (  # noqa: F401
     FLAG_NONFINITE,
     widen,
     unfold,
+    unfold_column,
+    activation_column,
+    gradient_column,
     layer_rows,
     kronecker_factor,
     ema,

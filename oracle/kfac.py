@@ -78,6 +78,42 @@ def unfold(x: np.ndarray, k: int, stride: int, pad: int) -> np.ndarray:
     return U.reshape(B * Ho * Wo, C * k * k)
 
 
+def unfold_column(x: np.ndarray, k: int, stride: int, pad: int, j: int) -> np.ndarray:
+    """Column j of ``unfold(x, k, stride, pad)`` alone (same definition, for
+    checking single outputs of full-size inputs): j = (c * k + kh) * k + kw."""
+    B, C, H, W = x.shape
+    c, kh, kw = j // (k * k), (j // k) % k, j % k
+    Ho = (H + 2 * pad - k) // stride + 1
+    Wo = (W + 2 * pad - k) // stride + 1
+    hi = np.arange(Ho) * stride - pad + kh          # input row of each output row
+    wi = np.arange(Wo) * stride - pad + kw
+    hv, wv = (hi >= 0) & (hi < H), (wi >= 0) & (wi < W)
+    col = np.zeros((B, Ho, Wo))                     # zero where the tap is in the padding
+    col[np.ix_(np.arange(B), np.flatnonzero(hv), np.flatnonzero(wv))] = widen(x[:, c][:, hi[hv]][:, :, wi[wv]])
+    return col.reshape(-1)
+
+
+def activation_column(layer, a: np.ndarray, j: int) -> np.ndarray:
+    """Column j of a_bar (R1-R3) without building the whole matrix."""
+    if layer.has_bias and j == layer.d_in:
+        if layer.kind == "conv":
+            B, C, H, W = a.shape
+            n = B * ((H + 2 * layer.pad - layer.k) // layer.stride + 1) * ((W + 2 * layer.pad - layer.k) // layer.stride + 1)
+        else:
+            n = a.shape[0]
+        return np.ones(n)
+    if layer.kind == "conv":
+        return unfold_column(a, layer.k, layer.stride, layer.pad, j)
+    return widen(a[:, j])
+
+
+def gradient_column(layer, g: np.ndarray, o: int) -> np.ndarray:
+    """Column o of the output-gradient rows (conv: all samples and positions)."""
+    if layer.kind == "conv":
+        return widen(g[:, o]).reshape(-1)
+    return widen(g[:, o])
+
+
 def layer_rows(layer, a: np.ndarray, g: np.ndarray):
     """The rows the factors are built from: (a_bar [N, d_a], g [N, d_out]).
 

@@ -1,0 +1,62 @@
+// Internal declarations shared by the library's translation units.
+// Everything here is gfx950 (CDNA4) code: 64-lane wavefronts, MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/kfac.h"
+
+namespace kfac {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+// Workspace layout: [0, 256) flag word (+ padding); then regions carved by the
+// planner, each 256-byte aligned.
+constexpr size_t kFlagBytes = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Sets `bits` in the workspace flag word.  Called by one lane.
+__device__ inline void raise_flag(uint32_t* flags, uint32_t bits) { atomicOr(flags, bits); }
+
+__device__ inline float bf16_bits_to_float(unsigned short u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+#define KFAC_HIP_TRY(expr)                                  \
+  do {                                                      \
+    hipError_t _e = (expr);                                 \
+    if (_e != hipSuccess) return KFAC_ERR_HIP;              \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// host-side helpers shared by the launchers
+
+struct LayerGeom {
+  int64_t rows;
+  int d_in, d_out, d_a;
+  bool conv, bias;
+  int batch, c_in, h, w, kh, kw, stride, pad, h_out, w_out;
+};
+
+LayerGeom geom_of(const kfac_layer_t& L);
+
+// diag method (diag.hip)
+size_t diag_workspace_bytes(const kfac_layer_t* layers, int n);
+kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                           size_t ws_bytes, hipStream_t stream, int phases);
+
+// full method (full.hip)
+size_t full_workspace_bytes(const kfac_layer_t* layers, int n);
+kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                           size_t ws_bytes, hipStream_t stream, int phases);
+
+}  // namespace kfac

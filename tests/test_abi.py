@@ -1,0 +1,175 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, its structs match the binding's, and invalid requests are
+rejected before anything touches a GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import second_order_optimizer_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kfac.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from second_order_optimizer_amd import build
+        build.build()
+    return K.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kfac_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(K.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert K.abi_version() == 1
+    assert K.status_string(K.KFAC_ERR_WORKSPACE) == "workspace missing or too small"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """sizeof/offsetof of both structs from the C compiler == ctypes mirror."""
+    fields = [f for f, _ in K.Layer._fields_]
+    hfields = [f for f, _ in K.HParams._fields_]
+    prog = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
+            'printf("%zu\\n", sizeof(kfac_layer_t));', 'printf("%zu\\n", sizeof(kfac_hparams_t));']
+    prog += [f'printf("%zu\\n", offsetof(kfac_layer_t, {f}));' for f in fields]
+    prog += [f'printf("%zu\\n", offsetof(kfac_hparams_t, {f}));' for f in hfields]
+    prog += ["return 0;}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(prog))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(c), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(K.Layer)
+    assert vals[1] == ctypes.sizeof(K.HParams)
+    got = [getattr(K.Layer, f).offset for f in fields] + [getattr(K.HParams, f).offset for f in hfields]
+    assert vals[2:] == got
+
+
+def _linear(**kw):
+    base = dict(kind=K.LINEAR, d_in=8, d_out=4, rows=16, has_bias=True)
+    base.update(kw)
+    return K.make_layer(base.pop("kind"), base.pop("d_in"), base.pop("d_out"), base.pop("rows"),
+                        base.pop("has_bias"), **base)
+
+
+def _conv(**kw):
+    base = dict(d_in=27, d_out=5, rows=2 * 4 * 4, has_bias=False, batch=2, c_in=3, height=7, width=7, k=3,
+                stride=2, pad=1)
+    base.update(kw)
+    return K.make_layer(K.CONV2D, base.pop("d_in"), base.pop("d_out"), base.pop("rows"), base.pop("has_bias"),
+                        **base)
+
+
+def _ws_status(layers, mode):
+    out = ctypes.c_size_t(0)
+    arr = K.layer_array(layers)
+    return K.load().kfac_workspace_size(arr, len(layers), mode, ctypes.byref(out)), out.value
+
+
+def test_workspace_size_valid_stacks(lib):
+    for mode in (K.MODE_FULL, K.MODE_DIAG):
+        st, n = _ws_status([_linear(), _conv()], mode)
+        assert st == K.KFAC_OK and n >= 256 and n % 256 == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(d_in=0), K.KFAC_ERR_ARG),
+    (dict(rows=-1), K.KFAC_ERR_ARG),
+    (dict(kind=7), K.KFAC_ERR_ARG),
+    (dict(has_bias=2), K.KFAC_ERR_ARG),
+    (dict(act_dtype=5), K.KFAC_ERR_DTYPE),
+    (dict(grad_dtype=-1), K.KFAC_ERR_DTYPE),
+])
+def test_linear_shape_errors(lib, bad, code):
+    for mode in (K.MODE_FULL, K.MODE_DIAG):
+        assert _ws_status([_linear(**bad)], mode)[0] == code
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(d_in=26), K.KFAC_ERR_ARG),              # != c_in * k * k
+    (dict(rows=33), K.KFAC_ERR_ARG),              # != batch * h_out * w_out
+    (dict(stride=0), K.KFAC_ERR_ARG),
+    (dict(k=9, d_in=243), K.KFAC_ERR_UNSUPPORTED),  # kernels up to 7x7
+    (dict(height=1, width=1, k=5, d_in=75, pad=0), K.KFAC_ERR_ARG),  # kernel larger than padded input
+])
+def test_conv_shape_errors(lib, bad, code):
+    assert _ws_status([_conv(**bad)], K.MODE_FULL)[0] == code
+
+
+def test_diag_rejects_bf16(lib):
+    assert _ws_status([_linear(act_dtype=K.BF16)], K.MODE_DIAG)[0] == K.KFAC_ERR_DTYPE
+    assert _ws_status([_linear(act_dtype=K.BF16, grad_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_OK
+
+
+def _call(fn, layers, hp, ws, ws_bytes):
+    arr = K.layer_array(layers) if layers else None
+    return fn(arr, len(layers) if layers else 0, ctypes.byref(hp) if hp is not None else None, ws, ws_bytes, None)
+
+
+def _ptrs(base=0x10000):
+    names = ["a", "g", "grad_w", "grad_b", "w", "b", "mom_w", "mom_b", "A", "G", "A_inv", "G_inv", "F_w", "F_b",
+             "dA", "dG"]
+    return {n: base + 0x1000 * i for i, n in enumerate(names)}
+
+
+def _fake_layer(**over):
+    """A descriptor with well-formed (never dereferenced) device addresses."""
+    L = _linear()
+    for n, p in _ptrs().items():
+        setattr(L, n, p)
+    for n, v in over.items():
+        setattr(L, n, v)
+    return L
+
+
+@pytest.mark.parametrize("fn_name,mode", [("kfac_step_full", K.MODE_FULL), ("kfac_step_diag", K.MODE_DIAG)])
+def test_step_rejects_before_enqueue(lib, fn_name, mode):
+    """Every error path returns before any HIP call (this host has no GPU, so
+    reaching the runtime would fail with KFAC_ERR_HIP instead)."""
+    fn = getattr(lib, fn_name)
+    hp = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3)
+    ws = 0x100000
+    good = _fake_layer()
+    need = K.workspace_size([good], mode)
+    assert _call(fn, [], hp, ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [good], None, ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [good], hp, 0, need) == K.KFAC_ERR_WORKSPACE
+    assert _call(fn, [good], hp, ws, need - 1) == K.KFAC_ERR_WORKSPACE
+    assert _call(fn, [good], hp, ws + 16, need) == K.KFAC_ERR_ALIGN
+    assert _call(fn, [_fake_layer(w=0x10004)], hp, ws, need) == K.KFAC_ERR_ALIGN
+    assert _call(fn, [_fake_layer(grad_w=None)], hp, ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [_fake_layer(has_bias=0)], hp, ws, need) == K.KFAC_ERR_ARG  # bias pointers without a bias
+    bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3)
+    bad.reserved = 1
+    assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
+    bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, phase_mask=8)
+    assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
+
+
+def test_read_flags_rejects_null(lib):
+    out = ctypes.c_uint32(0)
+    assert lib.kfac_read_flags(None, None, ctypes.byref(out), 0) == K.KFAC_ERR_ARG
+    assert lib.kfac_read_flags(0x1000, None, None, 0) == K.KFAC_ERR_ARG
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    """No silent fallback: a missing shared library is an error."""
+    monkeypatch.setattr(K, "_lib", None)
+    monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(FileNotFoundError):
+        K.load()
