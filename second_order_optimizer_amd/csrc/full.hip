@@ -1,13 +1,614 @@
-// Full K-FAC step launcher (placeholder until the factor, inverse and
-// preconditioning kernels land).
+// Full K-FAC step (Osawa et al., section 3.2): per layer
+//   [FACTORS] A <- eps A + (1 - eps) a_bar^T a_bar / N, G likewise (SYRK on
+//             matrix cores, EMA fused into the epilogue, upper tiles mirrored)
+//   [INVERT]  (A + lambda I)^-1, (G + lambda I)^-1 by a blocked Cholesky
+//             factorisation, a blocked triangular inverse and Z^T Z, batched
+//             over all factors of the stack (section 4.2: damping)
+//   [UPDATE]  T = [grad_w | grad_b] A_inv, then G_inv T with the momentum /
+//             weight-decay / parameter write fused into the second GEMM's
+//             epilogue.
+#include <algorithm>
+#include <vector>
+
 #include "common.h"
+#include "gemm.h"
+#include "syrk_bf16.h"
 
 namespace kfac {
 
-size_t full_workspace_bytes(const kfac_layer_t*, int) { return kFlagBytes; }
+namespace {
 
-kfac_status_t full_enqueue(const kfac_layer_t*, int, const kfac_hparams_t&, char*, size_t, hipStream_t, int) {
-  return KFAC_ERR_UNSUPPORTED;
+constexpr int kNb = kTile;   // Cholesky block size = GEMM tile
+
+// ---------------------------------------------------------------------------
+// im2col: U[n][j] = x[b][c][ho*s - p + kh][wo*s - p + kw], n = (b*Ho + ho)*Wo + wo,
+// j = (c*k + kh)*k + kw; one thread per output element (writes coalesced).
+__global__ void __launch_bounds__(256) unfold_kernel(const float* __restrict__ x, float* __restrict__ U, int C,
+                                                     int H, int W, int k, int s, int p, int Ho, int Wo,
+                                                     int64_t total, int dcols) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t n = e / dcols;
+  const int j = static_cast<int>(e - n * dcols);
+  const int wo = static_cast<int>(n % Wo);
+  const int64_t t = n / Wo;
+  const int ho = static_cast<int>(t % Ho);
+  const int b = static_cast<int>(t / Ho);
+  const int c = j / (k * k);
+  const int r = j - c * k * k;
+  const int kh = r / k, kw = r - (r / k) * k;
+  const int hh = ho * s - p + kh, ww = wo * s - p + kw;
+  float v = 0.f;
+  if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = x[((static_cast<int64_t>(b) * C + c) * H + hh) * W + ww];
+  U[e] = v;
+}
+
+// g [B][C][P] -> gT [B*P][C] through a 32 x 32 LDS tile.
+__global__ void __launch_bounds__(256) nchw_rows_kernel(const float* __restrict__ g, float* __restrict__ out,
+                                                        int C, int P) {
+  __shared__ float t[32][33];
+  const int b = blockIdx.z;
+  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+  const float* src = g + static_cast<int64_t>(b) * C * P;
+  float* dst = out + static_cast<int64_t>(b) * P * C;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    const int c = c0 + r, p = p0 + tx;
+    t[r][tx] = (c < C && p < P) ? src[static_cast<int64_t>(c) * P + p] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int p = p0 + r, c = c0 + tx;
+    if (p < P && c < C) dst[static_cast<int64_t>(p) * C + c] = t[tx][r];
+  }
+}
+
+// Split-K SYRK finish: F[i][j] = beta F[i][j] + alpha sum_s part[s][i][j] for
+// i <= j, mirrored.  Partial sums are added in split order.
+struct SymRed {
+  const float* part;
+  float* F;
+  int64_t stride;
+  int32_t d, nsplit;
+  float alpha, beta;
+};
+
+__global__ void __launch_bounds__(256) sym_reduce_kernel(SymRed r) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t dd = static_cast<int64_t>(r.d) * r.d;
+  if (e >= dd) return;
+  const int i = static_cast<int>(e / r.d), j = static_cast<int>(e - static_cast<int64_t>(i) * r.d);
+  if (i > j) return;
+  float s = 0.f;
+  for (int k = 0; k < r.nsplit; ++k) s += r.part[k * r.stride + e];
+  const float o = r.beta * r.F[e] + r.alpha * s;
+  r.F[e] = o;
+  if (i != j) r.F[static_cast<int64_t>(j) * r.d + i] = o;
+}
+
+// ---------------------------------------------------------------------------
+// damped Cholesky inverse, batched over matrices
+
+constexpr int kMaxMats = 40;
+
+struct Mat {
+  const float* F;     // factor (upper triangle read)
+  float* Finv;        // damped inverse (written unless the factorisation failed)
+  float* L;           // working copy -> Cholesky factor (lower)
+  float* Z;           // L^-1 (lower)
+  float* Dinv;        // inverses of the diagonal blocks, [nblk][128][128]
+  int32_t* fail;
+  int32_t d;
+  int32_t pad_;
+};
+struct MatTab {
+  Mat m[kMaxMats];
+  int32_t n;
+  int32_t k;          // current block
+  float damping;
+  uint32_t* flags;
+};
+
+// L = F + damping I (from F's upper triangle, both triangles written), Z = 0,
+// fail = 0.  grid.y = matrix, grid.x strides rows.
+__global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
+  const Mat& M = T.m[blockIdx.y];
+  const int d = M.d;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *M.fail = 0;
+  for (int i = blockIdx.x; i < d; i += gridDim.x) {
+    for (int j = threadIdx.x; j < d; j += 256) {
+      const int lo = min(i, j), hi = max(i, j);
+      float v = M.F[static_cast<int64_t>(lo) * d + hi];
+      if (i == j) v += T.damping;
+      M.L[static_cast<int64_t>(i) * d + j] = v;
+      M.Z[static_cast<int64_t>(i) * d + j] = 0.f;
+    }
+  }
+}
+
+// Block k of every matrix with more than k blocks: Cholesky of the diagonal
+// block (right-looking, in LDS) fused with the forward substitution that
+// inverts it.  Writes L_kk (zero above the diagonal) into L, its inverse into
+// Dinv[k] and into Z's diagonal block.  A pivot that is not positive (or not
+// finite) marks the matrix failed, raises KFAC_FLAG_NOT_PD and is replaced
+// by 1 so the remaining steps stay finite; a failed matrix's inverse is not
+// written.
+__global__ void __launch_bounds__(256) chol_diag_kernel(MatTab T) {
+  __shared__ float Ls[kNb][kNb + 1];
+  __shared__ float Xs[kNb][kNb + 1];
+  __shared__ float piv;
+  const Mat& M = T.m[blockIdx.x];
+  const int d = M.d, k = T.k;
+  const int nblk = (d + kNb - 1) / kNb;
+  if (k >= nblk) return;
+  const int r0 = k * kNb;
+  const int bk = min(kNb, d - r0);
+  const int tid = threadIdx.x;
+  float* Lg = M.L + static_cast<int64_t>(r0) * d + r0;
+  for (int e = tid; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e % kNb;
+    float v = 0.f;
+    if (r < bk && c <= r) v = Lg[static_cast<int64_t>(r) * d + c];
+    Ls[r][c] = v;
+    Xs[r][c] = (r == c && r < bk) ? 1.f : 0.f;
+  }
+  __syncthreads();
+  const int tr = tid >> 4, tc = tid & 15;
+  for (int j = 0; j < bk; ++j) {
+    if (tid == 0) {
+      float p = Ls[j][j];
+      if (!(p > 0.f) || !isfinite(p)) {
+        if (*M.fail == 0) {
+          *M.fail = 1;
+          raise_flag(T.flags, KFAC_FLAG_NOT_PD);
+        }
+        p = 1.f;
+      }
+      piv = sqrtf(p);
+      Ls[j][j] = piv;
+    }
+    __syncthreads();
+    const float dj = piv;
+    const float inv = 1.0f / dj;
+    for (int r = j + 1 + tid; r < bk; r += 256) Ls[r][j] *= inv;
+    for (int c = tid; c <= j; c += 256) Xs[j][c] *= inv;
+    __syncthreads();
+    // trailing update of L (j < c <= r) and of the inverse rows below j (c <= j)
+    for (int r = j + 1 + tr; r < bk; r += 16) {
+      const float lr = Ls[r][j];
+      for (int c = tc; c <= r; c += 16) {
+        if (c > j) Ls[r][c] -= lr * Ls[c][j];
+        else Xs[r][c] -= lr * Xs[j][c];
+      }
+    }
+    __syncthreads();
+  }
+  // write back: L_kk (lower, zero above), Dinv[k] and Z_kk
+  float* D = M.Dinv + static_cast<int64_t>(k) * kNb * kNb;
+  float* Zg = M.Z + static_cast<int64_t>(r0) * d + r0;
+  for (int e = tid; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e % kNb;
+    const float l = c <= r ? Ls[r][c] : 0.f;
+    const float x = c <= r ? Xs[r][c] : 0.f;
+    D[e] = (r < bk && c < bk) ? x : 0.f;
+    if (r < bk && c < bk) {
+      Lg[static_cast<int64_t>(r) * d + c] = l;
+      Zg[static_cast<int64_t>(r) * d + c] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// planning
+
+struct FullPlan {
+  size_t ws_bytes = kFlagBytes;
+  // per-layer scratch (shared, layers run one after another in FACTORS)
+  float* U = nullptr;
+  float* GT = nullptr;
+  float* part = nullptr;
+  size_t part_floats = 0;
+  std::vector<float*> T;         // per layer, d_out x d_a
+  std::vector<Mat> mats;         // inverse work per factor
+};
+
+size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
+
+// SYRK split count: enough workgroups to cover the chip, at least 2048 rows per split.
+int syrk_splits(int d, int64_t rows) {
+  const int T = (d + kTile - 1) / kTile;
+  const int tiles = T * (T + 1) / 2;
+  int s = std::max(1, 512 / tiles);
+  s = static_cast<int>(std::min<int64_t>(s, std::max<int64_t>(1, rows / 2048)));
+  return std::min(s, 256);
+}
+
+FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool refresh) {
+  FullPlan P;
+  size_t off = kFlagBytes;
+  auto carve = [&](size_t bytes) -> char* {
+    char* p = ws ? ws + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return p;
+  };
+  size_t u_floats = 0, gt_floats = 0, part_floats = 0;
+  for (int li = 0; li < n; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    if (g.conv) {
+      u_floats = std::max(u_floats, static_cast<size_t>(g.rows) * g.d_in);
+      gt_floats = std::max(gt_floats, static_cast<size_t>(g.rows) * g.d_out);
+    }
+    for (int which = 0; which < 2; ++which) {
+      const int d = which == 0 ? g.d_a : g.d_out;
+      const int s = syrk_splits(d, g.rows);
+      if (s > 1) part_floats = std::max(part_floats, static_cast<size_t>(s) * d * d);
+    }
+  }
+  // all regions are always carved so the size does not depend on the phases
+  P.U = reinterpret_cast<float*>(carve(u_floats * 4));
+  P.GT = reinterpret_cast<float*>(carve(gt_floats * 4));
+  P.part = reinterpret_cast<float*>(carve(part_floats * 4));
+  P.part_floats = part_floats;
+  for (int li = 0; li < n; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * g.d_a * 4)));
+  }
+  for (int li = 0; li < n; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    for (int which = 0; which < 2; ++which) {
+      const int d = which == 0 ? g.d_a : g.d_out;
+      Mat m{};
+      m.F = which == 0 ? layers[li].A : layers[li].G;
+      m.Finv = which == 0 ? layers[li].A_inv : layers[li].G_inv;
+      m.d = d;
+      m.L = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
+      m.Z = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
+      m.Dinv = reinterpret_cast<float*>(carve(nblk_of(d) * kNb * kNb * 4));
+      m.fail = reinterpret_cast<int32_t*>(carve(4));
+      P.mats.push_back(m);
+    }
+  }
+  (void)phases;
+  (void)refresh;
+  P.ws_bytes = off;
+  return P;
+}
+
+kfac_status_t sym_reduce(const FullPlan& P, float* F, int d, int s, float eps, int64_t rows, hipStream_t st);
+
+kfac_status_t syrk_fp32(const float* X, int width, int64_t rows, int d, int special, float* F, float eps,
+                        const FullPlan& P, hipStream_t st) {
+  const int s = syrk_splits(d, rows);
+  GemmProb p{};
+  p.A = X;
+  p.B = X;
+  p.lda = p.ldb = width;
+  p.M = p.N = d;
+  p.kb = 0;
+  p.ke = static_cast<int>(rows);
+  p.tri = TRI_UPPER;
+  p.a_special = p.b_special = special;
+  gemm_set_tiles(p);
+  GemmScalars sc{};
+  std::vector<GemmProb> v;
+  if (s == 1) {
+    p.C = F;
+    p.ldc = d;
+    p.nsplit = 1;
+    p.alpha = (1.0f - eps) / static_cast<float>(rows);
+    p.beta = eps;
+    v.push_back(p);
+    return launch_gemm(v, OP_MN, OP_MN, EPI_SYM_EMA, sc, st);
+  }
+  p.C = P.part;
+  p.ldc = d;
+  p.nsplit = s;
+  p.split_stride = static_cast<int64_t>(d) * d;
+  p.alpha = 1.0f;
+  v.push_back(p);
+  kfac_status_t r = launch_gemm(v, OP_MN, OP_MN, EPI_STORE, sc, st);
+  if (r != KFAC_OK) return r;
+  return sym_reduce(P, F, d, s, eps, rows, st);
+}
+
+kfac_status_t sym_reduce(const FullPlan& P, float* F, int d, int s, float eps, int64_t rows, hipStream_t st) {
+  SymRed red{P.part, F, static_cast<int64_t>(d) * d, d, s, (1.0f - eps) / static_cast<float>(rows), eps};
+  const int64_t dd = static_cast<int64_t>(d) * d;
+  hipLaunchKernelGGL(sym_reduce_kernel, dim3(static_cast<unsigned>((dd + 255) / 256)), dim3(256), 0, st, red);
+  return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+}
+
+kfac_status_t syrk_bf16_ema(const uint16_t* X, int width, int64_t rows, int d, int special, float* F, float eps,
+                            const FullPlan& P, hipStream_t st) {
+  const int s = syrk_splits(d, rows);
+  if (s == 1)
+    return launch_syrk_bf16(X, width, rows, d, special, F, (1.0f - eps) / static_cast<float>(rows), eps, 1, 0, st);
+  kfac_status_t r = launch_syrk_bf16(X, width, rows, d, special, P.part, 1.f, 0.f, s,
+                                     static_cast<int64_t>(d) * d, st);
+  if (r != KFAC_OK) return r;
+  return sym_reduce(P, F, d, s, eps, rows, st);
+}
+
+kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
+                            hipStream_t st) {
+  const float eps = hp.ema_decay;
+  for (int li = 0; li < n; ++li) {
+    const kfac_layer_t& L = layers[li];
+    const LayerGeom g = geom_of(L);
+    const int special = g.bias ? g.d_in : -1;
+    kfac_status_t r;
+    if (g.conv) {
+      const int64_t total = g.rows * static_cast<int64_t>(g.d_in);
+      hipLaunchKernelGGL(unfold_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
+                         static_cast<const float*>(L.a), P.U, g.c_in, g.h, g.w, g.kh, g.stride, g.pad, g.h_out,
+                         g.w_out, total, g.d_in);
+      KFAC_HIP_TRY(hipGetLastError());
+      const int Pp = g.h_out * g.w_out;
+      hipLaunchKernelGGL(nchw_rows_kernel, dim3((Pp + 31) / 32, (g.d_out + 31) / 32, g.batch), dim3(256), 0, st,
+                         static_cast<const float*>(L.g), P.GT, g.d_out, Pp);
+      KFAC_HIP_TRY(hipGetLastError());
+      r = syrk_fp32(P.U, g.d_in, g.rows, g.d_a, special, L.A, eps, P, st);
+      if (r != KFAC_OK) return r;
+      r = syrk_fp32(P.GT, g.d_out, g.rows, g.d_out, -1, L.G, eps, P, st);
+      if (r != KFAC_OK) return r;
+    } else if (L.act_dtype == KFAC_F32 && L.grad_dtype == KFAC_F32) {
+      r = syrk_fp32(static_cast<const float*>(L.a), g.d_in, g.rows, g.d_a, special, L.A, eps, P, st);
+      if (r != KFAC_OK) return r;
+      r = syrk_fp32(static_cast<const float*>(L.g), g.d_out, g.rows, g.d_out, -1, L.G, eps, P, st);
+      if (r != KFAC_OK) return r;
+    } else {
+      for (int which = 0; which < 2; ++which) {
+        const void* X = which == 0 ? L.a : L.g;
+        const int dt = which == 0 ? L.act_dtype : L.grad_dtype;
+        const int width = which == 0 ? g.d_in : g.d_out;
+        const int d = which == 0 ? g.d_a : g.d_out;
+        float* F = which == 0 ? L.A : L.G;
+        const int sp = which == 0 ? special : -1;
+        if (dt == KFAC_F32) r = syrk_fp32(static_cast<const float*>(X), width, g.rows, d, sp, F, eps, P, st);
+        else r = syrk_bf16_ema(static_cast<const uint16_t*>(X), width, g.rows, d, sp, F, eps, P, st);
+        if (r != KFAC_OK) return r;
+      }
+    }
+  }
+  return KFAC_OK;
+}
+
+kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st) {
+  const std::vector<Mat>& mats = P.mats;
+  int nblk_max = 0;
+  for (const Mat& m : mats) nblk_max = std::max<int>(nblk_max, static_cast<int>(nblk_of(m.d)));
+  GemmScalars sc{};
+  // runs `fn` on the matrices selected by `pred`, kMaxMats at a time
+  auto tables = [&](auto pred, int k, auto fn) -> kfac_status_t {
+    MatTab T{};
+    T.damping = hp.damping;
+    T.flags = flags;
+    T.k = k;
+    for (const Mat& m : mats) {
+      if (!pred(m)) continue;
+      T.m[T.n++] = m;
+      if (T.n == kMaxMats) {
+        kfac_status_t r = fn(T);
+        if (r != KFAC_OK) return r;
+        T.n = 0;
+      }
+    }
+    return T.n > 0 ? fn(T) : KFAC_OK;
+  };
+  kfac_status_t r = tables([](const Mat&) { return true; }, 0, [&](MatTab& T) {
+    hipLaunchKernelGGL(chol_init_kernel, dim3(64, T.n), dim3(256), 0, st, T);
+    return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+  });
+  if (r != KFAC_OK) return r;
+  // blocked right-looking Cholesky
+  for (int k = 0; k < nblk_max; ++k) {
+    r = tables([&](const Mat& m) { return static_cast<int>(nblk_of(m.d)) > k; }, k, [&](MatTab& T) {
+      hipLaunchKernelGGL(chol_diag_kernel, dim3(T.n), dim3(256), 0, st, T);
+      return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+    });
+    if (r != KFAC_OK) return r;
+    std::vector<GemmProb> panel, trail;
+    for (const Mat& m : mats) {
+      const int d = m.d;
+      if (static_cast<int>(nblk_of(d)) <= k + 1) continue;
+      const int r1 = (k + 1) * kNb;
+      GemmProb p{};
+      // L_ik = M_ik Dinv_k^T for the rows below block k
+      p.A = m.L + static_cast<int64_t>(r1) * d + k * kNb;
+      p.lda = d;
+      p.B = m.Dinv + static_cast<int64_t>(k) * kNb * kNb;
+      p.ldb = kNb;
+      p.C = m.L + static_cast<int64_t>(r1) * d + k * kNb;
+      p.ldc = d;
+      p.M = d - r1;
+      p.N = kNb;
+      p.kb = 0;
+      p.ke = kNb;
+      p.tri = TRI_FULL;
+      p.a_special = p.b_special = -1;
+      p.alpha = 1.f;
+      p.nsplit = 1;
+      gemm_set_tiles(p);
+      panel.push_back(p);
+      // M_ij -= L_ik L_jk^T for k < j <= i
+      GemmProb q = p;
+      q.B = p.A;
+      q.ldb = d;
+      q.C = m.L + static_cast<int64_t>(r1) * d + r1;
+      q.N = d - r1;
+      q.tri = TRI_LOWER;
+      gemm_set_tiles(q);
+      trail.push_back(q);
+    }
+    if (!panel.empty()) {
+      r = launch_gemm(panel, OP_K, OP_K, EPI_STORE, sc, st);
+      if (r != KFAC_OK) return r;
+      r = launch_gemm(trail, OP_K, OP_K, EPI_SUB, sc, st);
+      if (r != KFAC_OK) return r;
+    }
+  }
+  // Z = L^-1, block row by block row: Z_ik = Dinv_i R_ik (k < i), then
+  // R_jk -= L_ji Z_ik for the rows below (R starts at zero below the diagonal)
+  for (int i = 0; i < nblk_max; ++i) {
+    std::vector<GemmProb> fin, upd;
+    for (const Mat& m : mats) {
+      const int d = m.d;
+      const int nb = static_cast<int>(nblk_of(d));
+      if (nb <= i) continue;
+      const int r0 = i * kNb;
+      const int bk = std::min(kNb, d - r0);
+      if (i > 0) {
+        GemmProb p{};
+        p.A = m.Dinv + static_cast<int64_t>(i) * kNb * kNb;
+        p.lda = kNb;
+        p.B = m.Z + static_cast<int64_t>(r0) * d;
+        p.ldb = d;
+        p.C = m.Z + static_cast<int64_t>(r0) * d;
+        p.ldc = d;
+        p.M = bk;
+        p.N = r0;
+        p.kb = 0;
+        p.ke = bk;
+        p.tri = TRI_FULL;
+        p.a_special = p.b_special = -1;
+        p.alpha = 1.f;
+        p.nsplit = 1;
+        gemm_set_tiles(p);
+        fin.push_back(p);
+      }
+      if (nb > i + 1) {
+        const int r1 = r0 + kNb;
+        GemmProb q{};
+        q.A = m.L + static_cast<int64_t>(r1) * d + r0;
+        q.lda = d;
+        q.B = m.Z + static_cast<int64_t>(r0) * d;
+        q.ldb = d;
+        q.C = m.Z + static_cast<int64_t>(r1) * d;
+        q.ldc = d;
+        q.M = d - r1;
+        q.N = r1;
+        q.kb = 0;
+        q.ke = kNb;
+        q.tri = TRI_FULL;
+        q.a_special = q.b_special = -1;
+        q.alpha = 1.f;
+        q.nsplit = 1;
+        gemm_set_tiles(q);
+        upd.push_back(q);
+      }
+    }
+    if (!fin.empty()) {
+      r = launch_gemm(fin, OP_K, OP_MN, EPI_STORE, sc, st);
+      if (r != KFAC_OK) return r;
+    }
+    if (!upd.empty()) {
+      r = launch_gemm(upd, OP_K, OP_MN, EPI_SUB, sc, st);
+      if (r != KFAC_OK) return r;
+    }
+  }
+  // inverse = Z^T Z (upper tiles, mirrored), written only for matrices that factored
+  std::vector<GemmProb> lau;
+  for (size_t mi = 0; mi < mats.size(); ++mi) {
+    const Mat& m = mats[mi];
+    GemmProb p{};
+    p.A = m.Z;
+    p.B = m.Z;
+    p.lda = p.ldb = m.d;
+    p.C = m.Finv;
+    p.ldc = m.d;
+    p.M = p.N = m.d;
+    p.kb = 0;
+    p.ke = m.d;
+    p.tri = TRI_UPPER;
+    p.k_from_diag = 1;
+    p.a_special = p.b_special = -1;
+    p.fail = m.fail;
+    p.nsplit = 1;
+    gemm_set_tiles(p);
+    lau.push_back(p);
+  }
+  return launch_gemm(lau, OP_MN, OP_MN, EPI_SYM_IFOK, sc, st);
+}
+
+kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
+                           uint32_t* flags, hipStream_t st) {
+  std::vector<GemmProb> g1, g2;
+  for (int li = 0; li < n; ++li) {
+    const kfac_layer_t& L = layers[li];
+    const LayerGeom g = geom_of(L);
+    GemmProb p{};
+    // T = [grad_w | grad_b] A_inv
+    p.A = L.grad_w;
+    p.lda = g.d_in;
+    p.A_extra = g.bias ? L.grad_b : nullptr;
+    p.a_special = g.bias ? g.d_in : -1;
+    p.B = L.A_inv;
+    p.ldb = g.d_a;
+    p.b_special = -1;
+    p.C = P.T[li];
+    p.ldc = g.d_a;
+    p.M = g.d_out;
+    p.N = g.d_a;
+    p.kb = 0;
+    p.ke = g.d_a;
+    p.tri = TRI_FULL;
+    p.alpha = 1.f;
+    p.nsplit = 1;
+    gemm_set_tiles(p);
+    g1.push_back(p);
+    // P = G_inv T (G_inv symmetric: read as its transpose), fused update
+    GemmProb q{};
+    q.A = L.G_inv;
+    q.lda = g.d_out;
+    q.a_special = -1;
+    q.B = P.T[li];
+    q.ldb = g.d_a;
+    q.b_special = -1;
+    q.M = g.d_out;
+    q.N = g.d_a;
+    q.kb = 0;
+    q.ke = g.d_out;
+    q.tri = TRI_FULL;
+    q.W = L.w;
+    q.Wb = L.b;
+    q.V = L.mom_w;
+    q.Vb = L.mom_b;
+    q.d_in = g.d_in;
+    q.nsplit = 1;
+    gemm_set_tiles(q);
+    g2.push_back(q);
+  }
+  GemmScalars sc{hp.lr, hp.momentum, hp.weight_decay, flags};
+  kfac_status_t r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
+  if (r != KFAC_OK) return r;
+  return launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
+}
+
+}  // namespace
+
+size_t full_workspace_bytes(const kfac_layer_t* layers, int n) {
+  return plan_full(layers, n, nullptr, KFAC_PHASE_ALL, true).ws_bytes;
+}
+
+kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws, size_t ws_bytes,
+                           hipStream_t st, int phases) {
+  FullPlan P = plan_full(layers, n, ws, phases, hp.refresh != 0);
+  if (P.ws_bytes > ws_bytes) return KFAC_ERR_WORKSPACE;
+  uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
+  kfac_status_t r;
+  if (phases & KFAC_PHASE_FACTORS) {
+    r = factors_phase(layers, n, hp, P, st);
+    if (r != KFAC_OK) return r;
+  }
+  if ((phases & KFAC_PHASE_INVERT) && hp.refresh) {
+    r = invert_phase(hp, P, flags, st);
+    if (r != KFAC_OK) return r;
+  }
+  if (phases & KFAC_PHASE_UPDATE) {
+    r = update_phase(layers, n, hp, P, flags, st);
+    if (r != KFAC_OK) return r;
+  }
+  return KFAC_OK;
 }
 
 }  // namespace kfac

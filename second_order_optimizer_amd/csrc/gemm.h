@@ -1,0 +1,73 @@
+// Batched fp32 MFMA GEMM used by every dense contraction of the full K-FAC
+// step (factor SYRK, preconditioning, blocked Cholesky inverse).
+#pragma once
+
+#include <vector>
+
+#include "common.h"
+
+namespace kfac {
+
+constexpr int kTile = 128;     // output tile (both dimensions)
+constexpr int kTileK = 16;     // K step staged through LDS
+constexpr int kMaxGemmProbs = 22;
+
+// Operand layouts.  For A (M x K): OP_MN stores element (i, k) at
+// A[k * lda + i] (i contiguous), OP_K at A[i * lda + k] (k contiguous).
+// For B (K x N): OP_MN stores (k, j) at B[k * ldb + j], OP_K at B[j * ldb + k].
+enum GemmOp : int { OP_MN = 0, OP_K = 1 };
+
+// Epilogues.
+enum GemmEpi : int {
+  EPI_STORE = 0,      // C = alpha * acc
+  EPI_SUB = 1,        // C -= acc
+  EPI_SYM_EMA = 2,    // upper tiles; C = beta * C + alpha * acc, mirrored to the lower triangle
+  EPI_UPDATE = 3,     // P = acc; D = P + wd W; V = mu V + D; W -= lr V  (columns >= d_in go to b / mom_b)
+  EPI_SYM_IFOK = 4,   // upper tiles; C = acc mirrored, skipped when *fail != 0
+};
+
+// Tile grids.
+enum GemmTri : int { TRI_FULL = 0, TRI_UPPER = 1, TRI_LOWER = 2 };
+
+struct GemmProb {
+  const void* A;
+  const void* B;
+  float* C;
+  const float* A_extra;   // OP_K A: column `a_special` of A is A_extra[i]
+  float* W;               // EPI_UPDATE targets
+  float* Wb;
+  float* V;
+  float* Vb;
+  const int32_t* fail;    // EPI_SYM_IFOK
+  int64_t split_stride;   // C offset between K splits (floats)
+  int32_t lda, ldb, ldc;
+  int32_t M, N;
+  int32_t kb, ke;         // contraction range [kb, ke)
+  int32_t tiles_m, tiles_n;
+  int32_t tri;
+  int32_t k_from_diag;    // 1: a tile (ti, tj) starts its K loop at max(ti, tj) * kTile
+  int32_t a_special;      // OP_MN: element i == a_special is 1.0 (bias column); OP_K: see A_extra; -1 none
+  int32_t b_special;      // OP_MN: element j == b_special is 1.0; -1 none
+  int32_t d_in;           // EPI_UPDATE: columns < d_in go to W / V
+  int32_t nsplit;         // K splits (each writes C + s * split_stride)
+  int32_t blk_begin;
+  float alpha, beta;
+};
+
+struct GemmScalars {
+  float lr, momentum, weight_decay;
+  uint32_t* flags;
+};
+
+// Number of workgroups one problem needs.
+int gemm_blocks(const GemmProb& p);
+
+// Fills tiles_m / tiles_n from M / N.
+void gemm_set_tiles(GemmProb& p);
+
+// Launches the problems (any count; grouped internally) with operand layouts
+// (amode, bmode) and epilogue `epi` on `stream`.
+kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
+                          hipStream_t stream);
+
+}  // namespace kfac
