@@ -96,6 +96,140 @@ def cpu_baseline_diag(cfg_full, seconds_target=15.0):
                       f"(cost linear in batch)"}
 
 
+def full_flops(layers):
+    """Algorithmic flops of the full step per layer stack: SYRK (upper
+    triangle with diagonal, 2 flops per multiply-add: rows * d * (d + 1)),
+    preconditioning (2 d_g^2 d_a + 2 d_g d_a^2) and the damped inverse
+    (POTRF + TRTRI + LAUUM, d^3 / 3 each)."""
+    syrk = sum(L.rows * d * (d + 1) for L in layers for d in (L.d_a, L.d_out))
+    pre = sum(2 * L.d_out ** 2 * L.d_a + 2 * L.d_out * L.d_a ** 2 for L in layers)
+    inv = sum(L.d_a ** 3 + L.d_out ** 3 for L in layers)
+    return syrk, pre, inv
+
+
+def cpu_sample_layers(cfg):
+    """(layer indices, row divisor) of the CPU-baseline sample."""
+    n = len(cfg.layers)
+    if cfg.name == "mlp24_bf16":
+        return [0, 1], 1                   # one of 24 identical blocks
+    if cfg.name == "pair16k_bf16":
+        return [0], 8                      # the 4096->16384 layer at 2048 of 16384 tokens
+    if cfg.name == "resnet50_kfac":
+        return [0, 7, 20, 33, 46, n - 1], 1   # stem, 3x3 convs of each stage, FC
+    return list(range(n)), 1
+
+
+def cpu_baseline_full(cfg):
+    """The oracle's full step timed on a subset of the stack's layers, once as a
+    refresh step and once as a stale step; the amortised sample time is scaled
+    to the whole stack by the ratio of algorithmic flops."""
+    import dataclasses
+    import oracle
+    import synth
+    idx, div = cpu_sample_layers(cfg)
+    sub = [cfg.layers[i] if div == 1 else dataclasses.replace(cfg.layers[i], rows=cfg.layers[i].rows // div)
+           for i in idx]
+    scfg = dataclasses.replace(cfg, layers=tuple(sub))
+    hp = synth.hparams(cfg)
+    data = [(synth.initial_state(scfg, j), synth.step_inputs(scfg, 1, j)) for j in range(len(sub))]
+    times = {}
+    c0 = time.process_time()
+    w0 = time.perf_counter()
+    for refresh in (True, False):
+        t0 = time.perf_counter()
+        for (st, inp), L in zip(data, sub):
+            oracle.step_full(L, st, inp, hp, refresh)
+        times[refresh] = time.perf_counter() - t0
+    wall = time.perf_counter() - w0
+    cpu = time.process_time() - c0
+    k = cfg.refresh_every
+    t_sample = (times[True] + (k - 1) * times[False]) / k
+    fs, fp, fi = full_flops(sub)
+    ts, tp, ti = full_flops(cfg.layers)
+    scale = (ts + tp + ti / k) / (fs + fp + fi / k)
+    step_s = t_sample * scale
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": max(1, int(round(cpu / max(wall, 1e-9)))),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, full step on layers {idx} of {len(cfg.layers)}"
+                      f"{'' if div == 1 else f' at 1/{div} of the rows'}: refresh step "
+                      f"{times[True]:.2f} s, stale step {times[False]:.2f} s, amortised over a refresh interval "
+                      f"of {k}, scaled x{scale:.2f} by algorithmic flops"}
+
+
+def run_full(cfg, args):
+    import torch
+    import synth
+    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE
+    from second_order_optimizer_amd.stack import KfacStack
+
+    pool = max(1, args.pool)
+    st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype, pool=pool)
+    for li in range(len(cfg.layers)):
+        st.set_state(li, synth.initial_state(cfg, li))
+    for slot in range(pool):
+        for li in range(len(cfg.layers)):
+            st.set_inputs(li, synth.step_inputs(cfg, slot + 1, li), slot=slot)
+        log(f"[bench] input batch {slot + 1}/{pool} resident")
+    hp = synth.hparams(cfg)
+    k = cfg.refresh_every
+    steps = max(k, (args.steps + k - 1) // k * k)     # whole refresh intervals
+    H = {r: st.hparams(hp, refresh=r) for r in (True, False)}
+    torch.cuda.synchronize()
+    for i in range(max(1, args.warmup)):
+        st.use_inputs(i % pool)
+        st.step(H[i % k == 0])
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st.use_inputs(i % pool)
+        st.step(H[i % k == 0])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / steps
+    log(f"[bench] timed {steps} steps: {ms:.3f} ms/step")
+    stream = torch.cuda.current_stream()
+
+    def time_phase(mask, n, refresh=False):
+        Hm = st.hparams(hp, refresh=refresh, phase_mask=mask)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            st.use_inputs(i % pool)
+            evs[i][0].record(stream)
+            st.step(Hm)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
+    n = max(3, min(10, args.steps))
+    t_fac = time_phase(PHASE_FACTORS, n)
+    t_inv = time_phase(PHASE_INVERT, max(2, n // 3), refresh=True)
+    t_upd = time_phase(PHASE_UPDATE, n)
+    assert st.flags() == 0, "device flags raised"
+    fs, fp, fi = full_flops(cfg.layers)
+    syrk_peak = BF16_MFMA_TFLOPS if cfg.act_dtype == "bf16" else FP32_MFMA_TFLOPS
+    tf = lambda f, t: f / (t * 1e-3) / 1e12
+    phases = {
+        "factors": {"ms": t_fac, "tflops": tf(fs, t_fac), "peak": syrk_peak, "frac": tf(fs, t_fac) / syrk_peak,
+                    "flops": fs, "dtype": cfg.act_dtype},
+        "precond_update": {"ms": t_upd, "tflops": tf(fp, t_upd), "peak": FP32_MFMA_TFLOPS,
+                           "frac": tf(fp, t_upd) / FP32_MFMA_TFLOPS, "flops": fp, "dtype": "f32"},
+        "invert": {"ms": t_inv, "amortised_ms": t_inv / k, "tflops": tf(fi, t_inv), "peak": FP32_MFMA_TFLOPS,
+                   "frac": tf(fi, t_inv) / FP32_MFMA_TFLOPS, "flops": fi, "dtype": "f32"},
+    }
+    ideal = fs / (syrk_peak * 1e12) + fp / (FP32_MFMA_TFLOPS * 1e12)
+    phases["combined_mfma_frac"] = ideal / ((t_fac + t_upd) * 1e-3)
+    dom = max(("factors", t_fac), ("precond_update", t_upd), ("invert", t_inv / k), key=lambda x: x[1])[0]
+    names = {"factors": "factor SYRK + EMA launches (syrk_bf16_kernel / gemm_f32_kernel, EPI_SYM_EMA)",
+             "precond_update": "preconditioning GEMMs (gemm_f32_kernel, STORE then fused UPDATE epilogue)",
+             "invert": "blocked Cholesky inverse launches"}
+    d = phases[dom]
+    roof = {"bound": "mfma", "kernel": names[dom], "achieved": d["tflops"], "peak": d["peak"], "unit": "TFLOP/s",
+            "frac": d["frac"], "traffic": None, "flops_per_launch": d["flops"], "avg_launch_ms": d["ms"]}
+    return {"value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms, "dtype": cfg.act_dtype,
+            "roofline": roof, "phases": phases, "steps": steps}
+
+
 def run_diag(cfg, args):
     import torch
     import synth
@@ -190,14 +324,14 @@ def main():
     if cfg.variant == "diag":
         res = run_diag(cfg, args)
     else:
-        print(f"{cfg.name}: the full K-FAC step is not benchmarked yet", file=sys.stderr)
-        sys.exit(2)
+        res = run_full(cfg, args)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline_diag(cfg)
-    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+        cpu = cpu_baseline_diag(cfg) if cfg.variant == "diag" else cpu_baseline_full(cfg)
+    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+            "steps": res.get("steps", args.steps),
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": workload_desc(cfg),
             "roofline": res["roofline"], "cpu_baseline": cpu, "phases": res.get("phases")}

@@ -122,3 +122,89 @@ def test_full_deterministic(gpu_lib):
     for a, b in zip(*res):
         for k in a:
             assert np.array_equal(a[k], b[k]), k
+
+
+def _full_size_step(name):
+    import torch
+    from second_order_optimizer_amd.stack import KfacStack
+    cfg = synth.full_config(name)
+    hp = synth.hparams(cfg)
+    st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype)
+    inputs, init = [], []
+    for li in range(len(cfg.layers)):
+        s0 = synth.initial_state(cfg, li)
+        inp = synth.step_inputs(cfg, 1, li)
+        st.set_state(li, s0)
+        st.set_inputs(li, inp)
+        inputs.append(inp)
+        init.append(s0)
+    say(f"{name}: full-size inputs resident")
+    st.step(st.hparams(hp, refresh=True))
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    say(f"{name}: step done")
+    return cfg, hp, st, inputs, init
+
+
+@pytest.mark.parametrize("name", ["resnet50_kfac", "mlp24_bf16", "pair16k_bf16"])
+def test_full_size_sampled(gpu_lib, name):
+    """The workload at its stated size, in the launch configuration the
+    benchmark times (one refresh step from the synthetic state):
+      * factor entries (i, j) on sampled pairs vs the oracle's column products
+        (EMA from the identity), tolerance 1e-4 (fp32 inputs) / 2e-2 (bf16);
+      * inverse: on sampled columns, the exact float64 solve with the factor
+        the library produced agrees with the library's inverse to 1e-3;
+      * update: V1 - wd W0 = P satisfies (G + lam I) P (A + lam I) = grad on
+        sampled rows, relative to the gradient row."""
+    import scipy.linalg
+    cfg, hp, st, inputs, init = _full_size_step(name)
+    eps, lam = hp["ema_decay"], hp["damping"]
+    tol_f = 2e-2 if cfg.act_dtype == "bf16" else 1e-4
+    rng = np.random.default_rng(7)
+    layer_ids = range(len(cfg.layers))
+    if len(cfg.layers) > 12:
+        layer_ids = sorted(set([0, 1, len(cfg.layers) - 1] + list(rng.choice(len(cfg.layers), 6, replace=False))))
+    worst = {"A": 0.0, "G": 0.0, "inv": 0.0, "upd": 0.0}
+    for li in layer_ids:
+        L = cfg.layers[li]
+        got = st.get_state(li)
+        a, g = inputs[li]["a"], inputs[li]["g"]
+        # factors on sampled pairs
+        for key, d, col in (("A", L.d_a, lambda j: oracle.activation_column(L, a, j)),
+                            ("G", L.d_out, lambda j: oracle.gradient_column(L, g, j))):
+            idx = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, 4)]))
+            cols = {j: col(j) for j in idx}
+            ref = np.array([[eps * (i == j) + (1 - eps) * cols[i] @ cols[j] / L.rows for j in idx] for i in idx])
+            e = max_rel(got[key][np.ix_(idx, idx)], ref)
+            worst[key] = max(worst[key], e)
+            assert e <= tol_f, (L.name, key, e)
+        # inverse: exact float64 solve with the library's own factor, sampled columns
+        for key, ikey in (("A", "A_inv"), ("G", "G_inv")):
+            F = got[key].astype(np.float64)
+            d = F.shape[0]
+            F[np.diag_indices(d)] += lam
+            cf = scipy.linalg.cho_factor(F, lower=True)
+            js = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, 4)]))
+            E = np.zeros((d, len(js)))
+            E[js, np.arange(len(js))] = 1.0
+            X = scipy.linalg.cho_solve(cf, E)
+            e = max_rel(got[ikey][:, js], X)
+            worst["inv"] = max(worst["inv"], e)
+            assert e <= 1e-3, (L.name, ikey, e)
+        # update: P = V1 - wd W0 (V0 = 0); (G + lam I) P (A + lam I) = grad on sampled rows
+        W0 = np.concatenate([init[li]["w"], init[li]["b"][:, None]], 1) if L.has_bias else init[li]["w"]
+        V1 = np.concatenate([got["mom_w"], got["mom_b"][:, None]], 1) if L.has_bias else got["mom_w"]
+        W1 = np.concatenate([got["w"], got["b"][:, None]], 1) if L.has_bias else got["w"]
+        gr = inputs[li]["grad_w"].astype(np.float64)
+        if L.has_bias:
+            gr = np.concatenate([gr, inputs[li]["grad_b"][:, None]], 1)
+        P = V1.astype(np.float64) - hp["weight_decay"] * W0.astype(np.float64)
+        Ad = got["A"].astype(np.float64) + lam * np.eye(L.d_a)
+        Gd = got["G"].astype(np.float64) + lam * np.eye(L.d_out)
+        rows = np.unique(np.concatenate([[0, L.d_out - 1], rng.integers(0, L.d_out, 4)]))
+        lhs = (Gd[rows] @ P) @ Ad
+        e = max_rel(lhs, gr[rows])
+        worst["upd"] = max(worst["upd"], e)
+        assert e <= (2e-3 if cfg.act_dtype == "bf16" else 1e-3), (L.name, "update residual", e)
+        assert max_rel(W1, W0 - hp["lr"] * V1) <= 1e-6
+    say(f"{name} full-size worst:", {k: f"{v:.2e}" for k, v in worst.items()})
