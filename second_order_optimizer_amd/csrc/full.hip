@@ -318,20 +318,10 @@ kfac_status_t sym_reduce(const FullPlan& P, float* F, int d, int s, float eps, i
   return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
 }
 
-kfac_status_t syrk_bf16_ema(const uint16_t* X, int width, int64_t rows, int d, int special, float* F, float eps,
-                            const FullPlan& P, hipStream_t st) {
-  const int s = syrk_splits(d, rows);
-  if (s == 1)
-    return launch_syrk_bf16(X, width, rows, d, special, F, (1.0f - eps) / static_cast<float>(rows), eps, 1, 0, st);
-  kfac_status_t r = launch_syrk_bf16(X, width, rows, d, special, P.part, 1.f, 0.f, s,
-                                     static_cast<int64_t>(d) * d, st);
-  if (r != KFAC_OK) return r;
-  return sym_reduce(P, F, d, s, eps, rows, st);
-}
-
 kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                             hipStream_t st) {
   const float eps = hp.ema_decay;
+  std::vector<SyrkBf16Prob> bf16;   // all bf16 factors of the stack, one batched launch
   for (int li = 0; li < n; ++li) {
     const kfac_layer_t& L = layers[li];
     const LayerGeom g = geom_of(L);
@@ -351,11 +341,6 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
       if (r != KFAC_OK) return r;
       r = syrk_fp32(P.GT, g.d_out, g.rows, g.d_out, -1, L.G, eps, P, st);
       if (r != KFAC_OK) return r;
-    } else if (L.act_dtype == KFAC_F32 && L.grad_dtype == KFAC_F32) {
-      r = syrk_fp32(static_cast<const float*>(L.a), g.d_in, g.rows, g.d_a, special, L.A, eps, P, st);
-      if (r != KFAC_OK) return r;
-      r = syrk_fp32(static_cast<const float*>(L.g), g.d_out, g.rows, g.d_out, -1, L.G, eps, P, st);
-      if (r != KFAC_OK) return r;
     } else {
       for (int which = 0; which < 2; ++which) {
         const void* X = which == 0 ? L.a : L.g;
@@ -364,12 +349,24 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         const int d = which == 0 ? g.d_a : g.d_out;
         float* F = which == 0 ? L.A : L.G;
         const int sp = which == 0 ? special : -1;
-        if (dt == KFAC_F32) r = syrk_fp32(static_cast<const float*>(X), width, g.rows, d, sp, F, eps, P, st);
-        else r = syrk_bf16_ema(static_cast<const uint16_t*>(X), width, g.rows, d, sp, F, eps, P, st);
-        if (r != KFAC_OK) return r;
+        if (dt == KFAC_F32) {
+          r = syrk_fp32(static_cast<const float*>(X), width, g.rows, d, sp, F, eps, P, st);
+          if (r != KFAC_OK) return r;
+        } else {
+          SyrkBf16Prob q{};
+          q.X = static_cast<const uint16_t*>(X);
+          q.F = F;
+          q.rows = g.rows;
+          q.width = width;
+          q.bias = sp >= 0;
+          q.alpha = (1.0f - eps) / static_cast<float>(g.rows);
+          q.beta = eps;
+          bf16.push_back(q);
+        }
       }
     }
   }
+  if (!bf16.empty()) return launch_syrk_bf16(bf16, st);
   return KFAC_OK;
 }
 

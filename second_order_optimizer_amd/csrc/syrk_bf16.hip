@@ -1,13 +1,20 @@
-// Factor SYRK for bfloat16 inputs on CDNA4 bf16 matrix cores.
+// Factor SYRK for bfloat16 inputs on CDNA4 bf16 matrix cores, batched over
+// all bf16 factors of the stack.
 //
-// C[i][j] = sum_n X[n][i] X[n][j] over upper 128 x 128 tiles.  256 threads
-// (4 wavefronts, 2 x 2), each wavefront a 64 x 64 quarter as 2 x 2
-// v_mfma_f32_32x32x16_bf16 blocks.  K (the row index n) advances 32 per
-// stage.  The MFMA wants, per lane, 8 consecutive k of one column, so the
-// slab is stored in LDS column-major ([m][k], k contiguous): each thread
-// reads a 4 (rows) x 8 (columns) bf16 block with four 16-byte loads and
-// writes it transposed as eight 8-byte LDS stores.  Threads 0-127 stage the
-// row-tile operand, 128-255 the column-tile operand.
+// F <- beta F + alpha X^T X over upper 256 x 256 tiles, X = [rows, width]
+// row-major bf16.  512 threads (8 wavefronts, 2 x 4); each wavefront owns a
+// 128 x 64 part as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks (128 accumulators
+// per lane; two wavefronts per SIMD).  Each stage consumes 64 rows of X.  The MFMA wants 8 consecutive rows of one column per lane, so a
+// slab is kept in LDS column-major ([m][k], k contiguous, rows padded to 144
+// bytes, which makes both the 16-byte stores and the 16-byte MFMA operand
+// reads bank-conflict free): each thread reads an 8 x 8 bf16 block with
+// eight 16-byte loads (the next stage's, issued before this stage's MFMAs)
+// and writes it transposed with eight 16-byte LDS stores; threads 0-255
+// stage the row-tile operand, 256-511 the column-tile operand.  Diagonal
+// tiles stage one operand and skip their strictly-lower region.  With a bias
+// the constant-1 column is not materialised: the two otherwise idle
+// wavefronts of each diagonal tile multiply the slab by a ones operand,
+// which yields the column sums of X (the factor's last row and column).
 #include "syrk_bf16.h"
 
 #include <algorithm>
@@ -16,167 +23,228 @@ namespace kfac {
 
 namespace {
 
-constexpr int kT = 128;        // output tile
-constexpr int kK = 32;         // rows of X per stage
-constexpr int kRow = kK + 8;   // LDS row (bf16 elements) of one column, padded
-constexpr unsigned short kOne = 0x3F80;   // bf16 1.0
+constexpr int kBT = 256;        // block tile
+constexpr int kBK = 64;         // rows of X per stage
+constexpr int kLR = kBK + 8;    // LDS column length in bf16 (144 bytes)
+constexpr int kMaxProbs = 56;
 
-struct SyrkArgs {
+struct Prob {
   const uint16_t* X;
-  float* C;
-  int64_t split_stride;
+  float* F;
   int64_t rows;
-  int32_t width, d, special, tiles, nsplit, ldc;
+  int32_t width, bias, ldf, tiles, blk_begin, pad_;
   float alpha, beta;
 };
+struct Batch {
+  Prob p[kMaxProbs];
+  int32_t n;
+};
 
+__device__ inline int find_prob(const Batch& b, int blk) {
+  int lo = 0, hi = b.n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (b.p[mid].blk_begin <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// rows k .. k+7 of columns m .. m+7 (zero outside X)
 template <bool VEC>
-__device__ inline void load_block(u16x8 (&v)[4], const uint16_t* __restrict__ X, int64_t rows, int width,
-                                  int special, int64_t k, int m) {
+__device__ inline void load8(u16x8 (&v)[8], const uint16_t* __restrict__ X, int64_t rows, int width, int64_t k,
+                             int m) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t r = k + q;
-    u16x8 x;
-    if (VEC && r < rows && m + 8 <= width) {
-      x = *reinterpret_cast<const u16x8*>(X + r * width + m);
-    } else {
+  for (int r = 0; r < 8; ++r) {
+    const int64_t row = k + r;
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < rows) {
+      const uint16_t* p = X + row * width + m;
+      if (VEC && m + 8 <= width) {
+        x = *reinterpret_cast<const u16x8*>(p);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        unsigned short s = 0;
-        if (r < rows && m + e < width) s = X[r * width + m + e];
-        x[e] = s;
+        for (int e = 0; e < 8; ++e)
+          if (m + e < width) x[e] = p[e];
       }
     }
-    if (special >= m && special < m + 8 && r < rows) x[special - m] = kOne;
-    v[q] = x;
+    v[r] = x;
   }
 }
 
-__device__ inline void store_block(unsigned short* __restrict__ s, const u16x8 (&v)[4], int kk, int mm) {
-  // element (k = kk + q, m = mm + e) -> s[(mm + e) * kRow + kk + q]
+// element (k = kc*8 + r, m = mo*8 + e) -> s[(mo*8 + e) * kLR + kc*8 + r]
+__device__ inline void store_t(unsigned short* __restrict__ s, const u16x8 (&v)[8], int mo, int kc) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    u16x4 c = {v[0][e], v[1][e], v[2][e], v[3][e]};
-    *reinterpret_cast<u16x4*>(s + (mm + e) * kRow + kk) = c;
+    u16x8 w;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) w[r] = v[r][e];
+    *reinterpret_cast<u16x8*>(s + (mo * 8 + e) * kLR + kc * 8) = w;
   }
 }
 
-template <bool VEC, bool SPLIT>
-__global__ void __launch_bounds__(256) syrk_bf16_kernel(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned short sX[2][2][kT * kRow];
-  const int per = a.tiles * (a.tiles + 1) / 2;
-  int t = blockIdx.x;
-  const int split = t / per;
-  t -= split * per;
+template <bool VEC>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+syrk_bf16_kernel(Batch batch) {
+  __shared__ __attribute__((aligned(16))) unsigned short sX[2][2][kBT * kLR];
+  const Prob& P = batch.p[find_prob(batch, blockIdx.x)];
+  int t = blockIdx.x - P.blk_begin;
   int ti = 0;
-  while (t >= a.tiles - ti) { t -= a.tiles - ti; ++ti; }
+  while (t >= P.tiles - ti) { t -= P.tiles - ti; ++ti; }
   const int tj = ti + t;
-  const int i0 = ti * kT, j0 = tj * kT;
-  int64_t kb = 0, ke = a.rows;
-  if (SPLIT) {
-    const int64_t len = ((a.rows + a.nsplit - 1) / a.nsplit + kK - 1) / kK * kK;
-    kb = split * len;
-    ke = min(a.rows, kb + len);
-  }
-  float* C = a.C + (SPLIT ? split * a.split_stride : 0);
-
+  const bool diag = ti == tj;
+  const int i0 = ti * kBT, j0 = tj * kBT;
   const int tid = threadIdx.x;
-  const int half = tid >> 7;               // 0: row-tile operand, 1: column-tile operand
-  const int lt = tid & 127;
-  const int kk = (lt >> 4) * 4;            // 8 k-quads
-  const int mm = (lt & 15) * 8;            // 16 m-octets
-  const int m_base = half ? j0 : i0;
-
+  const int half = tid >> 8;                      // operand this thread stages
+  const int kc = tid & 7, mo = (tid & 255) >> 3;
+  const bool stager = !(diag && half == 1);       // a diagonal tile has one operand
   const int lane = tid & 63, wid = tid >> 6;
-  const int wm = (wid >> 1) * 64, wn = (wid & 1) * 64;
+  const int wm = (wid >> 2) * 128, wn = (wid & 3) * 64;
+  // In a diagonal tile the wavefronts over the strictly-lower region (rows
+  // 128.., columns ..127) have no output; with a bias they compute the column
+  // sums of the tile's columns instead (wave 4: columns 0..127, wave 5:
+  // 128..255, as acc[i][0]).
+  const bool work = !(diag && wm > wn + 63);
+  const bool colsum = P.bias && diag && !work;
+  const int cs0 = (wid & 1) * 128;
+  const int width = P.width;
+  const int64_t rows = P.rows;
+  const uint16_t* X = P.X;
+  const int mcol = (half ? j0 : i0) + mo * 8;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 
-  u16x8 v[4];
-  int buf = 0;
-  if (kb < ke) {
-    load_block<VEC>(v, a.X, ke, a.width, a.special, kb + kk, m_base + mm);
-    store_block(sX[0][half], v, kk, mm);
+  u16x8 v[8];
+  const int64_t nst = (rows + kBK - 1) / kBK;
+  if (stager) {
+    load8<VEC>(v, X, rows, width, kc * 8, mcol);
+    store_t(sX[0][half], v, mo, kc);
   }
   __syncthreads();
-  for (int64_t k0 = kb; k0 < ke; k0 += kK) {
-    const bool more = k0 + kK < ke;
-    if (more) load_block<VEC>(v, a.X, ke, a.width, a.special, k0 + kK + kk, m_base + mm);
+  int buf = 0;
+  for (int64_t s = 0; s < nst; ++s) {
+    const bool more = s + 1 < nst;
+    if (more && stager) load8<VEC>(v, X, rows, width, (s + 1) * kBK + kc * 8, mcol);
     const unsigned short* sa = sX[buf][0];
-    const unsigned short* sb = sX[buf][1];
+    const unsigned short* sb = diag ? sa : sX[buf][1];
+    if (work) {
 #pragma unroll
-    for (int ks = 0; ks < kK; ks += 16) {
-      const int ko = ks + 8 * (lane >> 5);
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(sa + (wm + (lane & 31)) * kRow + ko);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 + (lane & 31)) * kRow + ko);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sb + (wn + (lane & 31)) * kRow + ko);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 + (lane & 31)) * kRow + ko);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      for (int ks = 0; ks < kBK; ks += 16) {
+        const int ko = ks + 8 * (lane >> 5);
+        bf16x8 a[4], b[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i + (lane & 31)) * kLR + ko);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * j + (lane & 31)) * kLR + ko);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    } else if (colsum) {
+#pragma unroll
+      for (int ks = 0; ks < kBK; ks += 16) {
+        const int ko = ks + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(sa + (cs0 + 32 * i + (lane & 31)) * kLR + ko);
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, ones, acc[i][0], 0, 0, 0);
+        }
+      }
     }
-    if (more) store_block(sX[buf ^ 1][half], v, kk, mm);
+    if (more && stager) store_t(sX[buf ^ 1][half], v, mo, kc);
     __syncthreads();
     buf ^= 1;
   }
 
+  // accumulator r of block (i, j): row i0 + wm + 32 i + 8 (r/4) + 4 (lane/32) + r%4,
+  // column j0 + wn + 32 j + lane%32
+  float* F = P.F;
+  const int ldf = P.ldf;
+  if (work) {
 #pragma unroll
-  for (int si = 0; si < 2; ++si) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int sj = 0; sj < 2; ++sj) {
-      const int col = j0 + wn + 32 * sj + (lane & 31);
+      for (int j = 0; j < 2; ++j) {
+        const int col = j0 + wn + 32 * j + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= a.d || col >= a.d || row > col) continue;
-        const int64_t idx = static_cast<int64_t>(row) * a.ldc + col;
-        const float val = acc[si][sj][r];
-        if (SPLIT) {
-          C[idx] = val;
-        } else {
-          const float o = a.beta * C[idx] + a.alpha * val;
-          C[idx] = o;
-          if (row != col) C[static_cast<int64_t>(col) * a.ldc + row] = o;
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= width || col >= width || row > col) continue;
+          const int64_t idx = static_cast<int64_t>(row) * ldf + col;
+          const float o = P.beta * F[idx] + P.alpha * acc[i][j][r];
+          F[idx] = o;
+          if (row != col) F[static_cast<int64_t>(col) * ldf + row] = o;
         }
       }
+    }
+  }
+  if (colsum && (lane & 31) == 0) {
+    // every column of a ones-product block holds the same column sums of X
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = i0 + cs0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m >= width) continue;
+        const int64_t idx = static_cast<int64_t>(m) * ldf + width;
+        const float o = P.beta * F[idx] + P.alpha * acc[i][0][r];
+        F[idx] = o;
+        F[static_cast<int64_t>(width) * ldf + m] = o;
+      }
+    }
+    if (ti == 0 && cs0 == 0 && lane == 0) {
+      const int64_t c = static_cast<int64_t>(width) * ldf + width;
+      F[c] = P.beta * F[c] + P.alpha * static_cast<float>(rows);
     }
   }
 }
 
 }  // namespace
 
-kfac_status_t launch_syrk_bf16(const uint16_t* X, int width, int64_t rows, int d, int special, float* C,
-                               float alpha, float beta, int nsplit, int64_t split_stride, hipStream_t st) {
-  SyrkArgs a{};
-  a.X = X;
-  a.C = C;
-  a.split_stride = split_stride;
-  a.rows = rows;
-  a.width = width;
-  a.d = d;
-  a.special = special;
-  a.tiles = (d + kT - 1) / kT;
-  a.nsplit = std::max(1, nsplit);
-  a.ldc = d;
-  a.alpha = alpha;
-  a.beta = beta;
-  const int blocks = a.tiles * (a.tiles + 1) / 2 * a.nsplit;
-  const bool vec = (width % 8) == 0 && (reinterpret_cast<uintptr_t>(X) % 16) == 0;
-  if (a.nsplit > 1) {
-    if (vec) hipLaunchKernelGGL((syrk_bf16_kernel<true, true>), dim3(blocks), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((syrk_bf16_kernel<false, true>), dim3(blocks), dim3(256), 0, st, a);
-  } else {
-    if (vec) hipLaunchKernelGGL((syrk_bf16_kernel<true, false>), dim3(blocks), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((syrk_bf16_kernel<false, false>), dim3(blocks), dim3(256), 0, st, a);
+kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream_t st) {
+  // vector loads need 16-byte aligned rows; problems are launched per kind
+  for (int vec = 0; vec < 2; ++vec) {
+    size_t i = 0;
+    while (i < probs.size()) {
+      Batch b{};
+      int blocks = 0;
+      for (; i < probs.size() && b.n < kMaxProbs; ++i) {
+        const SyrkBf16Prob& q = probs[i];
+        const bool v = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
+        if (v != (vec == 1)) continue;
+        Prob p{};
+        p.X = q.X;
+        p.F = q.F;
+        p.rows = q.rows;
+        p.width = q.width;
+        p.bias = q.bias;
+        p.ldf = q.width + (q.bias ? 1 : 0);
+        p.tiles = (q.width + kBT - 1) / kBT;
+        p.alpha = q.alpha;
+        p.beta = q.beta;
+        p.blk_begin = blocks;
+        blocks += p.tiles * (p.tiles + 1) / 2;
+        b.p[b.n++] = p;
+      }
+      if (b.n == 0) continue;
+      if (vec) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
+      else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3(blocks), dim3(512), 0, st, b);
+      if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
+    }
   }
-  return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+  return KFAC_OK;
 }
 
 }  // namespace kfac
