@@ -109,6 +109,23 @@ struct MatTab {
   uint32_t* flags;
 };
 
+// Compact per-matrix view for the diagonal-block kernel (more matrices per launch).
+constexpr int kMaxDiagMats = 96;
+struct DMat {
+  float* L;
+  float* Z;
+  float* Dinv;
+  int32_t* fail;
+  int32_t d;
+  int32_t pad_;
+};
+struct DiagTab {
+  DMat m[kMaxDiagMats];
+  int32_t n;
+  int32_t k;
+  uint32_t* flags;
+};
+
 // L = F + damping I (from F's upper triangle, both triangles written), Z = 0,
 // fail = 0.  grid.y = matrix, grid.x strides rows.
 __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
@@ -127,73 +144,119 @@ __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
 }
 
 // Block k of every matrix with more than k blocks: Cholesky of the diagonal
-// block (right-looking, in LDS) fused with the forward substitution that
-// inverts it.  Writes L_kk (zero above the diagonal) into L, its inverse into
-// Dinv[k] and into Z's diagonal block.  A pivot that is not positive (or not
-// finite) marks the matrix failed, raises KFAC_FLAG_NOT_PD and is replaced
-// by 1 so the remaining steps stay finite; a failed matrix's inverse is not
-// written.
-__global__ void __launch_bounds__(256) chol_diag_kernel(MatTab T) {
-  __shared__ float Ls[kNb][kNb + 1];
-  __shared__ float Xs[kNb][kNb + 1];
-  __shared__ float piv;
-  const Mat& M = T.m[blockIdx.x];
+// block fused with the forward substitution that inverts it (right-looking,
+// column by column).  Thread (tr, tc) of a 16 x 16 grid keeps the 8 x 8
+// sub-block (rows 8 tr.., columns 8 tc..) of both the factor and the inverse
+// in registers; per column only the pivot, the scaled column of L and the
+// finished row of the inverse go through LDS (double-buffered, two barriers
+// per column).  Writes L_kk (zero above the diagonal) into L, its inverse
+// into Dinv[k] and into Z's diagonal block.  A pivot that is not positive (or
+// not finite) marks the matrix failed, raises KFAC_FLAG_NOT_PD and is
+// replaced by 1 so the remaining steps stay finite; a failed matrix's
+// inverse is not written.
+__global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
+  __shared__ __attribute__((aligned(16))) float colj[2][kNb];
+  __shared__ __attribute__((aligned(16))) float rowj[2][kNb];
+  __shared__ float pivs[2];
+  const DMat& M = T.m[blockIdx.x];
   const int d = M.d, k = T.k;
   const int nblk = (d + kNb - 1) / kNb;
   if (k >= nblk) return;
   const int r0 = k * kNb;
   const int bk = min(kNb, d - r0);
   const int tid = threadIdx.x;
-  float* Lg = M.L + static_cast<int64_t>(r0) * d + r0;
-  for (int e = tid; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e % kNb;
-    float v = 0.f;
-    if (r < bk && c <= r) v = Lg[static_cast<int64_t>(r) * d + c];
-    Ls[r][c] = v;
-    Xs[r][c] = (r == c && r < bk) ? 1.f : 0.f;
-  }
-  __syncthreads();
   const int tr = tid >> 4, tc = tid & 15;
-  for (int j = 0; j < bk; ++j) {
-    if (tid == 0) {
-      float p = Ls[j][j];
-      if (!(p > 0.f) || !isfinite(p)) {
-        if (*M.fail == 0) {
-          *M.fail = 1;
-          raise_flag(T.flags, KFAC_FLAG_NOT_PD);
+  const int R0 = tr * 8, C0 = tc * 8;
+  float* Lg = M.L + static_cast<int64_t>(r0) * d + r0;
+  float a[8][8], x[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = R0 + i, c = C0 + j;
+      a[i][j] = (r < bk && c <= r) ? Lg[static_cast<int64_t>(r) * d + c] : 0.f;
+      x[i][j] = (r < bk && r == c) ? 1.f : 0.f;
+    }
+  }
+  const int nbk = (bk + 7) / 8;
+  for (int jb = 0; jb < nbk; ++jb) {
+#pragma unroll
+    for (int jl = 0; jl < 8; ++jl) {
+      const int j = jb * 8 + jl;
+      if (j >= bk) break;
+      const int p = j & 1;
+      if (tr == jb && tc == jb) {
+        float v = a[jl][jl];
+        if (!(v > 0.f) || !isfinite(v)) {
+          if (*M.fail == 0) {
+            *M.fail = 1;
+            raise_flag(T.flags, KFAC_FLAG_NOT_PD);
+          }
+          v = 1.f;
         }
-        p = 1.f;
+        pivs[p] = sqrtf(v);
       }
-      piv = sqrtf(p);
-      Ls[j][j] = piv;
-    }
-    __syncthreads();
-    const float dj = piv;
-    const float inv = 1.0f / dj;
-    for (int r = j + 1 + tid; r < bk; r += 256) Ls[r][j] *= inv;
-    for (int c = tid; c <= j; c += 256) Xs[j][c] *= inv;
-    __syncthreads();
-    // trailing update of L (j < c <= r) and of the inverse rows below j (c <= j)
-    for (int r = j + 1 + tr; r < bk; r += 16) {
-      const float lr = Ls[r][j];
-      for (int c = tc; c <= r; c += 16) {
-        if (c > j) Ls[r][c] -= lr * Ls[c][j];
-        else Xs[r][c] -= lr * Xs[j][c];
+      __syncthreads();
+      const float s = pivs[p];
+      const float inv = 1.0f / s;
+      if (tc == jb) {                      // column j of L: scale below the pivot, publish all 128 rows
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = R0 + i;
+          const float v = a[i][jl] * inv;
+          a[i][jl] = r > j ? v : (r == j ? s : a[i][jl]);
+          colj[p][r] = r > j ? v : 0.f;
+        }
+      }
+      if (tr == jb) {                      // row j of the inverse is final once scaled
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          x[jl][c] *= inv;
+          rowj[p][C0 + c] = x[jl][c];
+        }
+      }
+      __syncthreads();
+      // Rank-1 updates, branch-free: colj is zero at rows <= j, so columns <= j
+      // of L and rows <= j of the inverse are left as they are; entries above
+      // the diagonal of L are never read and are zeroed at write-back; row j
+      // of the inverse is zero beyond column j.
+      if (tr >= tc) {
+        f32x4 cr0 = *reinterpret_cast<const f32x4*>(&colj[p][R0]);
+        f32x4 cr1 = *reinterpret_cast<const f32x4*>(&colj[p][R0 + 4]);
+        f32x4 cc0 = *reinterpret_cast<const f32x4*>(&colj[p][C0]);
+        f32x4 cc1 = *reinterpret_cast<const f32x4*>(&colj[p][C0 + 4]);
+        f32x4 rj0 = *reinterpret_cast<const f32x4*>(&rowj[p][C0]);
+        f32x4 rj1 = *reinterpret_cast<const f32x4*>(&rowj[p][C0 + 4]);
+        const float cr[8] = {cr0[0], cr0[1], cr0[2], cr0[3], cr1[0], cr1[1], cr1[2], cr1[3]};
+        const float cc[8] = {cc0[0], cc0[1], cc0[2], cc0[3], cc1[0], cc1[1], cc1[2], cc1[3]};
+        const float rj[8] = {rj0[0], rj0[1], rj0[2], rj0[3], rj1[0], rj1[1], rj1[2], rj1[3]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            a[i][c] = fmaf(-cr[i], cc[c], a[i][c]);
+            x[i][c] = fmaf(-cr[i], rj[c], x[i][c]);
+          }
+        }
       }
     }
-    __syncthreads();
   }
   // write back: L_kk (lower, zero above), Dinv[k] and Z_kk
   float* D = M.Dinv + static_cast<int64_t>(k) * kNb * kNb;
   float* Zg = M.Z + static_cast<int64_t>(r0) * d + r0;
-  for (int e = tid; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e % kNb;
-    const float l = c <= r ? Ls[r][c] : 0.f;
-    const float x = c <= r ? Xs[r][c] : 0.f;
-    D[e] = (r < bk && c < bk) ? x : 0.f;
-    if (r < bk && c < bk) {
-      Lg[static_cast<int64_t>(r) * d + c] = l;
-      Zg[static_cast<int64_t>(r) * d + c] = x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = R0 + i, c = C0 + j;
+      const bool in = r < bk && c < bk;
+      const float l = c <= r ? a[i][j] : 0.f;
+      const float xv = c <= r ? x[i][j] : 0.f;
+      D[r * kNb + c] = in ? xv : 0.f;
+      if (in) {
+        Lg[static_cast<int64_t>(r) * d + c] = l;
+        Zg[static_cast<int64_t>(r) * d + c] = xv;
+      }
     }
   }
 }
@@ -399,11 +462,24 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   if (r != KFAC_OK) return r;
   // blocked right-looking Cholesky
   for (int k = 0; k < nblk_max; ++k) {
-    r = tables([&](const Mat& m) { return static_cast<int>(nblk_of(m.d)) > k; }, k, [&](MatTab& T) {
-      hipLaunchKernelGGL(chol_diag_kernel, dim3(T.n), dim3(256), 0, st, T);
-      return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
-    });
-    if (r != KFAC_OK) return r;
+    {
+      DiagTab D{};
+      D.k = k;
+      D.flags = flags;
+      for (size_t mi = 0; mi <= mats.size(); ++mi) {
+        if (mi == mats.size() || D.n == kMaxDiagMats) {
+          if (D.n > 0) {
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, st, D);
+            KFAC_HIP_TRY(hipGetLastError());
+          }
+          D.n = 0;
+          if (mi == mats.size()) break;
+        }
+        const Mat& m = mats[mi];
+        if (static_cast<int>(nblk_of(m.d)) <= k) continue;
+        D.m[D.n++] = DMat{m.L, m.Z, m.Dinv, m.fail, m.d, 0};
+      }
+    }
     std::vector<GemmProb> panel, trail;
     for (const Mat& m : mats) {
       const int d = m.d;

@@ -1,11 +1,12 @@
 // Batched fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// A workgroup of 256 threads (4 wavefronts, 2 x 2) computes one 128 x 128
-// output tile; each wavefront owns a 64 x 64 quarter as 2 x 2 MFMA 32 x 32
-// blocks (64 accumulators per lane).  K advances 16 at a time: the next A/B
-// slabs are fetched into registers while the current ones, staged in LDS as
-// [k][m] rows (m contiguous, padded), feed the MFMAs.  fp32 in, fp32
-// accumulate, fp32 out.
+// Two tile shapes, picked per launch: 128 x 128 tiles on 256 threads (4
+// wavefronts of 64 x 64 = 2 x 2 MFMA 32 x 32 blocks) for small problem sets,
+// 256 x 256 tiles on 512 threads (8 wavefronts of 128 x 64 = 4 x 2 blocks)
+// when there are at least two such tiles per CU.  K advances 16 at a time:
+// the next A/B slabs are fetched into registers while the current ones,
+// staged in LDS as [k][m] rows (m contiguous, padded), feed the MFMAs.  fp32
+// in, fp32 accumulate, fp32 out.
 //
 // One launch runs a table of independent problems (layers, matrices, K
 // splits); each workgroup finds its problem by binary search over the
@@ -18,9 +19,21 @@ namespace kfac {
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kLdsPad = 4;
-constexpr int kLdsRow = kTile + kLdsPad;
+
+// Two shapes: SMALL = 128 x 128 tile, 4 wavefronts (2 x 2) of 64 x 64;
+// BIG = 256 x 256 tile, 8 wavefronts (2 x 4) of 128 x 64.
+template <bool BIG>
+struct Cfg {
+  static constexpr int kThreads = BIG ? 512 : 256;
+  static constexpr int kBT = BIG ? 256 : 128;          // output tile
+  static constexpr int kRow = kBT + kLdsPad;           // LDS row (floats)
+  static constexpr int kWavesN = BIG ? 4 : 2;
+  static constexpr int kWM = BIG ? 128 : 64;           // wavefront tile rows
+  static constexpr int kWN = 64;                       // wavefront tile cols
+  static constexpr int kBI = kWM / 32, kBJ = kWN / 32; // MFMA blocks per wavefront
+  static constexpr int kItems = kTileK * kBT / 4 / kThreads;   // float4 groups per thread per operand
+};
 
 struct GemmBatch {
   GemmProb p[kMaxGemmProbs];
@@ -37,19 +50,19 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
   return lo;
 }
 
-// Loads this thread's share of a 16 x 128 operand slab (8 floats) into regs.
-// MN layout: thread covers rows kk = t/32 and t/32 + 8, columns 4*(t%32)..+3.
-// K layout : thread covers rows mm = t/4 and t/4 + 64, k = 4*(t%4)..+3.
-template <int MODE, bool EXTRA>
-__device__ inline void load_slab(float (&r)[8], const float* __restrict__ base, int ld, int m0, int mlim, int k0,
-                                 int klim, int special, const float* __restrict__ extra) {
-  const int t = threadIdx.x;
-  if (MODE == OP_MN) {
-    const int mm = (t & 31) * 4;
+// This thread's share of a 16 x BT operand slab (kItems groups of 4 floats).
+// MN layout: group g covers row kk = g / (BT/4), columns 4 (g % (BT/4)) .. +3.
+// K layout : group g covers column mm = g / 4, k = 4 (g % 4) .. +3.
+template <bool BIG, int MODE, bool EXTRA>
+__device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
+                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra) {
+  using C = Cfg<BIG>;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + (t >> 5) + 8 * h;
-      const int m = m0 + mm;
+  for (int h = 0; h < C::kItems; ++h) {
+    const int g = threadIdx.x + h * C::kThreads;
+    if (MODE == OP_MN) {
+      const int k = k0 + g / (C::kBT / 4);
+      const int m = m0 + (g % (C::kBT / 4)) * 4;
       const bool kin = k < klim;
       const float* p = base + static_cast<int64_t>(k) * ld + m;
 #pragma unroll
@@ -61,13 +74,9 @@ __device__ inline void load_slab(float (&r)[8], const float* __restrict__ base, 
         }
         r[4 * h + q] = v;
       }
-    }
-  } else {
-    const int kq = (t & 3) * 4;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = m0 + (t >> 2) + 64 * h;
-      const int k = k0 + kq;
+    } else {
+      const int m = m0 + g / 4;
+      const int k = k0 + (g % 4) * 4;
       const bool min_ = m < mlim;
       const float* p = base + static_cast<int64_t>(m) * ld + k;
 #pragma unroll
@@ -83,24 +92,22 @@ __device__ inline void load_slab(float (&r)[8], const float* __restrict__ base, 
   }
 }
 
-template <int MODE>
-__device__ inline void store_slab(float* __restrict__ s, const float (&r)[8]) {
-  const int t = threadIdx.x;
-  if (MODE == OP_MN) {
-    const int mm = (t & 31) * 4;
+template <bool BIG, int MODE>
+__device__ inline void store_slab(float* __restrict__ s, const float (&r)[Cfg<BIG>::kItems * 4]) {
+  using C = Cfg<BIG>;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = (t >> 5) + 8 * h;
+  for (int h = 0; h < C::kItems; ++h) {
+    const int g = threadIdx.x + h * C::kThreads;
+    if (MODE == OP_MN) {
+      const int kk = g / (C::kBT / 4);
+      const int mm = (g % (C::kBT / 4)) * 4;
       f32x4 v = {r[4 * h], r[4 * h + 1], r[4 * h + 2], r[4 * h + 3]};
-      *reinterpret_cast<f32x4*>(s + kk * kLdsRow + mm) = v;
-    }
-  } else {
-    const int kq = (t & 3) * 4;
+      *reinterpret_cast<f32x4*>(s + kk * C::kRow + mm) = v;
+    } else {
+      const int mm = g / 4;
+      const int kq = (g % 4) * 4;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int mm = (t >> 2) + 64 * h;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) s[(kq + q) * kLdsRow + mm] = r[4 * h + q];
+      for (int q = 0; q < 4; ++q) s[(kq + q) * C::kRow + mm] = r[4 * h + q];
     }
   }
 }
@@ -126,14 +133,15 @@ __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti
   }
 }
 
-template <int AMODE, int BMODE, int EPI>
-__global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch batch) {
-  __shared__ float sA[2][kTileK * kLdsRow];
-  __shared__ float sB[2][kTileK * kLdsRow];
+template <int AMODE, int BMODE, int EPI, bool BIG>
+__global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch batch) {
+  using C = Cfg<BIG>;
+  __shared__ float sA[2][kTileK * C::kRow];
+  __shared__ float sB[2][kTileK * C::kRow];
   const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
-  const int i0 = ti * kTile, j0 = tj * kTile;
+  const int i0 = ti * C::kBT, j0 = tj * C::kBT;
   int kb = P.kb, ke = P.ke;
   if (P.k_from_diag) kb = max(kb, max(i0, j0));
   if (P.nsplit > 1) {
@@ -142,54 +150,56 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch batch) {
     ke = min(ke, s0 + len);
     kb = s0;
   }
-  float* C = P.C + static_cast<int64_t>(split) * P.split_stride;
+  float* Cp = P.C + static_cast<int64_t>(split) * P.split_stride;
   const float* Ab = static_cast<const float*>(P.A);
   const float* Bb = static_cast<const float*>(P.B);
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int wm = (wid >> 1) * 64, wn = (wid & 1) * 64;
+  const int wm = (wid / C::kWavesN) * C::kWM, wn = (wid % C::kWavesN) * C::kWN;
 
-  f32x16 acc[2][2];
+  f32x16 acc[C::kBI][C::kBJ];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < C::kBI; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < C::kBJ; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  float ra[8], rb[8];
+  float ra[C::kItems * 4], rb[C::kItems * 4];
   int buf = 0;
   if (kb < ke) {
-    load_slab<AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra);
-    load_slab<BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb);
-    store_slab<AMODE>(sA[0], ra);
-    store_slab<BMODE>(sB[0], rb);
+    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra);
+    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb);
+    store_slab<BIG, AMODE>(sA[0], ra);
+    store_slab<BIG, BMODE>(sB[0], rb);
   }
   __syncthreads();
   for (int k0 = kb; k0 < ke; k0 += kTileK) {
     const bool more = k0 + kTileK < ke;
     if (more) {
-      load_slab<AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra);
-      load_slab<BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb);
+      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra);
+      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb);
     }
     const float* a = sA[buf];
     const float* b = sB[buf];
 #pragma unroll
     for (int kk = 0; kk < kTileK; kk += 2) {
-      const int row = (kk + (lane >> 5)) * kLdsRow;
-      const float a0 = a[row + wm + (lane & 31)];
-      const float a1 = a[row + wm + 32 + (lane & 31)];
-      const float b0 = b[row + wn + (lane & 31)];
-      const float b1 = b[row + wn + 32 + (lane & 31)];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      const int row = (kk + (lane >> 5)) * C::kRow;
+      float af[C::kBI], bf[C::kBJ];
+#pragma unroll
+      for (int i = 0; i < C::kBI; ++i) af[i] = a[row + wm + 32 * i + (lane & 31)];
+#pragma unroll
+      for (int j = 0; j < C::kBJ; ++j) bf[j] = b[row + wn + 32 * j + (lane & 31)];
+#pragma unroll
+      for (int i = 0; i < C::kBI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kBJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if (more) {
-      store_slab<AMODE>(sA[buf ^ 1], ra);
-      store_slab<BMODE>(sB[buf ^ 1], rb);
+      store_slab<BIG, AMODE>(sA[buf ^ 1], ra);
+      store_slab<BIG, BMODE>(sB[buf ^ 1], rb);
     }
     __syncthreads();
     buf ^= 1;
@@ -201,9 +211,9 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch batch) {
   bool skip = false;
   if (EPI == EPI_SYM_IFOK) skip = *P.fail != 0;
 #pragma unroll
-  for (int si = 0; si < 2; ++si) {
+  for (int si = 0; si < C::kBI; ++si) {
 #pragma unroll
-    for (int sj = 0; sj < 2; ++sj) {
+    for (int sj = 0; sj < C::kBJ; ++sj) {
       const int col = j0 + wn + 32 * sj + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -212,19 +222,19 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch batch) {
         const float v = acc[si][sj][r];
         const int64_t idx = static_cast<int64_t>(row) * P.ldc + col;
         if (EPI == EPI_STORE) {
-          C[idx] = P.alpha * v;
+          Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SUB) {
-          C[idx] -= v;
+          Cp[idx] -= v;
         } else if (EPI == EPI_SYM_EMA) {
           if (row <= col) {
-            const float o = P.beta * C[idx] + P.alpha * v;
-            C[idx] = o;
-            if (row != col) C[static_cast<int64_t>(col) * P.ldc + row] = o;
+            const float o = P.beta * Cp[idx] + P.alpha * v;
+            Cp[idx] = o;
+            if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
         } else if (EPI == EPI_SYM_IFOK) {
           if (row <= col && !skip) {
-            C[idx] = v;
-            if (row != col) C[static_cast<int64_t>(col) * P.ldc + row] = v;
+            Cp[idx] = v;
+            if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = v;
           }
         } else if (EPI == EPI_UPDATE) {
           float* wp;
@@ -253,14 +263,15 @@ __global__ void __launch_bounds__(kThreads) gemm_f32_kernel(GemmBatch batch) {
 }
 
 template <int AM, int BM, int EPI>
-kfac_status_t launch_group(const GemmBatch& b, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI>), dim3(blocks), dim3(kThreads), 0, s, b);
+kfac_status_t launch_group(const GemmBatch& b, int blocks, bool big, hipStream_t s) {
+  if (big) hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, true>), dim3(blocks), dim3(512), 0, s, b);
+  else hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, false>), dim3(blocks), dim3(256), 0, s, b);
   return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
 }
 
-kfac_status_t dispatch(const GemmBatch& b, int blocks, int am, int bm, int epi, hipStream_t s) {
+kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm, int epi, hipStream_t s) {
 #define KFAC_GEMM_CASE(A_, B_, E_) \
-  if (am == A_ && bm == B_ && epi == E_) return launch_group<A_, B_, E_>(b, blocks, s);
+  if (am == A_ && bm == B_ && epi == E_) return launch_group<A_, B_, E_>(b, blocks, big, s);
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYM_EMA)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_UPDATE)
@@ -273,6 +284,12 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, int am, int bm, int epi, 
   return KFAC_ERR_UNSUPPORTED;
 }
 
+int tiles_for(const GemmProb& p, int bt) {
+  const int tm = (p.M + bt - 1) / bt, tn = (p.N + bt - 1) / bt;
+  const int per = p.tri == TRI_FULL ? tm * tn : tm * (tm + 1) / 2;
+  return per * std::max(1, p.nsplit);
+}
+
 }  // namespace
 
 void gemm_set_tiles(GemmProb& p) {
@@ -280,13 +297,15 @@ void gemm_set_tiles(GemmProb& p) {
   p.tiles_n = (p.N + kTile - 1) / kTile;
 }
 
-int gemm_blocks(const GemmProb& p) {
-  const int per = p.tri == TRI_FULL ? p.tiles_m * p.tiles_n : p.tiles_m * (p.tiles_m + 1) / 2;
-  return per * std::max(1, p.nsplit);
-}
+int gemm_blocks(const GemmProb& p) { return tiles_for(p, kTile); }
 
 kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
                           hipStream_t stream) {
+  // 256 x 256 tiles when the launch still has at least two tiles per CU
+  int big_tiles = 0;
+  for (const GemmProb& p : probs) big_tiles += tiles_for(p, 2 * kTile);
+  const bool big = big_tiles >= 512;
+  const int bt = big ? 2 * kTile : kTile;
   size_t i = 0;
   while (i < probs.size()) {
     GemmBatch b{};
@@ -296,18 +315,17 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
     for (; i < probs.size() && n < kMaxGemmProbs; ++i) {
       GemmProb p = probs[i];
       if (p.nsplit < 1) p.nsplit = 1;
-      const int nb = gemm_blocks(p);
-      if (nb == 0 || p.ke <= p.kb) {
-        // empty contraction: only EPI_STORE / EPI_SYM_EMA must still write; callers avoid it
-        if (nb == 0) continue;
-      }
+      p.tiles_m = (p.M + bt - 1) / bt;
+      p.tiles_n = (p.N + bt - 1) / bt;
+      const int nb = tiles_for(p, bt);
+      if (nb == 0) continue;
       p.blk_begin = blocks;
       blocks += nb;
       b.p[n++] = p;
     }
     if (n == 0) continue;
     b.n = n;
-    kfac_status_t st = dispatch(b, blocks, amode, bmode, epi, stream);
+    kfac_status_t st = dispatch(b, blocks, big, amode, bmode, epi, stream);
     if (st != KFAC_OK) return st;
   }
   return KFAC_OK;
