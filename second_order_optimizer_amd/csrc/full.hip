@@ -126,19 +126,37 @@ struct DiagTab {
   uint32_t* flags;
 };
 
-// L = F + damping I (from F's upper triangle, both triangles written), Z = 0,
-// fail = 0.  grid.y = matrix, grid.x strides rows.
+// L = F + damping I from F's upper triangle (both triangles of L written),
+// Z = 0, fail = 0.  grid = (32 x 32 tiles, matrix); a lower tile (I > J) is
+// read from F's upper tile (J, I) row by row and transposed through LDS.
 __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
+  __shared__ float t[32][33];
   const Mat& M = T.m[blockIdx.y];
   const int d = M.d;
+  const int nt = (d + 31) / 32;
   if (blockIdx.x == 0 && threadIdx.x == 0) *M.fail = 0;
-  for (int i = blockIdx.x; i < d; i += gridDim.x) {
-    for (int j = threadIdx.x; j < d; j += 256) {
-      const int lo = min(i, j), hi = max(i, j);
-      float v = M.F[static_cast<int64_t>(lo) * d + hi];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
+    const int I = tile / nt, J = tile - (tile / nt) * nt;
+    const bool lower = I > J;
+    const int sr = (lower ? J : I) * 32, sc = (lower ? I : J) * 32;   // source tile in the upper triangle
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+      const int i = sr + r, j = sc + tx;
+      t[r][tx] = (i < d && j < d) ? M.F[static_cast<int64_t>(i) * d + j] : 0.f;
+    }
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+      const int i = I * 32 + r, j = J * 32 + tx;
+      if (i >= d || j >= d) continue;
+      float v;
+      if (lower) v = t[tx][r];
+      else if (I == J) v = t[min(r, tx)][max(r, tx)];   // diagonal tile: mirror its upper part
+      else v = t[r][tx];
       if (i == j) v += T.damping;
-      M.L[static_cast<int64_t>(i) * d + j] = v;
-      M.Z[static_cast<int64_t>(i) * d + j] = 0.f;
+      const int64_t e = static_cast<int64_t>(i) * d + j;
+      M.L[e] = v;
+      M.Z[e] = 0.f;
     }
   }
 }
@@ -456,7 +474,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     return T.n > 0 ? fn(T) : KFAC_OK;
   };
   kfac_status_t r = tables([](const Mat&) { return true; }, 0, [&](MatTab& T) {
-    hipLaunchKernelGGL(chol_init_kernel, dim3(64, T.n), dim3(256), 0, st, T);
+    hipLaunchKernelGGL(chol_init_kernel, dim3(2048, T.n), dim3(256), 0, st, T);
     return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
   });
   if (r != KFAC_OK) return r;

@@ -51,6 +51,7 @@ struct GemmProb {
   int32_t d_in;           // EPI_UPDATE: columns < d_in go to W / V
   int32_t nsplit;         // K splits (each writes C + s * split_stride)
   int32_t blk_begin;
+  int32_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
   float alpha, beta;
 };
 

@@ -27,7 +27,9 @@ template <bool BIG>
 struct Cfg {
   static constexpr int kThreads = BIG ? 512 : 256;
   static constexpr int kBT = BIG ? 256 : 128;          // output tile
-  static constexpr int kRow = kBT + kLdsPad;           // LDS row (floats)
+  static constexpr int kRow = kBT + kLdsPad;           // MN operand: LDS row of one k (floats)
+  static constexpr int kKRow = kTileK + 1;             // K operand: LDS row of one m (odd: conflict-free reads)
+  static constexpr int kSlab = (kTileK * kRow > kBT * kKRow) ? kTileK * kRow : kBT * kKRow;
   static constexpr int kWavesN = BIG ? 4 : 2;
   static constexpr int kWM = BIG ? 128 : 64;           // wavefront tile rows
   static constexpr int kWN = 64;                       // wavefront tile cols
@@ -55,7 +57,7 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
 // K layout : group g covers column mm = g / 4, k = 4 (g % 4) .. +3.
 template <bool BIG, int MODE, bool EXTRA>
 __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
-                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra) {
+                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec) {
   using C = Cfg<BIG>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
@@ -65,6 +67,11 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
       const int m = m0 + (g % (C::kBT / 4)) * 4;
       const bool kin = k < klim;
       const float* p = base + static_cast<int64_t>(k) * ld + m;
+      if (vec && kin && m + 3 < mlim && (special < m || special > m + 3)) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        r[4 * h] = v[0]; r[4 * h + 1] = v[1]; r[4 * h + 2] = v[2]; r[4 * h + 3] = v[3];
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v = 0.f;
@@ -79,6 +86,11 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
       const int k = k0 + (g % 4) * 4;
       const bool min_ = m < mlim;
       const float* p = base + static_cast<int64_t>(m) * ld + k;
+      if (vec && min_ && k + 3 < klim && (!EXTRA || special < k || special > k + 3)) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+        r[4 * h] = v[0]; r[4 * h + 1] = v[1]; r[4 * h + 2] = v[2]; r[4 * h + 3] = v[3];
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v = 0.f;
@@ -107,7 +119,7 @@ __device__ inline void store_slab(float* __restrict__ s, const float (&r)[Cfg<BI
       const int mm = g / 4;
       const int kq = (g % 4) * 4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s[(kq + q) * C::kRow + mm] = r[4 * h + q];
+      for (int q = 0; q < 4; ++q) s[mm * C::kKRow + kq + q] = r[4 * h + q];
     }
   }
 }
@@ -136,8 +148,8 @@ __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti
 template <int AMODE, int BMODE, int EPI, bool BIG>
 __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch batch) {
   using C = Cfg<BIG>;
-  __shared__ float sA[2][kTileK * C::kRow];
-  __shared__ float sB[2][kTileK * C::kRow];
+  __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
+  __shared__ __attribute__((aligned(16))) float sB[2][C::kSlab];
   const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
@@ -169,8 +181,8 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   float ra[C::kItems * 4], rb[C::kItems * 4];
   int buf = 0;
   if (kb < ke) {
-    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra);
-    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb);
+    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec);
+    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec);
     store_slab<BIG, AMODE>(sA[0], ra);
     store_slab<BIG, BMODE>(sB[0], rb);
   }
@@ -178,19 +190,25 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   for (int k0 = kb; k0 < ke; k0 += kTileK) {
     const bool more = k0 + kTileK < ke;
     if (more) {
-      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra);
-      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb);
+      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec);
+      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec);
     }
     const float* a = sA[buf];
     const float* b = sB[buf];
 #pragma unroll
     for (int kk = 0; kk < kTileK; kk += 2) {
-      const int row = (kk + (lane >> 5)) * C::kRow;
+      const int kl = kk + (lane >> 5);
       float af[C::kBI], bf[C::kBJ];
 #pragma unroll
-      for (int i = 0; i < C::kBI; ++i) af[i] = a[row + wm + 32 * i + (lane & 31)];
+      for (int i = 0; i < C::kBI; ++i) {
+        const int m = wm + 32 * i + (lane & 31);
+        af[i] = AMODE == OP_MN ? a[kl * C::kRow + m] : a[m * C::kKRow + kl];
+      }
 #pragma unroll
-      for (int j = 0; j < C::kBJ; ++j) bf[j] = b[row + wn + 32 * j + (lane & 31)];
+      for (int j = 0; j < C::kBJ; ++j) {
+        const int n = wn + 32 * j + (lane & 31);
+        bf[j] = BMODE == OP_MN ? b[kl * C::kRow + n] : b[n * C::kKRow + kl];
+      }
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i)
 #pragma unroll
@@ -317,6 +335,8 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
       if (p.nsplit < 1) p.nsplit = 1;
       p.tiles_m = (p.M + bt - 1) / bt;
       p.tiles_n = (p.N + bt - 1) / bt;
+      p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
+      p.b_vec = (p.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0 && (p.kb % 4) == 0;
       const int nb = tiles_for(p, bt);
       if (nb == 0) continue;
       p.blk_begin = blocks;
