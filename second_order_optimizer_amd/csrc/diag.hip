@@ -66,7 +66,8 @@ struct FinTask {
   int32_t blk_begin;
   float scale;
   int32_t bias_index;                       // >= 0: dst[bias_index] = 1
-  int32_t tpb;                              // FIN_WINDOW: taps per block
+  int32_t tpb;                              // FIN_WINDOW: taps per unit (channel, tap group)
+  int32_t upw;                              // FIN_WINDOW: 0 = one unit per block, else units per wavefront
 };
 struct FinTasks {
   FinTask t[kMaxFinTasks];
@@ -124,19 +125,20 @@ __global__ void __launch_bounds__(kColThreads) diag_colsq_kernel(ColTasks tasks)
     const float* p = T.src + r0 * K + c0;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
     int64_t r = r0;
-    for (; r + 8 <= r1; r += 8) {
-      f32x4 v[8];
+    for (; r + 16 <= r1; r += 16) {
+      f32x4 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(p + u * static_cast<int64_t>(K));
+      for (int u = 0; u < 16; ++u)
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + u * static_cast<int64_t>(K)));
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
+      for (int u = 0; u < 16; u += 2) {
         acc0 += v[u] * v[u];
         acc1 += v[u + 1] * v[u + 1];
       }
-      p += 8 * static_cast<int64_t>(K);
+      p += 16 * static_cast<int64_t>(K);
     }
     for (; r < r1; ++r) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(p);
+      f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
       acc0 += v * v;
       p += K;
     }
@@ -164,7 +166,7 @@ __device__ inline float wave_sum(float v) {
 
 __global__ void __launch_bounds__(kFinThreads) diag_finish_kernel(FinTasks tasks) {
   __shared__ float red[kFinThreads / kWave][kMaxTpb];
-  const int ti = find_task(tasks.t, tasks.n, blockIdx.x);
+  const int ti = find_task(tasks.t, tasks.n, blockIdx.x);  // uniform per block
   const FinTask& T = tasks.t[ti];
   const int b = blockIdx.x - T.blk_begin;
   if (T.bias_index >= 0 && b == 0 && threadIdx.x == 0) T.dst[T.bias_index] = 1.0f;
@@ -177,46 +179,83 @@ __global__ void __launch_bounds__(kFinThreads) diag_finish_kernel(FinTasks tasks
     }
     return;
   }
-  // FIN_WINDOW: block b -> (channel c, tap group tg of `tpb` taps); threads
-  // stride over the output positions and add S at each tap's input pixel.
+  // FIN_WINDOW.  A unit is (channel c, tap group of `tpb` taps): the sum of S
+  // at each tap's input pixel over all output positions.  Large units take a
+  // block each (positions spread over 256 threads, block reduction); small
+  // units (few output positions) go to single wavefronts, `upw` each, with a
+  // shuffle reduction and no block barrier.
   const int k = T.k, taps = k * k, tpb = T.tpb;
   const int groups = (taps + tpb - 1) / tpb;
-  const int c = b / groups, tg = b - c * groups;
-  const int t0 = tg * tpb, nt = min(tpb, taps - t0);
-  const float* S = T.src + static_cast<int64_t>(c) * T.H * T.W;
-  float acc[kMaxTpb];
-  int dh[kMaxTpb], dw[kMaxTpb];
-#pragma unroll
-  for (int t = 0; t < kMaxTpb; ++t) {
-    acc[t] = 0.f;
-    const int tap = t0 + (t < nt ? t : 0);
-    dh[t] = tap / k - T.pad;
-    dw[t] = tap % k - T.pad;
-  }
+  const int units = T.C * groups;
   const int npos = T.Ho * T.Wo;
-  for (int q = threadIdx.x; q < npos; q += kFinThreads) {
-    const int ho = q / T.Wo, wo = q - (q / T.Wo) * T.Wo;
-    const int hb = ho * T.stride, wb = wo * T.stride;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int nthr = T.upw ? kWave : kFinThreads;
+  const int tix = T.upw ? lane : threadIdx.x;
+  const int ubeg = T.upw ? (b * (kFinThreads / kWave) + wid) * T.upw : b;
+  const int uend = T.upw ? min(units, ubeg + T.upw) : b + 1;
+  for (int unit = ubeg; unit < uend; ++unit) {
+    const int c = unit / groups, tg = unit - c * groups;
+    const int t0 = tg * tpb, nt = min(tpb, taps - t0);
+    const float* S = T.src + static_cast<int64_t>(c) * T.H * T.W;
+    float acc[kMaxTpb];
+    int dh[kMaxTpb], dw[kMaxTpb];
 #pragma unroll
     for (int t = 0; t < kMaxTpb; ++t) {
-      if (t >= nt) break;
-      const int hh = hb + dh[t], ww = wb + dw[t];
-      if (hh >= 0 && hh < T.H && ww >= 0 && ww < T.W) acc[t] += S[hh * T.W + ww];
+      acc[t] = 0.f;
+      const int tap = t0 + (t < nt ? t : 0);
+      dh[t] = tap / k - T.pad;
+      dw[t] = tap % k - T.pad;
     }
-  }
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    // 8 independent loads in flight per thread per tap; the thread's output
+    // position advances by nthr each time, (ho, wo) stepped without division
+    const int sh = nthr / T.Wo, sw = nthr - sh * T.Wo;
+    int ho = tix / T.Wo, wo = tix - (tix / T.Wo) * T.Wo;
+    for (int q0 = tix; q0 < npos; q0 += nthr * 8) {
+      int hb[8], wb[8];
 #pragma unroll
-  for (int t = 0; t < kMaxTpb; ++t) {
-    if (t >= nt) break;
-    const float v = wave_sum(acc[t]);
-    if (lane == 0) red[wid][t] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < nt) {
-    float v = 0.f;
+      for (int u = 0; u < 8; ++u) {
+        hb[u] = q0 + u * nthr < npos ? ho * T.stride : -(1 << 20);   // out of range -> every tap invalid
+        wb[u] = wo * T.stride;
+        ho += sh;
+        wo += sw;
+        if (wo >= T.Wo) { wo -= T.Wo; ++ho; }
+      }
 #pragma unroll
-    for (int w = 0; w < kFinThreads / kWave; ++w) v += red[w][threadIdx.x];
-    T.dst[static_cast<int64_t>(c) * taps + t0 + threadIdx.x] = v * T.scale;
+      for (int t = 0; t < kMaxTpb; ++t) {
+        if (t >= nt) break;
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int hh = hb[u] + dh[t], ww = wb[u] + dw[t];
+          v[u] = (hh >= 0 && hh < T.H && ww >= 0 && ww < T.W) ? S[hh * T.W + ww] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[t] += v[u];
+      }
+    }
+    float* out = T.dst + static_cast<int64_t>(c) * taps + t0;
+    if (T.upw) {
+#pragma unroll
+      for (int t = 0; t < kMaxTpb; ++t) {
+        if (t >= nt) break;
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) out[t] = v * T.scale;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kMaxTpb; ++t) {
+        if (t >= nt) break;
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) red[wid][t] = v;
+      }
+      __syncthreads();
+      if (threadIdx.x < nt) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFinThreads / kWave; ++w) v += red[w][threadIdx.x];
+        out[threadIdx.x] = v * T.scale;
+      }
+    }
   }
 }
 
@@ -308,15 +347,28 @@ struct DiagPlan {
   size_t ws_bytes = kFlagBytes;
 };
 
-// Taps per finishing block: about 4096 position-taps of work per block.
+// Taps per unit: about 4096 position-taps of work per unit.
 int window_tpb(int k, int positions) {
   const int taps = k * k;
   int tpb = std::max(1, 4096 / std::max(1, positions));
   return std::min(std::min(tpb, kMaxTpb), taps);
 }
 
+// Units per wavefront for small units (<= 1024 output positions): each unit
+// costs a load round trip, so a wavefront takes at most 4; 0 = one unit per
+// block.
+int window_upw(int tpb, int positions) {
+  if (positions > 1024) return 0;
+  return std::min(4, std::max(1, 4096 / std::max(1, tpb * positions)));
+}
+
 int fin_blocks(const FinTask& t) {
-  if (t.kind == FIN_WINDOW) return t.C * ((t.k * t.k + t.tpb - 1) / t.tpb);
+  if (t.kind == FIN_WINDOW) {
+    const int units = t.C * ((t.k * t.k + t.tpb - 1) / t.tpb);
+    if (t.upw == 0) return units;
+    const int per_block = t.upw * (kFinThreads / kWave);
+    return (units + per_block - 1) / per_block;
+  }
   return t.chunks > 1 ? (t.K + kFinThreads - 1) / kFinThreads : 1;
 }
 
@@ -364,6 +416,7 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
       fx.C = g.c_in; fx.H = g.h; fx.W = g.w; fx.k = g.kh; fx.stride = g.stride; fx.pad = g.pad;
       fx.Ho = g.h_out; fx.Wo = g.w_out; fx.scale = invN; fx.bias_index = g.bias ? g.d_in : -1;
       fx.tpb = window_tpb(g.kh, g.h_out * g.w_out);
+      fx.upw = window_upw(fx.tpb, g.h_out * g.w_out);
       add_fin(fx, fin_blocks(fx));
       const int Kg = g.d_out * g.h_out * g.w_out;
       float* Sg = carve(Kg);
@@ -373,6 +426,7 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
       fg.C = g.d_out; fg.H = g.h_out; fg.W = g.w_out; fg.k = 1; fg.stride = 1; fg.pad = 0;
       fg.Ho = g.h_out; fg.Wo = g.w_out; fg.scale = invN; fg.bias_index = -1;
       fg.tpb = 1;
+      fg.upw = window_upw(1, g.h_out * g.w_out);
       add_fin(fg, fin_blocks(fg));
     } else {
       const int64_t R = g.rows;
