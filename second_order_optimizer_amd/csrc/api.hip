@@ -47,6 +47,8 @@ kfac_status_t check_shape(const kfac_layer_t& L, int mode) {
         L.pad < 0)
       return KFAC_ERR_ARG;
     if (L.kh != L.kw || L.kh > 7) return KFAC_ERR_UNSUPPORTED;
+    // convolution inputs and gradients are read as float32
+    if (L.act_dtype != KFAC_F32 || L.grad_dtype != KFAC_F32) return KFAC_ERR_DTYPE;
     const int64_t ho = (static_cast<int64_t>(L.height) + 2 * L.pad - L.kh) / L.stride + 1;
     const int64_t wo = (static_cast<int64_t>(L.width) + 2 * L.pad - L.kw) / L.stride + 1;
     if (L.height + 2 * L.pad < L.kh || L.width + 2 * L.pad < L.kw || ho <= 0 || wo <= 0) return KFAC_ERR_ARG;

@@ -1,6 +1,8 @@
 // Full K-FAC step (Osawa et al., section 3.2): per layer
 //   [FACTORS] A <- eps A + (1 - eps) a_bar^T a_bar / N, G likewise (SYRK on
-//             matrix cores, EMA fused into the epilogue, upper tiles mirrored)
+//             matrix cores, EMA fused into the epilogue, upper tiles mirrored;
+//             convolution rows are gathered im2col-style inside the GEMM
+//             loader, never materialised)
 //   [INVERT]  (A + lambda I)^-1, (G + lambda I)^-1 by a blocked Cholesky
 //             factorisation, a blocked triangular inverse and Z^T Z, batched
 //             over all factors of the stack (section 4.2: damping)
@@ -21,69 +23,55 @@ namespace {
 constexpr int kNb = kTile;   // Cholesky block size = GEMM tile
 
 // ---------------------------------------------------------------------------
-// im2col: U[n][j] = x[b][c][ho*s - p + kh][wo*s - p + kw], n = (b*Ho + ho)*Wo + wo,
-// j = (c*k + kh)*k + kw; one thread per output element (writes coalesced).
-__global__ void __launch_bounds__(256) unfold_kernel(const float* __restrict__ x, float* __restrict__ U, int C,
-                                                     int H, int W, int k, int s, int p, int Ho, int Wo,
-                                                     int64_t total, int dcols) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int64_t n = e / dcols;
-  const int j = static_cast<int>(e - n * dcols);
-  const int wo = static_cast<int>(n % Wo);
-  const int64_t t = n / Wo;
-  const int ho = static_cast<int>(t % Ho);
-  const int b = static_cast<int>(t / Ho);
-  const int c = j / (k * k);
-  const int r = j - c * k * k;
-  const int kh = r / k, kw = r - (r / k) * k;
-  const int hh = ho * s - p + kh, ww = wo * s - p + kw;
-  float v = 0.f;
-  if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = x[((static_cast<int64_t>(b) * C + c) * H + hh) * W + ww];
-  U[e] = v;
-}
+// Split-K SYRK finish, batched over factors: F[i][j] = beta F[i][j] +
+// alpha * sum_s part[s][i][j] on the upper triangle, in split order, and the
+// mirrored lower triangle.  One block per 32 x 32 upper tile; the mirror goes
+// through LDS so both writes are row-contiguous.
+constexpr int kMaxReds = 64;
+struct SymRedItem {
+  const float* part;
+  float* F;
+  int32_t d, nsplit, blk_begin, pad_;
+  float alpha, beta;
+};
+struct SymRedTab {
+  SymRedItem r[kMaxReds];
+  int32_t n;
+};
 
-// g [B][C][P] -> gT [B*P][C] through a 32 x 32 LDS tile.
-__global__ void __launch_bounds__(256) nchw_rows_kernel(const float* __restrict__ g, float* __restrict__ out,
-                                                        int C, int P) {
+__global__ void __launch_bounds__(256) sym_reduce_kernel(SymRedTab tab) {
   __shared__ float t[32][33];
-  const int b = blockIdx.z;
-  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
-  const float* src = g + static_cast<int64_t>(b) * C * P;
-  float* dst = out + static_cast<int64_t>(b) * P * C;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  int lo = 0, hi = tab.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.r[mid].blk_begin <= static_cast<int>(blockIdx.x)) lo = mid; else hi = mid - 1;
+  }
+  const SymRedItem& R = tab.r[lo];
+  const int T = (R.d + 31) / 32;
+  int u = blockIdx.x - R.blk_begin, I = 0;
+  while (u >= T - I) { u -= T - I; ++I; }
+  const int J = I + u;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t dd = static_cast<int64_t>(R.d) * R.d;
   for (int r = ty; r < 32; r += 8) {
-    const int c = c0 + r, p = p0 + tx;
-    t[r][tx] = (c < C && p < P) ? src[static_cast<int64_t>(c) * P + p] : 0.f;
+    const int i = I * 32 + r, j = J * 32 + tx;
+    float o = 0.f;
+    if (i < R.d && j < R.d) {
+      const int64_t e = static_cast<int64_t>(i) * R.d + j;
+      float sum = 0.f;
+      for (int k = 0; k < R.nsplit; ++k) sum += R.part[k * dd + e];
+      o = R.beta * R.F[e] + R.alpha * sum;
+      if (I != J || i <= j) R.F[e] = o;
+    }
+    t[r][tx] = o;
   }
   __syncthreads();
   for (int r = ty; r < 32; r += 8) {
-    const int p = p0 + r, c = c0 + tx;
-    if (p < P && c < C) dst[static_cast<int64_t>(p) * C + c] = t[tx][r];
+    const int i = J * 32 + r, j = I * 32 + tx;   // lower tile (J, I) = transpose of (I, J)
+    if (i >= R.d || j >= R.d) continue;
+    if (I == J && i <= j) continue;
+    R.F[static_cast<int64_t>(i) * R.d + j] = t[tx][r];
   }
-}
-
-// Split-K SYRK finish: F[i][j] = beta F[i][j] + alpha sum_s part[s][i][j] for
-// i <= j, mirrored.  Partial sums are added in split order.
-struct SymRed {
-  const float* part;
-  float* F;
-  int64_t stride;
-  int32_t d, nsplit;
-  float alpha, beta;
-};
-
-__global__ void __launch_bounds__(256) sym_reduce_kernel(SymRed r) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t dd = static_cast<int64_t>(r.d) * r.d;
-  if (e >= dd) return;
-  const int i = static_cast<int>(e / r.d), j = static_cast<int>(e - static_cast<int64_t>(i) * r.d);
-  if (i > j) return;
-  float s = 0.f;
-  for (int k = 0; k < r.nsplit; ++k) s += r.part[k * r.stride + e];
-  const float o = r.beta * r.F[e] + r.alpha * s;
-  r.F[e] = o;
-  if (i != j) r.F[static_cast<int64_t>(j) * r.d + i] = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -284,24 +272,23 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
 
 struct FullPlan {
   size_t ws_bytes = kFlagBytes;
-  // per-layer scratch (shared, layers run one after another in FACTORS)
-  float* U = nullptr;
-  float* GT = nullptr;
-  float* part = nullptr;
-  size_t part_floats = 0;
+  std::vector<float*> part;      // per layer and factor (2 li + which): split-K partials, or null
+  std::vector<int> nsplit;       // per layer and factor
   std::vector<float*> T;         // per layer, d_out x d_a
   std::vector<Mat> mats;         // inverse work per factor
 };
 
 size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
 
-// SYRK split count: enough workgroups to cover the chip, at least 2048 rows per split.
-int syrk_splits(int d, int64_t rows) {
-  const int T = (d + kTile - 1) / kTile;
-  const int tiles = T * (T + 1) / 2;
-  int s = std::max(1, 512 / tiles);
-  s = static_cast<int>(std::min<int64_t>(s, std::max<int64_t>(1, rows / 2048)));
-  return std::min(s, 256);
+// K splits of an fp32 factor SYRK: at most 16384 rows per split, so that the
+// tallest factors (a stem convolution's 401,408 rows) do not serialise the
+// launch; the partial sums are added by sym_reduce_kernel in split order.
+int syrk_splits(int64_t rows) {
+  return static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (rows + 16383) / 16384)));
+}
+
+bool fp32_factor(const kfac_layer_t& L, int which) {
+  return (which == 0 ? L.act_dtype : L.grad_dtype) == KFAC_F32;
 }
 
 FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool refresh) {
@@ -312,24 +299,16 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
     off = align_up(off + bytes, 256);
     return p;
   };
-  size_t u_floats = 0, gt_floats = 0, part_floats = 0;
+  // all regions are always carved so the size does not depend on the phases
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
-    if (g.conv) {
-      u_floats = std::max(u_floats, static_cast<size_t>(g.rows) * g.d_in);
-      gt_floats = std::max(gt_floats, static_cast<size_t>(g.rows) * g.d_out);
-    }
     for (int which = 0; which < 2; ++which) {
       const int d = which == 0 ? g.d_a : g.d_out;
-      const int s = syrk_splits(d, g.rows);
-      if (s > 1) part_floats = std::max(part_floats, static_cast<size_t>(s) * d * d);
+      const int s = fp32_factor(layers[li], which) ? syrk_splits(g.rows) : 1;
+      P.nsplit.push_back(s);
+      P.part.push_back(s > 1 ? reinterpret_cast<float*>(carve(static_cast<size_t>(s) * d * d * 4)) : nullptr);
     }
   }
-  // all regions are always carved so the size does not depend on the phases
-  P.U = reinterpret_cast<float*>(carve(u_floats * 4));
-  P.GT = reinterpret_cast<float*>(carve(gt_floats * 4));
-  P.part = reinterpret_cast<float*>(carve(part_floats * 4));
-  P.part_floats = part_floats;
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
     P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * g.d_a * 4)));
@@ -355,100 +334,119 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   return P;
 }
 
-kfac_status_t sym_reduce(const FullPlan& P, float* F, int d, int s, float eps, int64_t rows, hipStream_t st);
-
-kfac_status_t syrk_fp32(const float* X, int width, int64_t rows, int d, int special, float* F, float eps,
-                        const FullPlan& P, hipStream_t st) {
-  const int s = syrk_splits(d, rows);
-  GemmProb p{};
-  p.A = X;
-  p.B = X;
-  p.lda = p.ldb = width;
-  p.M = p.N = d;
-  p.kb = 0;
-  p.ke = static_cast<int>(rows);
-  p.tri = TRI_UPPER;
-  p.a_special = p.b_special = special;
-  gemm_set_tiles(p);
-  GemmScalars sc{};
-  std::vector<GemmProb> v;
-  if (s == 1) {
-    p.C = F;
-    p.ldc = d;
-    p.nsplit = 1;
-    p.alpha = (1.0f - eps) / static_cast<float>(rows);
-    p.beta = eps;
-    v.push_back(p);
-    return launch_gemm(v, OP_MN, OP_MN, EPI_SYM_EMA, sc, st);
+kfac_status_t launch_sym_reduce(const std::vector<SymRedItem>& items, hipStream_t st) {
+  for (size_t i0 = 0; i0 < items.size(); i0 += kMaxReds) {
+    SymRedTab tab{};
+    int blocks = 0;
+    for (size_t i = i0; i < std::min(items.size(), i0 + kMaxReds); ++i) {
+      SymRedItem r = items[i];
+      const int T = (r.d + 31) / 32;
+      r.blk_begin = blocks;
+      blocks += T * (T + 1) / 2;
+      tab.r[tab.n++] = r;
+    }
+    hipLaunchKernelGGL(sym_reduce_kernel, dim3(blocks), dim3(256), 0, st, tab);
+    KFAC_HIP_TRY(hipGetLastError());
   }
-  p.C = P.part;
-  p.ldc = d;
-  p.nsplit = s;
-  p.split_stride = static_cast<int64_t>(d) * d;
-  p.alpha = 1.0f;
-  v.push_back(p);
-  kfac_status_t r = launch_gemm(v, OP_MN, OP_MN, EPI_STORE, sc, st);
-  if (r != KFAC_OK) return r;
-  return sym_reduce(P, F, d, s, eps, rows, st);
+  return KFAC_OK;
 }
 
-kfac_status_t sym_reduce(const FullPlan& P, float* F, int d, int s, float eps, int64_t rows, hipStream_t st) {
-  SymRed red{P.part, F, static_cast<int64_t>(d) * d, d, s, (1.0f - eps) / static_cast<float>(rows), eps};
-  const int64_t dd = static_cast<int64_t>(d) * d;
-  hipLaunchKernelGGL(sym_reduce_kernel, dim3(static_cast<unsigned>((dd + 255) / 256)), dim3(256), 0, st, red);
-  return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
-}
-
+// FACTORS: every factor of the stack in a few batched launches, one per
+// operand kind (row-major fp32, implicit im2col, NCHW gradient, bf16), each
+// split into direct-EMA and split-K problems; then the batched split reduce.
 kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                             hipStream_t st) {
   const float eps = hp.ema_decay;
-  std::vector<SyrkBf16Prob> bf16;   // all bf16 factors of the stack, one batched launch
+  enum { K_MN = 0, K_IM2COL = 1, K_NCHW = 2 };
+  std::vector<GemmProb> direct[3], split[3];
+  std::vector<SymRedItem> reds;
+  std::vector<SyrkBf16Prob> bf16;
   for (int li = 0; li < n; ++li) {
     const kfac_layer_t& L = layers[li];
     const LayerGeom g = geom_of(L);
-    const int special = g.bias ? g.d_in : -1;
-    kfac_status_t r;
-    if (g.conv) {
-      const int64_t total = g.rows * static_cast<int64_t>(g.d_in);
-      hipLaunchKernelGGL(unfold_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
-                         static_cast<const float*>(L.a), P.U, g.c_in, g.h, g.w, g.kh, g.stride, g.pad, g.h_out,
-                         g.w_out, total, g.d_in);
-      KFAC_HIP_TRY(hipGetLastError());
-      const int Pp = g.h_out * g.w_out;
-      hipLaunchKernelGGL(nchw_rows_kernel, dim3((Pp + 31) / 32, (g.d_out + 31) / 32, g.batch), dim3(256), 0, st,
-                         static_cast<const float*>(L.g), P.GT, g.d_out, Pp);
-      KFAC_HIP_TRY(hipGetLastError());
-      r = syrk_fp32(P.U, g.d_in, g.rows, g.d_a, special, L.A, eps, P, st);
-      if (r != KFAC_OK) return r;
-      r = syrk_fp32(P.GT, g.d_out, g.rows, g.d_out, -1, L.G, eps, P, st);
-      if (r != KFAC_OK) return r;
-    } else {
-      for (int which = 0; which < 2; ++which) {
-        const void* X = which == 0 ? L.a : L.g;
-        const int dt = which == 0 ? L.act_dtype : L.grad_dtype;
-        const int width = which == 0 ? g.d_in : g.d_out;
-        const int d = which == 0 ? g.d_a : g.d_out;
-        float* F = which == 0 ? L.A : L.G;
-        const int sp = which == 0 ? special : -1;
-        if (dt == KFAC_F32) {
-          r = syrk_fp32(static_cast<const float*>(X), width, g.rows, d, sp, F, eps, P, st);
-          if (r != KFAC_OK) return r;
-        } else {
-          SyrkBf16Prob q{};
-          q.X = static_cast<const uint16_t*>(X);
-          q.F = F;
-          q.rows = g.rows;
-          q.width = width;
-          q.bias = sp >= 0;
-          q.alpha = (1.0f - eps) / static_cast<float>(g.rows);
-          q.beta = eps;
-          bf16.push_back(q);
-        }
+    for (int which = 0; which < 2; ++which) {
+      const int d = which == 0 ? g.d_a : g.d_out;
+      const int special = (which == 0 && g.bias) ? g.d_in : -1;
+      float* F = which == 0 ? L.A : L.G;
+      const void* X = which == 0 ? L.a : L.g;
+      const float alpha = (1.0f - eps) / static_cast<float>(g.rows);
+      if (!fp32_factor(L, which)) {
+        SyrkBf16Prob q{};
+        q.X = static_cast<const uint16_t*>(X);
+        q.F = F;
+        q.rows = g.rows;
+        q.width = which == 0 ? g.d_in : g.d_out;
+        q.bias = special >= 0;
+        q.alpha = alpha;
+        q.beta = eps;
+        bf16.push_back(q);
+        continue;
+      }
+      GemmProb p{};
+      p.A = X;
+      p.B = X;
+      p.M = p.N = d;
+      p.kb = 0;
+      p.ke = static_cast<int>(g.rows);
+      p.tri = TRI_UPPER;
+      p.a_special = p.b_special = special;
+      int kind;
+      if (!g.conv) {
+        kind = K_MN;
+        p.lda = p.ldb = which == 0 ? g.d_in : g.d_out;
+      } else if (which == 0) {
+        kind = K_IM2COL;
+        const int geo[8] = {g.c_in, g.h, g.w, g.kh, g.stride, g.pad, g.h_out, g.w_out};
+        for (int e = 0; e < 8; ++e) p.geo[e] = geo[e];
+      } else {
+        kind = K_NCHW;
+        p.geo[0] = g.h_out * g.w_out;
+        p.geo[1] = g.d_out;
+      }
+      const int s = P.nsplit[2 * li + which];
+      if (s == 1) {
+        p.C = F;
+        p.ldc = d;
+        p.nsplit = 1;
+        p.alpha = alpha;
+        p.beta = eps;
+        direct[kind].push_back(p);
+      } else {
+        p.C = P.part[2 * li + which];
+        p.ldc = d;
+        p.nsplit = s;
+        p.split_stride = static_cast<int64_t>(d) * d;
+        p.alpha = 1.0f;
+        split[kind].push_back(p);
+        SymRedItem r{};
+        r.part = p.C;
+        r.F = F;
+        r.d = d;
+        r.nsplit = s;
+        r.alpha = alpha;
+        r.beta = eps;
+        reds.push_back(r);
       }
     }
   }
-  if (!bf16.empty()) return launch_syrk_bf16(bf16, st);
-  return KFAC_OK;
+  GemmScalars sc{};
+  const int modes[3] = {OP_MN, OP_IM2COL, OP_NCHW};
+  kfac_status_t r;
+  for (int kind = 0; kind < 3; ++kind) {
+    if (!split[kind].empty()) {
+      r = launch_gemm(split[kind], modes[kind], modes[kind], EPI_STORE, sc, st);
+      if (r != KFAC_OK) return r;
+    }
+    if (!direct[kind].empty()) {
+      r = launch_gemm(direct[kind], modes[kind], modes[kind], EPI_SYM_EMA, sc, st);
+      if (r != KFAC_OK) return r;
+    }
+  }
+  if (!bf16.empty()) {
+    r = launch_syrk_bf16(bf16, st);
+    if (r != KFAC_OK) return r;
+  }
+  return reds.empty() ? KFAC_OK : launch_sym_reduce(reds, st);
 }
 
 kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st) {

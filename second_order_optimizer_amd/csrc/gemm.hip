@@ -37,6 +37,20 @@ struct Cfg {
   static constexpr int kItems = kTileK * kBT / 4 / kThreads;   // float4 groups per thread per operand
 };
 
+// LDS layout of an operand mode: [k][m] rows for i-contiguous (and im2col)
+// operands, [m][k] rows for k-contiguous (and NCHW-gradient) ones.
+__host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K || mode == OP_NCHW; }
+
+// Per-thread column decomposition of an im2col operand, fixed for the whole K
+// loop: for each of the thread's 4 * kItems columns, the offset of (c, kh, kw)
+// inside a sample and the (kh, kw) tap for the padding test.
+template <bool BIG>
+struct ColInfo {
+  int off[8];
+  int kh[8];
+  int kw[8];
+};
+
 struct GemmBatch {
   GemmProb p[kMaxGemmProbs];
   int32_t n;
@@ -55,9 +69,33 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
 // This thread's share of a 16 x BT operand slab (kItems groups of 4 floats).
 // MN layout: group g covers row kk = g / (BT/4), columns 4 (g % (BT/4)) .. +3.
 // K layout : group g covers column mm = g / 4, k = 4 (g % 4) .. +3.
+template <bool BIG, int MODE>
+__device__ inline void col_info(ColInfo<BIG>& ci, const int* geo, int m0, int mlim, int special) {
+  using C = Cfg<BIG>;
+  static_assert(C::kItems * 4 <= 8, "column info holds 8 columns");
+  if (MODE != OP_IM2COL) return;
+  const int k = geo[GEO_K], HW = geo[GEO_H] * geo[GEO_W];
+#pragma unroll
+  for (int h = 0; h < C::kItems; ++h) {
+    const int g = threadIdx.x + h * C::kThreads;
+    const int m = m0 + (g % (C::kBT / 4)) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int mq = m + q;
+      const int c = mq / (k * k), r = mq - c * k * k;
+      const int kh = r / k, kw = r - (r / k) * k;
+      const bool real = mq < mlim && mq != special;
+      ci.off[4 * h + q] = c * HW + kh * geo[GEO_W] + kw;
+      ci.kh[4 * h + q] = real ? kh : -(1 << 20);   // never inside the image
+      ci.kw[4 * h + q] = kw;
+    }
+  }
+}
+
 template <bool BIG, int MODE, bool EXTRA>
 __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
-                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec) {
+                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec,
+                                 const int* geo, const ColInfo<BIG>& ci) {
   using C = Cfg<BIG>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
@@ -80,6 +118,46 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
           else if (m + q < mlim) v = p[q];
         }
         r[4 * h + q] = v;
+      }
+    } else if (MODE == OP_IM2COL) {
+      // row n = (b, ho, wo) of the unfolded input; columns from the column info
+      const int n = k0 + g / (C::kBT / 4);
+      const int m = m0 + (g % (C::kBT / 4)) * 4;
+      const int HoWo = geo[GEO_HO] * geo[GEO_WO];
+      const int b = n / HoWo, rem = n - b * HoWo;
+      const int ho = rem / geo[GEO_WO], wo = rem - (rem / geo[GEO_WO]) * geo[GEO_WO];
+      const int hb = ho * geo[GEO_S] - geo[GEO_P], wb = wo * geo[GEO_S] - geo[GEO_P];
+      const int H = geo[GEO_H], W = geo[GEO_W];
+      const int64_t row = static_cast<int64_t>(b) * geo[GEO_C] * H * W + hb * W + wb;   // may be < 0 (padding)
+      const bool kin = n < klim;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * h + q;
+        const int hh = hb + ci.kh[e], ww = wb + ci.kw[e];
+        float v = 0.f;
+        if (kin) {
+          if (m + q == special) v = 1.0f;
+          else if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = base[row + ci.off[e]];
+        }
+        r[e] = v;
+      }
+    } else if (MODE == OP_NCHW) {
+      // element (m = channel, n = b * P + p) at base[(b * channels + m) * P + p]
+      const int m = m0 + g / 4;
+      const int k = k0 + (g % 4) * 4;
+      const int P = geo[0], ch = geo[1];
+      const bool min_ = m < mlim;
+      const int b0 = k / P, p0 = k - b0 * P;
+      if (vec && min_ && k + 3 < klim && p0 + 3 < P) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(base + (static_cast<int64_t>(b0) * ch + m) * P + p0);
+        r[4 * h] = v[0]; r[4 * h + 1] = v[1]; r[4 * h + 2] = v[2]; r[4 * h + 3] = v[3];
+        continue;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = k + q;
+        const int b = n / P, p = n - b * P;
+        r[4 * h + q] = (min_ && n < klim) ? base[(static_cast<int64_t>(b) * ch + m) * P + p] : 0.f;
       }
     } else {
       const int m = m0 + g / 4;
@@ -110,7 +188,7 @@ __device__ inline void store_slab(float* __restrict__ s, const float (&r)[Cfg<BI
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
     const int g = threadIdx.x + h * C::kThreads;
-    if (MODE == OP_MN) {
+    if (!k_major(MODE)) {
       const int kk = g / (C::kBT / 4);
       const int mm = (g % (C::kBT / 4)) * 4;
       f32x4 v = {r[4 * h], r[4 * h + 1], r[4 * h + 2], r[4 * h + 3]};
@@ -179,10 +257,13 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   float ra[C::kItems * 4], rb[C::kItems * 4];
+  ColInfo<BIG> cia, cib;
+  col_info<BIG, AMODE>(cia, P.geo, i0, P.M, P.a_special);
+  col_info<BIG, BMODE>(cib, P.geo, j0, P.N, P.b_special);
   int buf = 0;
   if (kb < ke) {
-    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec);
-    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec);
+    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec, P.geo, cia);
+    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec, P.geo, cib);
     store_slab<BIG, AMODE>(sA[0], ra);
     store_slab<BIG, BMODE>(sB[0], rb);
   }
@@ -190,8 +271,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   for (int k0 = kb; k0 < ke; k0 += kTileK) {
     const bool more = k0 + kTileK < ke;
     if (more) {
-      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec);
-      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec);
+      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec, P.geo,
+                                  cia);
+      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec, P.geo, cib);
     }
     const float* a = sA[buf];
     const float* b = sB[buf];
@@ -202,12 +284,12 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i) {
         const int m = wm + 32 * i + (lane & 31);
-        af[i] = AMODE == OP_MN ? a[kl * C::kRow + m] : a[m * C::kKRow + kl];
+        af[i] = !k_major(AMODE) ? a[kl * C::kRow + m] : a[m * C::kKRow + kl];
       }
 #pragma unroll
       for (int j = 0; j < C::kBJ; ++j) {
         const int n = wn + 32 * j + (lane & 31);
-        bf[j] = BMODE == OP_MN ? b[kl * C::kRow + n] : b[n * C::kKRow + kl];
+        bf[j] = !k_major(BMODE) ? b[kl * C::kRow + n] : b[n * C::kKRow + kl];
       }
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i)
@@ -298,6 +380,10 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_SUB)
+  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_SYM_EMA)
+  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_STORE)
+  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_SYM_EMA)
+  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_STORE)
 #undef KFAC_GEMM_CASE
   return KFAC_ERR_UNSUPPORTED;
 }
@@ -337,6 +423,7 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
       p.tiles_n = (p.N + bt - 1) / bt;
       p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
       p.b_vec = (p.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0 && (p.kb % 4) == 0;
+      if (amode == OP_NCHW) p.a_vec = p.b_vec = (p.geo[0] % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0;
       const int nb = tiles_for(p, bt);
       if (nb == 0) continue;
       p.blk_begin = blocks;

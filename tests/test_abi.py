@@ -114,6 +114,8 @@ def test_conv_shape_errors(lib, bad, code):
 def test_diag_rejects_bf16(lib):
     assert _ws_status([_linear(act_dtype=K.BF16)], K.MODE_DIAG)[0] == K.KFAC_ERR_DTYPE
     assert _ws_status([_linear(act_dtype=K.BF16, grad_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_OK
+    # convolution inputs are read as float32 in both methods
+    assert _ws_status([_conv(act_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_ERR_DTYPE
 
 
 def _call(fn, layers, hp, ws, ws_bytes):

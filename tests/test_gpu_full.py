@@ -50,6 +50,18 @@ def test_fp32_linear_split_k(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
+def test_conv_split_k_and_layouts(gpu_lib):
+    """Convolution factors gathered im2col-style inside the GEMM: a 7x7/2 stem
+    with more rows than one K split (16,900 rows -> 2 splits), an output plane
+    whose size is not a multiple of 4 (scalar gradient loads) and one that is
+    (vector loads), a conv with a bias column."""
+    L = [synth.conv("stem", 3, 8, 7, 2, 3, 4, 130),
+         synth.conv("odd_plane", 5, 7, 3, 1, 1, 3, 7),
+         synth.conv("even_plane", 6, 9, 3, 2, 1, 2, 16, bias=True)]
+    cfg = with_layers(synth.small_config("resnet50_kfac"), L, steps=2)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
 def test_sgd_reduction_update_phase(gpu_lib):
     """UPDATE phase alone with identity inverses: the step is SGD with momentum
     and weight decay (closed form from the oracle's update)."""
