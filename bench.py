@@ -27,6 +27,9 @@ FP32_MFMA_TFLOPS = 157.3       # dense fp32 MFMA
 BF16_MFMA_TFLOPS = 2500.0      # dense bf16 MFMA
 
 METRIC = "K-FAC steps/s per layer stack; factor+precond TFLOP/s (%MFMA); diag-step GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "diag_colsq_resnet18_b128_traffic.md")
+DIAG_SRC = os.path.join(ROOT, "second_order_optimizer_amd", "csrc", "diag.hip")
+COPY_BYTES = 1 << 30     # the --traffic-probe calibration copy reads and writes 1 GiB
 
 
 def log(*a):
@@ -230,6 +233,56 @@ def run_full(cfg, args):
             "roofline": roof, "phases": phases, "steps": steps}
 
 
+def source_sha256(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of diag_colsq_kernel from the committed counter
+    summary, or None when it is missing or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("    ") and ":" in line:
+            k, v = line.strip().split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_sha256(DIAG_SRC):
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe(args):
+    """What the FETCH_SIZE / WRITE_SIZE passes profile: a plain 1 GiB device
+    copy (calibration of the counters) and `--steps` FACTORS-only diagonal
+    calls on ResNet-18 @ 128 (each one launch of diag_colsq_kernel)."""
+    import torch
+    import synth
+    from second_order_optimizer_amd import PHASE_FACTORS
+    from second_order_optimizer_amd.stack import KfacStack
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    cfg = synth.full_config("resnet18_diag")
+    st = KfacStack(cfg.layers, "diag")
+    for li in range(len(cfg.layers)):
+        st.set_state(li, synth.initial_state(cfg, li))
+        st.set_inputs(li, synth.step_inputs(cfg, 1, li))
+    H = st.hparams(synth.hparams(cfg), phase_mask=PHASE_FACTORS)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        st.step(H)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES, "factor_calls": args.steps,
+                      "diag_src_sha256": source_sha256(DIAG_SRC)}), flush=True)
+
+
 def run_diag(cfg, args):
     import torch
     import synth
@@ -285,7 +338,7 @@ def run_diag(cfg, args):
     out = {
         "value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms, "dtype": "f32",
         "roofline": {"bound": "hbm", "kernel": "diag_colsq_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "bytes_per_launch": fb, "avg_launch_ms": t_fac},
         "phases": {"factors_ms": t_fac, "update_ms": t_upd,
                    "update_GBps": ub / (t_upd * 1e-3) / 1e9,
@@ -302,6 +355,8 @@ def main():
     ap.add_argument("--config", default="resnet18_diag")
     ap.add_argument("--pool", type=int, default=2, help="pre-loaded input batches cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only what the FETCH_SIZE / WRITE_SIZE counter passes measure")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -319,6 +374,9 @@ def main():
     if args.config not in synth.CONFIG_NAMES:
         print(f"unknown config {args.config}; choose from {synth.CONFIG_NAMES}", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
     cfg = synth.full_config(args.config)
     log(f"[bench] {cfg.name}: {len(cfg.layers)} layers, {cfg.n_params} params")
     if cfg.variant == "diag":

@@ -280,11 +280,15 @@ struct FullPlan {
 
 size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
 
-// K splits of an fp32 factor SYRK: at most 16384 rows per split, so that the
-// tallest factors (a stem convolution's 401,408 rows) do not serialise the
-// launch; the partial sums are added by sym_reduce_kernel in split order.
-int syrk_splits(int64_t rows) {
-  return static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (rows + 16383) / 16384)));
+// K splits of an fp32 factor SYRK: blocks of one launch get comparable work,
+// at most 4096 rows per 256 x 256 tile and 8192 rows per 128 x 128 tile
+// (factors below kBigMin use the small tiles), so tall factors (a stem
+// convolution's 401,408 rows, 25,088-row stage-2 layers) do not serialise
+// the launch; the partial sums are added by sym_reduce_kernel in split order.
+int syrk_splits(int d, int64_t rows) {
+  const bool big = d >= kBigMin && (d + 2 * kTile - 1) / (2 * kTile) * 2 * kTile == (d + kTile - 1) / kTile * kTile;
+  const int64_t per = big ? 4096 : 8192;
+  return static_cast<int>(std::min<int64_t>(128, std::max<int64_t>(1, (rows + per - 1) / per)));
 }
 
 bool fp32_factor(const kfac_layer_t& L, int which) {
@@ -304,7 +308,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
     const LayerGeom g = geom_of(layers[li]);
     for (int which = 0; which < 2; ++which) {
       const int d = which == 0 ? g.d_a : g.d_out;
-      const int s = fp32_factor(layers[li], which) ? syrk_splits(g.rows) : 1;
+      const int s = fp32_factor(layers[li], which) ? syrk_splits(d, g.rows) : 1;
       P.nsplit.push_back(s);
       P.part.push_back(s > 1 ? reinterpret_cast<float*>(carve(static_cast<size_t>(s) * d * d * 4)) : nullptr);
     }
@@ -434,11 +438,11 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
   kfac_status_t r;
   for (int kind = 0; kind < 3; ++kind) {
     if (!split[kind].empty()) {
-      r = launch_gemm(split[kind], modes[kind], modes[kind], EPI_STORE, sc, st);
+      r = launch_gemm(split[kind], modes[kind], modes[kind], EPI_STORE, sc, st, TILES_PER_PROBLEM);
       if (r != KFAC_OK) return r;
     }
     if (!direct[kind].empty()) {
-      r = launch_gemm(direct[kind], modes[kind], modes[kind], EPI_SYM_EMA, sc, st);
+      r = launch_gemm(direct[kind], modes[kind], modes[kind], EPI_SYM_EMA, sc, st, TILES_PER_PROBLEM);
       if (r != KFAC_OK) return r;
     }
   }

@@ -76,9 +76,16 @@ int gemm_blocks(const GemmProb& p);
 // Fills tiles_m / tiles_n from M / N.
 void gemm_set_tiles(GemmProb& p);
 
+// Tile-size policy of a launch: AUTO picks 256 x 256 tiles for the whole
+// launch when it has at least two such tiles per CU; PER_PROBLEM gives
+// problems with both sides >= kBigMin the 256 x 256 tiles and the rest
+// 128 x 128 tiles (two launches).
+enum TilePolicy : int { TILES_AUTO = 0, TILES_PER_PROBLEM = 1 };
+constexpr int kBigMin = 384;
+
 // Launches the problems (any count; grouped internally) with operand layouts
 // (amode, bmode) and epilogue `epi` on `stream`.
 kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
-                          hipStream_t stream);
+                          hipStream_t stream, int policy = TILES_AUTO);
 
 }  // namespace kfac

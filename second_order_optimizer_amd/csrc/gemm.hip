@@ -39,7 +39,7 @@ struct Cfg {
 
 // LDS layout of an operand mode: [k][m] rows for i-contiguous (and im2col)
 // operands, [m][k] rows for k-contiguous (and NCHW-gradient) ones.
-__host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K || mode == OP_NCHW; }
+__host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K || mode == OP_NCHW || mode == OP_IM2COL; }
 
 // Per-thread column decomposition of an im2col operand, fixed for the whole K
 // loop: for each of the thread's 4 * kItems columns, the offset of (c, kh, kw)
@@ -49,6 +49,13 @@ struct ColInfo {
   int off[8];
   int kh[8];
   int kw[8];
+};
+
+// Per-thread row decomposition of an im2col operand: for each of the
+// thread's kItems rows n of the current K stage, (b, ho, wo); advanced by
+// kTileK rows per stage without division.
+struct RowState {
+  int b[2], ho[2], wo[2];
 };
 
 struct GemmBatch {
@@ -72,30 +79,60 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
 template <bool BIG, int MODE>
 __device__ inline void col_info(ColInfo<BIG>& ci, const int* geo, int m0, int mlim, int special) {
   using C = Cfg<BIG>;
-  static_assert(C::kItems * 4 <= 8, "column info holds 8 columns");
   if (MODE != OP_IM2COL) return;
   const int k = geo[GEO_K], HW = geo[GEO_H] * geo[GEO_W];
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
-    const int g = threadIdx.x + h * C::kThreads;
-    const int m = m0 + (g % (C::kBT / 4)) * 4;
+    const int mq = m0 + (threadIdx.x + h * C::kThreads) / 4;   // k-major: one column per item
+    const int c = mq / (k * k), r = mq - c * k * k;
+    const int kh = r / k, kw = r - (r / k) * k;
+    const bool real = mq < mlim && mq != special;
+    ci.off[h] = c * HW + kh * geo[GEO_W] + kw;
+    ci.kh[h] = real ? kh : -(1 << 20);   // never inside the image
+    ci.kw[h] = kw;
+  }
+}
+
+// k-major im2col items: item h of this thread covers rows n .. n+3 with
+// n = k0 + 4 (g % 4); the state holds (b, ho, wo) of n.
+template <bool BIG, int MODE>
+__device__ inline void row_init(RowState& rs, const int* geo, int k0) {
+  using C = Cfg<BIG>;
+  static_assert(C::kItems <= 2, "row state holds 2 rows");
+  if (MODE != OP_IM2COL) return;
+  const int HoWo = geo[GEO_HO] * geo[GEO_WO];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int mq = m + q;
-      const int c = mq / (k * k), r = mq - c * k * k;
-      const int kh = r / k, kw = r - (r / k) * k;
-      const bool real = mq < mlim && mq != special;
-      ci.off[4 * h + q] = c * HW + kh * geo[GEO_W] + kw;
-      ci.kh[4 * h + q] = real ? kh : -(1 << 20);   // never inside the image
-      ci.kw[4 * h + q] = kw;
+  for (int h = 0; h < C::kItems; ++h) {
+    const int n = k0 + ((threadIdx.x + h * C::kThreads) % 4) * 4;
+    rs.b[h] = n / HoWo;
+    const int rem = n - rs.b[h] * HoWo;
+    rs.ho[h] = rem / geo[GEO_WO];
+    rs.wo[h] = rem - rs.ho[h] * geo[GEO_WO];
+  }
+}
+
+__device__ inline void step_pos(int& b, int& ho, int& wo, int by, int Ho, int Wo) {
+  wo += by;
+  while (wo >= Wo) {
+    wo -= Wo;
+    if (++ho == Ho) {
+      ho = 0;
+      ++b;
     }
   }
+}
+
+template <bool BIG, int MODE>
+__device__ inline void row_advance(RowState& rs, const int* geo) {
+  if (MODE != OP_IM2COL) return;
+#pragma unroll
+  for (int h = 0; h < Cfg<BIG>::kItems; ++h) step_pos(rs.b[h], rs.ho[h], rs.wo[h], kTileK, geo[GEO_HO], geo[GEO_WO]);
 }
 
 template <bool BIG, int MODE, bool EXTRA>
 __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
                                  int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec,
-                                 const int* geo, const ColInfo<BIG>& ci) {
+                                 const int* geo, const ColInfo<BIG>& ci, const RowState& rs) {
   using C = Cfg<BIG>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
@@ -120,26 +157,27 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
         r[4 * h + q] = v;
       }
     } else if (MODE == OP_IM2COL) {
-      // row n = (b, ho, wo) of the unfolded input; columns from the column info
-      const int n = k0 + g / (C::kBT / 4);
-      const int m = m0 + (g % (C::kBT / 4)) * 4;
-      const int HoWo = geo[GEO_HO] * geo[GEO_WO];
-      const int b = n / HoWo, rem = n - b * HoWo;
-      const int ho = rem / geo[GEO_WO], wo = rem - (rem / geo[GEO_WO]) * geo[GEO_WO];
-      const int hb = ho * geo[GEO_S] - geo[GEO_P], wb = wo * geo[GEO_S] - geo[GEO_P];
+      // column m of the unfolded input (tap (c, kh, kw) from the column
+      // info), rows n .. n+3 = consecutive output positions: for stride 1
+      // consecutive input addresses, so a wavefront's lanes read few lines
+      const int m = m0 + g / 4;
+      const int n = k0 + (g % 4) * 4;
       const int H = geo[GEO_H], W = geo[GEO_W];
-      const int64_t row = static_cast<int64_t>(b) * geo[GEO_C] * H * W + hb * W + wb;   // may be < 0 (padding)
-      const bool kin = n < klim;
+      const int64_t CHW = static_cast<int64_t>(geo[GEO_C]) * H * W;
+      const bool special_col = m == special;
+      int b = rs.b[h], ho = rs.ho[h], wo = rs.wo[h];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int e = 4 * h + q;
-        const int hh = hb + ci.kh[e], ww = wb + ci.kw[e];
+        const unsigned hh = static_cast<unsigned>(ho * geo[GEO_S] - geo[GEO_P] + ci.kh[h]);
+        const unsigned ww = static_cast<unsigned>(wo * geo[GEO_S] - geo[GEO_P] + ci.kw[h]);
         float v = 0.f;
-        if (kin) {
-          if (m + q == special) v = 1.0f;
-          else if (hh >= 0 && hh < H && ww >= 0 && ww < W) v = base[row + ci.off[e]];
+        if (n + q < klim) {
+          if (special_col) v = 1.0f;
+          else if (hh < static_cast<unsigned>(H) && ww < static_cast<unsigned>(W))
+            v = base[b * CHW + ci.off[h] + (static_cast<int>(hh) - ci.kh[h]) * W + (static_cast<int>(ww) - ci.kw[h])];
         }
-        r[e] = v;
+        r[4 * h + q] = v;
+        if (q < 3) step_pos(b, ho, wo, 1, geo[GEO_HO], geo[GEO_WO]);
       }
     } else if (MODE == OP_NCHW) {
       // element (m = channel, n = b * P + p) at base[(b * channels + m) * P + p]
@@ -260,10 +298,14 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   ColInfo<BIG> cia, cib;
   col_info<BIG, AMODE>(cia, P.geo, i0, P.M, P.a_special);
   col_info<BIG, BMODE>(cib, P.geo, j0, P.N, P.b_special);
+  // both operands of an im2col SYRK walk the same rows
+  RowState rs;
+  row_init<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo, kb);
   int buf = 0;
   if (kb < ke) {
-    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec, P.geo, cia);
-    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec, P.geo, cib);
+    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec, P.geo, cia, rs);
+    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec, P.geo, cib, rs);
+    row_advance<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo);
     store_slab<BIG, AMODE>(sA[0], ra);
     store_slab<BIG, BMODE>(sB[0], rb);
   }
@@ -272,8 +314,10 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     const bool more = k0 + kTileK < ke;
     if (more) {
       load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec, P.geo,
-                                  cia);
-      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec, P.geo, cib);
+                                  cia, rs);
+      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec, P.geo, cib,
+                                   rs);
+      row_advance<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo);
     }
     const float* a = sA[buf];
     const float* b = sB[buf];
@@ -403,12 +447,10 @@ void gemm_set_tiles(GemmProb& p) {
 
 int gemm_blocks(const GemmProb& p) { return tiles_for(p, kTile); }
 
-kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
-                          hipStream_t stream) {
-  // 256 x 256 tiles when the launch still has at least two tiles per CU
-  int big_tiles = 0;
-  for (const GemmProb& p : probs) big_tiles += tiles_for(p, 2 * kTile);
-  const bool big = big_tiles >= 512;
+namespace {
+
+kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
+                          hipStream_t stream, bool big) {
   const int bt = big ? 2 * kTile : kTile;
   size_t i = 0;
   while (i < probs.size()) {
@@ -436,6 +478,29 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
     if (st != KFAC_OK) return st;
   }
   return KFAC_OK;
+}
+
+}  // namespace
+
+kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
+                          hipStream_t stream, int policy) {
+  if (policy == TILES_PER_PROBLEM) {
+    std::vector<GemmProb> big, small;
+    // 256 x 256 tiles only where they add no padding over 128 x 128 tiles
+    auto pad = [](int x, int t) { return (x + t - 1) / t * t; };
+    for (const GemmProb& p : probs) {
+      const bool b = p.M >= kBigMin && p.N >= kBigMin && pad(p.M, 2 * kTile) == pad(p.M, kTile) &&
+                     pad(p.N, 2 * kTile) == pad(p.N, kTile);
+      (b ? big : small).push_back(p);
+    }
+    kfac_status_t st = big.empty() ? KFAC_OK : launch_with(big, amode, bmode, epi, sc, stream, true);
+    if (st != KFAC_OK) return st;
+    return small.empty() ? KFAC_OK : launch_with(small, amode, bmode, epi, sc, stream, false);
+  }
+  // 256 x 256 tiles when the launch still has at least two tiles per CU
+  int big_tiles = 0;
+  for (const GemmProb& p : probs) big_tiles += tiles_for(p, 2 * kTile);
+  return launch_with(probs, amode, bmode, epi, sc, stream, big_tiles >= 512);
 }
 
 }  // namespace kfac
