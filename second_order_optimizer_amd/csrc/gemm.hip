@@ -23,6 +23,10 @@ constexpr int kLdsPad = 4;
 
 // Two shapes: SMALL = 128 x 128 tile, 4 wavefronts (2 x 2) of 64 x 64;
 // BIG = 256 x 256 tile, 8 wavefronts (2 x 4) of 128 x 64.
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 template <bool BIG>
 struct Cfg {
   static constexpr int kThreads = BIG ? 512 : 256;
@@ -321,25 +325,35 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     }
     const float* a = sA[buf];
     const float* b = sB[buf];
-#pragma unroll
-    for (int kk = 0; kk < kTileK; kk += 2) {
+    // fragments of k-substep kk + 2 are read while the MFMAs of kk run
+    float af[2][C::kBI], bf[2][C::kBJ];
+    auto frag = [&](int kk, float (&fa)[C::kBI], float (&fb)[C::kBJ]) {
       const int kl = kk + (lane >> 5);
-      float af[C::kBI], bf[C::kBJ];
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i) {
         const int m = wm + 32 * i + (lane & 31);
-        af[i] = !k_major(AMODE) ? a[kl * C::kRow + m] : a[m * C::kKRow + kl];
+        fa[i] = !k_major(AMODE) ? a[kl * C::kRow + m] : a[m * C::kKRow + kl];
       }
 #pragma unroll
       for (int j = 0; j < C::kBJ; ++j) {
         const int n = wn + 32 * j + (lane & 31);
-        bf[j] = !k_major(BMODE) ? b[kl * C::kRow + n] : b[n * C::kKRow + kl];
+        fb[j] = !k_major(BMODE) ? b[kl * C::kRow + n] : b[n * C::kKRow + kl];
       }
+    };
+    frag(0, af[0], bf[0]);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kBI + C::kBJ, 0);
+#pragma unroll
+    for (int kk = 0; kk < kTileK; kk += 2) {
+      const int cur = (kk >> 1) & 1;
+      if (kk + 2 < kTileK) frag(kk + 2, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i)
 #pragma unroll
         for (int j = 0; j < C::kBJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+      // the scheduler would otherwise sink the reads next to their MFMAs
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kBI + C::kBJ, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kBI * C::kBJ, 0);
     }
     if (more) {
       store_slab<BIG, AMODE>(sA[buf ^ 1], ra);

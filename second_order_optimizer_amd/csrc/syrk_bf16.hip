@@ -27,6 +27,9 @@ constexpr int kBT = 256;        // block tile
 constexpr int kBK = 64;         // rows of X per stage
 constexpr int kLR = kBK + 8;    // LDS column length in bf16 (144 bytes)
 constexpr int kMaxProbs = 56;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 struct Prob {
   const uint16_t* X;
@@ -136,21 +139,31 @@ syrk_bf16_kernel(Batch batch) {
     const unsigned short* sa = sX[buf][0];
     const unsigned short* sb = diag ? sa : sX[buf][1];
     if (work) {
-#pragma unroll
-      for (int ks = 0; ks < kBK; ks += 16) {
+      // fragments of k-step ks + 16 are read while the MFMAs of ks run
+      bf16x8 fa[2][4], fb[2][2];
+      auto frag = [&](int ks, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
         const int ko = ks + 8 * (lane >> 5);
-        bf16x8 a[4], b[2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm + 32 * i + (lane & 31)) * kLR + ko);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn + 32 * j + (lane & 31)) * kLR + ko);
+      };
+      frag(0, fa[0], fb[0]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+      for (int ks = 0; ks < kBK; ks += 16) {
+        const int cur = (ks >> 4) & 1;
+        if (ks + 16 < kBK) frag(ks + 16, fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        // keep the next reads ahead of this k-step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
       }
     } else if (colsum) {
 #pragma unroll
