@@ -280,15 +280,15 @@ struct FullPlan {
 
 size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
 
-// K splits of an fp32 factor SYRK: blocks of one launch get comparable work,
-// at most 4096 rows per 256 x 256 tile and 8192 rows per 128 x 128 tile
-// (factors below kBigMin use the small tiles), so tall factors (a stem
-// convolution's 401,408 rows, 25,088-row stage-2 layers) do not serialise
-// the launch; the partial sums are added by sym_reduce_kernel in split order.
-int syrk_splits(int d, int64_t rows) {
-  const bool big = d >= kBigMin && (d + 2 * kTile - 1) / (2 * kTile) * 2 * kTile == (d + kTile - 1) / kTile * kTile;
-  const int64_t per = big ? 4096 : 8192;
-  return static_cast<int>(std::min<int64_t>(128, std::max<int64_t>(1, (rows + per - 1) / per)));
+// Row splits of an fp32 factor SYRK (128 x 128 tiles): one workgroup
+// contracts about kSplitRows rows, so a launch holds many workgroups of
+// similar length and tall factors (a stem convolution's 401,408 rows) do not
+// serialise it; sym_reduce_kernel adds the partial products in split order.
+constexpr int64_t kSplitRows = 2048;
+
+int syrk_splits(int, int64_t rows) {
+  if (rows < 2 * kSplitRows) return 1;
+  return static_cast<int>(std::min<int64_t>(128, (rows + kSplitRows - 1) / kSplitRows));
 }
 
 bool fp32_factor(const kfac_layer_t& L, int which) {
@@ -362,7 +362,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
                             hipStream_t st) {
   const float eps = hp.ema_decay;
   enum { K_MN = 0, K_IM2COL = 1, K_NCHW = 2 };
-  std::vector<GemmProb> direct[3], split[3];
+  std::vector<GemmProb> probs[3];
   std::vector<SymRedItem> reds;
   std::vector<SyrkBf16Prob> bf16;
   for (int li = 0; li < n; ++li) {
@@ -408,20 +408,18 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         p.geo[1] = g.d_out;
       }
       const int s = P.nsplit[2 * li + which];
+      p.ldc = d;
+      p.nsplit = s;
       if (s == 1) {
         p.C = F;
-        p.ldc = d;
-        p.nsplit = 1;
         p.alpha = alpha;
         p.beta = eps;
-        direct[kind].push_back(p);
+        probs[kind].push_back(p);
       } else {
         p.C = P.part[2 * li + which];
-        p.ldc = d;
-        p.nsplit = s;
         p.split_stride = static_cast<int64_t>(d) * d;
         p.alpha = 1.0f;
-        split[kind].push_back(p);
+        probs[kind].push_back(p);
         SymRedItem r{};
         r.part = p.C;
         r.F = F;
@@ -437,14 +435,9 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
   const int modes[3] = {OP_MN, OP_IM2COL, OP_NCHW};
   kfac_status_t r;
   for (int kind = 0; kind < 3; ++kind) {
-    if (!split[kind].empty()) {
-      r = launch_gemm(split[kind], modes[kind], modes[kind], EPI_STORE, sc, st, TILES_PER_PROBLEM);
-      if (r != KFAC_OK) return r;
-    }
-    if (!direct[kind].empty()) {
-      r = launch_gemm(direct[kind], modes[kind], modes[kind], EPI_SYM_EMA, sc, st, TILES_PER_PROBLEM);
-      if (r != KFAC_OK) return r;
-    }
+    if (probs[kind].empty()) continue;
+    r = launch_gemm(probs[kind], modes[kind], modes[kind], EPI_SYRK, sc, st, TILES_SMALL);
+    if (r != KFAC_OK) return r;
   }
   if (!bf16.empty()) {
     r = launch_syrk_bf16(bf16, st);

@@ -33,6 +33,7 @@ enum GemmEpi : int {
   EPI_SYM_EMA = 2,    // upper tiles; C = beta * C + alpha * acc, mirrored to the lower triangle
   EPI_UPDATE = 3,     // P = acc; D = P + wd W; V = mu V + D; W -= lr V  (columns >= d_in go to b / mom_b)
   EPI_SYM_IFOK = 4,   // upper tiles; C = acc mirrored, skipped when *fail != 0
+  EPI_SYRK = 5,       // upper tiles; nsplit == 1: as EPI_SYM_EMA, else C + split * split_stride = alpha * acc
 };
 
 // Tile grids.
@@ -79,12 +80,14 @@ void gemm_set_tiles(GemmProb& p);
 // Tile-size policy of a launch: AUTO picks 256 x 256 tiles for the whole
 // launch when it has at least two such tiles per CU; PER_PROBLEM gives
 // problems with both sides >= kBigMin the 256 x 256 tiles and the rest
-// 128 x 128 tiles (two launches).
-enum TilePolicy : int { TILES_AUTO = 0, TILES_PER_PROBLEM = 1 };
+// 128 x 128 tiles (two launches); SMALL uses 128 x 128 tiles throughout.
+enum TilePolicy : int { TILES_AUTO = 0, TILES_PER_PROBLEM = 1, TILES_SMALL = 2 };
 constexpr int kBigMin = 384;
 
 // Launches the problems (any count; grouped internally) with operand layouts
-// (amode, bmode) and epilogue `epi` on `stream`.
+// (amode, bmode) and epilogue `epi` on `stream`.  Problems must be
+// independent: within a launch they are ordered by the contraction length of
+// one workgroup, longest first, and spread over launches of similar work.
 kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
                           hipStream_t stream, int policy = TILES_AUTO);
 

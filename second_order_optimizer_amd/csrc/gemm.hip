@@ -14,6 +14,7 @@
 #include "gemm.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace kfac {
 
@@ -290,6 +291,11 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   const int wid = threadIdx.x >> 6;
   const int wm = (wid / C::kWavesN) * C::kWM, wn = (wid % C::kWavesN) * C::kWN;
 
+  // A wavefront whose part of the tile lies outside C, or strictly below the
+  // diagonal of a diagonal tile of an upper-triangle grid, has no output to
+  // produce and skips its MFMAs (it still stages its share of the slabs).
+  const bool live = i0 + wm < P.M && j0 + wn < P.N && !(P.tri == TRI_UPPER && ti == tj && wm >= wn + C::kWN);
+
   f32x16 acc[C::kBI][C::kBJ];
 #pragma unroll
   for (int a = 0; a < C::kBI; ++a)
@@ -314,6 +320,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     store_slab<BIG, BMODE>(sB[0], rb);
   }
   __syncthreads();
+  // The main loop is instantiated twice: wavefronts without output run it
+  // without MFMAs (a branch inside one loop costs the others registers).
+  auto main_loop = [&](auto compute) {
   for (int k0 = kb; k0 < ke; k0 += kTileK) {
     const bool more = k0 + kTileK < ke;
     if (more) {
@@ -323,6 +332,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
                                    rs);
       row_advance<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo);
     }
+    if constexpr (decltype(compute)::value) {
     const float* a = sA[buf];
     const float* b = sB[buf];
     // fragments of k-substep kk + 2 are read while the MFMAs of kk run
@@ -355,6 +365,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kBI + C::kBJ, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kBI * C::kBJ, 0);
     }
+    }
     if (more) {
       store_slab<BIG, AMODE>(sA[buf ^ 1], ra);
       store_slab<BIG, BMODE>(sB[buf ^ 1], rb);
@@ -362,6 +373,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     __syncthreads();
     buf ^= 1;
   }
+  };
+  if (live) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
   // epilogue: accumulator r of block (si, sj) is C[row][col] with
   // row = i0 + wm + 32 si + 8 (r / 4) + 4 (lane / 32) + r % 4, col = j0 + wn + 32 sj + lane % 32
@@ -383,7 +397,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SUB) {
           Cp[idx] -= v;
-        } else if (EPI == EPI_SYM_EMA) {
+        } else if (EPI == EPI_SYRK && P.nsplit > 1) {
+          Cp[idx] = P.alpha * v;
+        } else if (EPI == EPI_SYM_EMA || EPI == EPI_SYRK) {
           if (row <= col) {
             const float o = P.beta * Cp[idx] + P.alpha * v;
             Cp[idx] = o;
@@ -430,18 +446,15 @@ kfac_status_t launch_group(const GemmBatch& b, int blocks, bool big, hipStream_t
 kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm, int epi, hipStream_t s) {
 #define KFAC_GEMM_CASE(A_, B_, E_) \
   if (am == A_ && bm == B_ && epi == E_) return launch_group<A_, B_, E_>(b, blocks, big, s);
-  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYM_EMA)
-  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_UPDATE)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYM_IFOK)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_SUB)
-  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_SYM_EMA)
-  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_STORE)
-  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_SYM_EMA)
-  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_STORE)
+  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYRK)
+  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_SYRK)
+  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_SYRK)
 #undef KFAC_GEMM_CASE
   return KFAC_ERR_UNSUPPORTED;
 }
@@ -463,32 +476,48 @@ int gemm_blocks(const GemmProb& p) { return tiles_for(p, kTile); }
 
 namespace {
 
+// contraction length of one workgroup of `p`
+int64_t block_k(const GemmProb& p) {
+  const int64_t k = std::max(0, p.ke - p.kb);
+  return (k + std::max(1, p.nsplit) - 1) / std::max(1, p.nsplit);
+}
+
 kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
                           hipStream_t stream, bool big) {
   const int bt = big ? 2 * kTile : kTile;
-  size_t i = 0;
-  while (i < probs.size()) {
-    GemmBatch b{};
-    b.sc = sc;
-    int blocks = 0;
-    int n = 0;
-    for (; i < probs.size() && n < kMaxGemmProbs; ++i) {
-      GemmProb p = probs[i];
-      if (p.nsplit < 1) p.nsplit = 1;
-      p.tiles_m = (p.M + bt - 1) / bt;
-      p.tiles_n = (p.N + bt - 1) / bt;
-      p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
-      p.b_vec = (p.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0 && (p.kb % 4) == 0;
-      if (amode == OP_NCHW) p.a_vec = p.b_vec = (p.geo[0] % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0;
-      const int nb = tiles_for(p, bt);
-      if (nb == 0) continue;
-      p.blk_begin = blocks;
-      blocks += nb;
-      b.p[n++] = p;
-    }
-    if (n == 0) continue;
-    b.n = n;
-    kfac_status_t st = dispatch(b, blocks, big, amode, bmode, epi, stream);
+  std::vector<GemmProb> ps;
+  for (GemmProb p : probs) {
+    if (p.nsplit < 1) p.nsplit = 1;
+    p.tiles_m = (p.M + bt - 1) / bt;
+    p.tiles_n = (p.N + bt - 1) / bt;
+    p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
+    p.b_vec = (p.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0 && (p.kb % 4) == 0;
+    if (amode == OP_NCHW) p.a_vec = p.b_vec = (p.geo[0] % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0;
+    if (tiles_for(p, bt) > 0) ps.push_back(p);
+  }
+  // longest workgroups first, so a launch ends on short ones
+  std::stable_sort(ps.begin(), ps.end(),
+                   [](const GemmProb& a, const GemmProb& b) { return block_k(a) > block_k(b); });
+  // greedy balance of the work over the fewest launches the table size allows
+  const size_t nl = (ps.size() + kMaxGemmProbs - 1) / kMaxGemmProbs;
+  std::vector<GemmBatch> batches(nl);
+  std::vector<double> work(nl, 0.0);
+  std::vector<int> blocks(nl, 0);
+  for (const GemmProb& p : ps) {
+    size_t best = nl;
+    for (size_t l = 0; l < nl; ++l)
+      if (batches[l].n < kMaxGemmProbs && (best == nl || work[l] < work[best])) best = l;
+    GemmBatch& b = batches[best];
+    GemmProb q = p;
+    const int nb = tiles_for(q, bt);
+    q.blk_begin = blocks[best];
+    blocks[best] += nb;
+    work[best] += static_cast<double>(nb) * static_cast<double>(block_k(q));
+    b.p[b.n++] = q;
+  }
+  for (size_t l = 0; l < nl; ++l) {
+    batches[l].sc = sc;
+    kfac_status_t st = dispatch(batches[l], blocks[l], big, amode, bmode, epi, stream);
     if (st != KFAC_OK) return st;
   }
   return KFAC_OK;
@@ -498,6 +527,7 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
 
 kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
                           hipStream_t stream, int policy) {
+  if (policy == TILES_SMALL) return launch_with(probs, amode, bmode, epi, sc, stream, false);
   if (policy == TILES_PER_PROBLEM) {
     std::vector<GemmProb> big, small;
     // 256 x 256 tiles only where they add no padding over 128 x 128 tiles
