@@ -149,121 +149,196 @@ __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
   }
 }
 
-// Block k of every matrix with more than k blocks: Cholesky of the diagonal
-// block fused with the forward substitution that inverts it (right-looking,
-// column by column).  Thread (tr, tc) of a 16 x 16 grid keeps the 8 x 8
-// sub-block (rows 8 tr.., columns 8 tc..) of both the factor and the inverse
-// in registers; per column only the pivot, the scaled column of L and the
-// finished row of the inverse go through LDS (double-buffered, two barriers
-// per column).  Writes L_kk (zero above the diagonal) into L, its inverse
-// into Dinv[k] and into Z's diagonal block.  A pivot that is not positive (or
-// not finite) marks the matrix failed, raises KFAC_FLAG_NOT_PD and is
-// replaced by 1 so the remaining steps stay finite; a failed matrix's
-// inverse is not written.
+// Block k of every matrix with more than k blocks: Cholesky factor of the
+// diagonal block and its inverse, one workgroup (4 wavefronts) per block,
+// blocked by 32 columns with the whole block in LDS.  Per 32-column panel:
+//  - wavefront 0 factors the 32 x 32 diagonal sub-block in registers: lane c
+//    holds column c of the sub-block, lane 32 + c column c of an identity;
+//    elimination is sqrt-free (row r -= (B_rj / B_jj) row j, column j
+//    broadcast from lane j by v_readlane), which yields D^-1/2-scaled forms
+//    of both L (columns) and L^-1 (rows);
+//  - the sub-diagonal panel L_qp = M_qp Z_pp^T and the trailing update
+//    M_ij -= L_ip L_jp^T run on MFMA, one 32 x 32 tile per wavefront.
+// The off-diagonal blocks of the inverse follow by rows,
+// Z_ij = -Z_ii sum_{j<=m<i} L_im Z_mj, also on MFMA.  The inverse goes to
+// Dinv[k] and to Z's diagonal block; L_kk itself is not written back (later
+// steps use only its inverse).  A pivot that is not positive (or not finite)
+// marks the matrix failed, raises KFAC_FLAG_NOT_PD and is replaced by 1 so the
+// remaining steps stay finite; a failed matrix's inverse is not written.
+// Rows and columns beyond a partial last block are an identity.
+constexpr int kLd = kNb + 1;   // LDS pitch: row and column walks hit distinct banks
+constexpr int kSd = 33;        // pitch of a wavefront's 32 x 32 staging tile
+
+__device__ inline f32x16 mfma32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// acc += sign * A B^T with A = X[ar.., ac..], B = Y[br.., bc..] (32 x 32 each, pitch kLd)
+__device__ inline void mma_nt(f32x16& acc, const float* X, int ar, int ac, const float* Y, int br, int bc, float sign,
+                              int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 32; kk += 2) {
+    const int k = kk + (lane >> 5);
+    acc = mfma32(sign * X[(ar + (lane & 31)) * kLd + ac + k], Y[(br + (lane & 31)) * kLd + bc + k], acc);
+  }
+}
+
+// acc += A B with A = X[ar.., ac..] (pitch kLd), B = Y[br.., bc..] (pitch ldy)
+__device__ inline void mma_nn(f32x16& acc, const float* X, int ar, int ac, const float* Y, int ldy, int br, int bc,
+                              int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 32; kk += 2) {
+    const int k = kk + (lane >> 5);
+    acc = mfma32(X[(ar + (lane & 31)) * kLd + ac + k], Y[(br + k) * ldy + bc + (lane & 31)], acc);
+  }
+}
+
+// accumulator r of lane l is element (8 (r/4) + 4 (l/32) + r%4, l%32) of the tile
+__device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+__device__ inline void tile_load(f32x16& acc, const float* S, int ld, int r0, int c0, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = S[(r0 + acc_row(r, lane)) * ld + c0 + (lane & 31)];
+}
+
+__device__ inline void tile_store(float* S, int ld, int r0, int c0, const f32x16& acc, float sign, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[(r0 + acc_row(r, lane)) * ld + c0 + (lane & 31)] = sign * acc[r];
+}
+
+// Wavefront-level factorization of the 32 x 32 diagonal sub-block at (c0, c0)
+// of Ms; writes the factor into Ms and its inverse into Zs at the same place.
+__device__ inline void factor_diag32(float* Ms, float* Zs, int c0, const DMat& M, uint32_t* flags, int lane) {
+  const int c = lane & 31;
+  const bool xl = lane >= 32;
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = xl ? (r == c ? 1.f : 0.f) : Ms[(c0 + r) * kLd + c0 + c];
+  float pv[32];
+  float dmine = 1.f;
+  bool bad = false;
+  // no branch inside the loop: the scheduler may start step j + 1 while
+  // step j's remaining updates issue
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), j));
+    const bool ok = piv > 0.f && isfinite(piv);
+    bad = bad || !ok;
+    piv = ok ? piv : 1.f;
+    pv[j] = piv;
+    if (c == j) dmine = piv;
+    const float inv = __builtin_amdgcn_rcpf(piv);
+    // A lanes: columns c > j take the rank-1 update (row j of column c is
+    // B_jc = B_cj); finished columns keep their multipliers.  X lanes: row
+    // operation on the whole row.
+    const float t = (xl || c > j) ? v[j] * inv : 0.f;
+#pragma unroll
+    for (int r = j + 1; r < 32; ++r) {
+      const float col = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), j));
+      v[r] = fmaf(-col, t, v[r]);
+    }
+  }
+  if (bad && lane == 0 && *M.fail == 0) {
+    *M.fail = 1;
+    raise_flag(flags, KFAC_FLAG_NOT_PD);
+  }
+  if (!xl) {
+    // L_rc = B_rc / sqrt(d_c) below the diagonal, sqrt(d_c) on it
+    const float s = sqrtf(dmine), is = 1.0f / s;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) Ms[(c0 + r) * kLd + c0 + c] = r > c ? v[r] * is : (r == c ? s : 0.f);
+  } else {
+    // (L^-1)_rc = X_rc / sqrt(d_r)
+#pragma unroll
+    for (int r = 0; r < 32; ++r) Zs[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * (1.0f / sqrtf(pv[r])) : 0.f;
+  }
+}
+
 __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
-  __shared__ __attribute__((aligned(16))) float colj[2][kNb];
-  __shared__ __attribute__((aligned(16))) float rowj[2][kNb];
-  __shared__ float pivs[2];
+  __shared__ __attribute__((aligned(16))) float Ms[kNb * kLd];
+  __shared__ __attribute__((aligned(16))) float Zs[kNb * kLd];
+  __shared__ __attribute__((aligned(16))) float Ss[4][32 * kSd];
   const DMat& M = T.m[blockIdx.x];
   const int d = M.d, k = T.k;
   const int nblk = (d + kNb - 1) / kNb;
   if (k >= nblk) return;
   const int r0 = k * kNb;
   const int bk = min(kNb, d - r0);
-  const int tid = threadIdx.x;
-  const int tr = tid >> 4, tc = tid & 15;
-  const int R0 = tr * 8, C0 = tc * 8;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   float* Lg = M.L + static_cast<int64_t>(r0) * d + r0;
-  float a[8][8], x[8][8];
+
+  // symmetric working block from the lower triangle; identity beyond bk.
+  // Thread t reads column t % 128 of rows t / 128 + 2 i, 32 loads in flight.
+  const int lc = tid & (kNb - 1), lr = tid >> 7;
+  for (int i0 = 0; i0 < kNb / 2; i0 += 32) {
+    float vals[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int u = 0; u < 32; ++u) {
+      const int r = lr + 2 * (i0 + u);
+      vals[u] = (r < bk && lc <= r) ? Lg[static_cast<int64_t>(r) * d + lc] : 0.f;
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = R0 + i, c = C0 + j;
-      a[i][j] = (r < bk && c <= r) ? Lg[static_cast<int64_t>(r) * d + c] : 0.f;
-      x[i][j] = (r < bk && r == c) ? 1.f : 0.f;
+    for (int u = 0; u < 32; ++u) {
+      const int r = lr + 2 * (i0 + u);
+      if (lc > r) continue;
+      const float v = r < bk ? vals[u] : (r == lc ? 1.f : 0.f);
+      Ms[r * kLd + lc] = v;
+      Ms[lc * kLd + r] = v;
     }
   }
-  const int nbk = (bk + 7) / 8;
-  for (int jb = 0; jb < nbk; ++jb) {
-#pragma unroll
-    for (int jl = 0; jl < 8; ++jl) {
-      const int j = jb * 8 + jl;
-      if (j >= bk) break;
-      const int p = j & 1;
-      if (tr == jb && tc == jb) {
-        float v = a[jl][jl];
-        if (!(v > 0.f) || !isfinite(v)) {
-          if (*M.fail == 0) {
-            *M.fail = 1;
-            raise_flag(T.flags, KFAC_FLAG_NOT_PD);
-          }
-          v = 1.f;
-        }
-        pivs[p] = sqrtf(v);
-      }
-      __syncthreads();
-      const float s = pivs[p];
-      const float inv = 1.0f / s;
-      if (tc == jb) {                      // column j of L: scale below the pivot, publish all 128 rows
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = R0 + i;
-          const float v = a[i][jl] * inv;
-          a[i][jl] = r > j ? v : (r == j ? s : a[i][jl]);
-          colj[p][r] = r > j ? v : 0.f;
-        }
-      }
-      if (tr == jb) {                      // row j of the inverse is final once scaled
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          x[jl][c] *= inv;
-          rowj[p][C0 + c] = x[jl][c];
-        }
-      }
-      __syncthreads();
-      // Rank-1 updates, branch-free: colj is zero at rows <= j, so columns <= j
-      // of L and rows <= j of the inverse are left as they are; entries above
-      // the diagonal of L are never read and are zeroed at write-back; row j
-      // of the inverse is zero beyond column j.
-      if (tr >= tc) {
-        f32x4 cr0 = *reinterpret_cast<const f32x4*>(&colj[p][R0]);
-        f32x4 cr1 = *reinterpret_cast<const f32x4*>(&colj[p][R0 + 4]);
-        f32x4 cc0 = *reinterpret_cast<const f32x4*>(&colj[p][C0]);
-        f32x4 cc1 = *reinterpret_cast<const f32x4*>(&colj[p][C0 + 4]);
-        f32x4 rj0 = *reinterpret_cast<const f32x4*>(&rowj[p][C0]);
-        f32x4 rj1 = *reinterpret_cast<const f32x4*>(&rowj[p][C0 + 4]);
-        const float cr[8] = {cr0[0], cr0[1], cr0[2], cr0[3], cr1[0], cr1[1], cr1[2], cr1[3]};
-        const float cc[8] = {cc0[0], cc0[1], cc0[2], cc0[3], cc1[0], cc1[1], cc1[2], cc1[3]};
-        const float rj[8] = {rj0[0], rj0[1], rj0[2], rj0[3], rj1[0], rj1[1], rj1[2], rj1[3]};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            a[i][c] = fmaf(-cr[i], cc[c], a[i][c]);
-            x[i][c] = fmaf(-cr[i], rj[c], x[i][c]);
-          }
-        }
-      }
+  __syncthreads();
+
+  for (int p = 0; p < kNb / 32; ++p) {
+    const int c0 = 32 * p;
+    if (wid == 0) factor_diag32(Ms, Zs, c0, M, T.flags, lane);
+    __syncthreads();
+    // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
+    if (wid < kNb / 32 - 1 - p) {
+      const int q = p + 1 + wid;
+      f32x16 acc = {};
+      mma_nt(acc, Ms, 32 * q, c0, Zs, c0, c0, 1.f, lane);
+      tile_store(Ms, kLd, 32 * q, c0, acc, 1.f, lane);
     }
+    __syncthreads();
+    // trailing lower tiles (ib, jb), p < jb <= ib: M_ij -= L_ip L_jp^T
+    const int nr = kNb / 32 - 1 - p;
+    for (int t = wid; t < nr * (nr + 1) / 2; t += 4) {
+      int ib = 0, u = t;
+      while (u > ib) { u -= ib + 1; ++ib; }
+      const int I = 32 * (p + 1 + ib), J = 32 * (p + 1 + u);
+      f32x16 acc;
+      tile_load(acc, Ms, kLd, I, J, lane);
+      mma_nt(acc, Ms, I, c0, Ms, J, c0, -1.f, lane);
+      tile_store(Ms, kLd, I, J, acc, 1.f, lane);
+    }
+    __syncthreads();
   }
-  // write back: L_kk (lower, zero above), Dinv[k] and Z_kk
+
+  // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj
+  for (int i = 1; i < kNb / 32; ++i) {
+    if (wid < i) {
+      const int j = wid;
+      f32x16 acc = {};
+      for (int m = j; m < i; ++m) mma_nn(acc, Ms, 32 * i, 32 * m, Zs, kLd, 32 * m, 32 * j, lane);
+      tile_store(Ss[wid], kSd, 0, 0, acc, 1.f, lane);
+      f32x16 z = {};
+      mma_nn(z, Zs, 32 * i, 32 * i, Ss[wid], kSd, 0, 0, lane);
+      tile_store(Zs, kLd, 32 * i, 32 * j, z, -1.f, lane);
+    }
+    __syncthreads();
+  }
+
+  // write back Dinv[k] and Z_kk (L_kk itself is not read again: the panel
+  // below it is formed with Dinv[k])
   float* D = M.Dinv + static_cast<int64_t>(k) * kNb * kNb;
   float* Zg = M.Z + static_cast<int64_t>(r0) * d + r0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = R0 + i, c = C0 + j;
-      const bool in = r < bk && c < bk;
-      const float l = c <= r ? a[i][j] : 0.f;
-      const float xv = c <= r ? x[i][j] : 0.f;
-      D[r * kNb + c] = in ? xv : 0.f;
-      if (in) {
-        Lg[static_cast<int64_t>(r) * d + c] = l;
-        Zg[static_cast<int64_t>(r) * d + c] = xv;
-      }
-    }
+#pragma unroll 8
+  for (int e = tid; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e - (e / kNb) * kNb;
+    const bool in = r < bk && c < bk;
+    const float z = c <= r ? Zs[r * kLd + c] : 0.f;
+    D[e] = in ? z : 0.f;
+    if (in) Zg[static_cast<int64_t>(r) * d + c] = z;
   }
 }
 

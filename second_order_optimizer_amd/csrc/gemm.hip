@@ -24,6 +24,15 @@ constexpr int kLdsPad = 4;
 
 // Two shapes: SMALL = 128 x 128 tile, 4 wavefronts (2 x 2) of 64 x 64;
 // BIG = 256 x 256 tile, 8 wavefronts (2 x 4) of 128 x 64.
+// f(std::integral_constant<int, i>) for i = B .. E - 1
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -378,12 +387,39 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   else main_loop(std::false_type{});
 
   // epilogue: accumulator r of block (si, sj) is C[row][col] with
-  // row = i0 + wm + 32 si + 8 (r / 4) + 4 (lane / 32) + r % 4, col = j0 + wn + 32 sj + lane % 32
+  // row = i0 + wm + 32 si + 8 (r / 4) + 4 (lane / 32) + r % 4, col = j0 + wn + 32 sj + lane % 32.
+  // Read-modify-write epilogues first issue every read of a block row (from a
+  // clamped, always valid address), then compute and store: one memory round
+  // trip per block row instead of one per element.
+  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_SYM_EMA || EPI == EPI_SYRK || EPI == EPI_UPDATE;
+  const bool ema = (EPI == EPI_SYM_EMA) || (EPI == EPI_SYRK && P.nsplit == 1);
   bool bad = false;
   bool skip = false;
   if (EPI == EPI_SYM_IFOK) skip = *P.fail != 0;
+  // block rows by a compile-time index: a runtime one would place acc in scratch
+  static_for<0, C::kBI>([&](auto si_c) {
+    constexpr int si = decltype(si_c)::value;
+    float c0v[C::kBJ][16], c1v[C::kBJ][16];
+    if (kReads) {
 #pragma unroll
-  for (int si = 0; si < C::kBI; ++si) {
+      for (int sj = 0; sj < C::kBJ; ++sj) {
+        const int col = j0 + wn + 32 * sj + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const bool in = row < P.M && col < P.N;
+          const int64_t idx = in ? static_cast<int64_t>(row) * P.ldc + col : 0;
+          if (EPI == EPI_UPDATE) {
+            const bool wcol = !in || col < P.d_in;
+            const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
+            c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
+            c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
+          } else if (EPI == EPI_SUB || ema) {
+            c0v[sj][r] = Cp[idx];
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int sj = 0; sj < C::kBJ; ++sj) {
       const int col = j0 + wn + 32 * sj + (lane & 31);
@@ -396,12 +432,12 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
         if (EPI == EPI_STORE) {
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SUB) {
-          Cp[idx] -= v;
-        } else if (EPI == EPI_SYRK && P.nsplit > 1) {
+          Cp[idx] = c0v[sj][r] - v;
+        } else if (EPI == EPI_SYRK && !ema) {
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SYM_EMA || EPI == EPI_SYRK) {
           if (row <= col) {
-            const float o = P.beta * Cp[idx] + P.alpha * v;
+            const float o = P.beta * c0v[sj][r] + P.alpha * v;
             Cp[idx] = o;
             if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
@@ -411,18 +447,12 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
             if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = v;
           }
         } else if (EPI == EPI_UPDATE) {
-          float* wp;
-          float* vp;
-          if (col < P.d_in) {
-            wp = P.W + static_cast<int64_t>(row) * P.d_in + col;
-            vp = P.V + static_cast<int64_t>(row) * P.d_in + col;
-          } else {
-            wp = P.Wb + row;
-            vp = P.Vb + row;
-          }
-          const float w = *wp;
+          const bool wcol = col < P.d_in;
+          float* wp = wcol ? P.W + static_cast<int64_t>(row) * P.d_in + col : P.Wb + row;
+          float* vp = wcol ? P.V + static_cast<int64_t>(row) * P.d_in + col : P.Vb + row;
+          const float w = c0v[sj][r];
           const float d = fmaf(batch.sc.weight_decay, w, v);
-          const float vn = fmaf(batch.sc.momentum, *vp, d);
+          const float vn = fmaf(batch.sc.momentum, c1v[sj][r], d);
           const float wn2 = fmaf(-batch.sc.lr, vn, w);
           *vp = vn;
           *wp = wn2;
@@ -430,7 +460,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
         }
       }
     }
-  }
+  });
   if (EPI == EPI_UPDATE) {
     if (__any(bad) && lane == 0) raise_flag(batch.sc.flags, KFAC_FLAG_NONFINITE);
   }
