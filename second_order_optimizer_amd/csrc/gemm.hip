@@ -391,7 +391,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   // Read-modify-write epilogues first issue every read of a block row (from a
   // clamped, always valid address), then compute and store: one memory round
   // trip per block row instead of one per element.
-  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_SYM_EMA || EPI == EPI_SYRK || EPI == EPI_UPDATE;
+  // (the factor SYRK reads C in place: its EMA problems are few and the
+  // staging registers would cost the far more numerous split problems)
+  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_SYM_EMA || EPI == EPI_UPDATE;
   const bool ema = (EPI == EPI_SYM_EMA) || (EPI == EPI_SYRK && P.nsplit == 1);
   bool bad = false;
   bool skip = false;
@@ -437,7 +439,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SYM_EMA || EPI == EPI_SYRK) {
           if (row <= col) {
-            const float o = P.beta * c0v[sj][r] + P.alpha * v;
+            const float o = P.beta * (EPI == EPI_SYRK ? Cp[idx] : c0v[sj][r]) + P.alpha * v;
             Cp[idx] = o;
             if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
