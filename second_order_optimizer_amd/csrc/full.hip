@@ -75,6 +75,113 @@ __global__ void __launch_bounds__(256) sym_reduce_kernel(SymRedTab tab) {
 }
 
 // ---------------------------------------------------------------------------
+// im2col of convolution tensors for the factor SYRK: X[n][i] with
+// n = (b, ho, wo) and i = (c, kh, kw), zero in the padding, rows of pitch ld.
+// An output gradient [B, C, Ho, Wo] is the case k = 1, stride 1, pad 0 (a
+// transpose to [B Ho Wo, C]).  The SYRK then reads X row-major with 16-byte
+// loads instead of gathering.  One block per 64 x 64 tile of X, transposed
+// through LDS: reads run along n (contiguous input for stride 1), writes
+// along i.
+
+constexpr int kMaxCols = 56;
+constexpr int kColTile = 64;
+struct ColItem {
+  const float* x;
+  float* X;
+  int32_t C, H, W, k, stride, pad, Ho, Wo;
+  int32_t d_in, ld, rows, blk_begin;
+};
+struct ColTab {
+  ColItem c[kMaxCols];
+  int32_t n;
+};
+
+__global__ void __launch_bounds__(256) im2col_kernel(ColTab tab) {
+  __shared__ float t[kColTile][kColTile + 1];
+  __shared__ int32_t coff[kColTile];   // per column of the tile: c H W + kh W + kw, or -1 past d_in
+  __shared__ int32_t ckh[kColTile], ckw[kColTile];
+  int lo = 0, hi = tab.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.c[mid].blk_begin <= static_cast<int>(blockIdx.x)) lo = mid; else hi = mid - 1;
+  }
+  const ColItem& It = tab.c[lo];
+  const float* __restrict__ x = It.x;
+  float* __restrict__ X = It.X;
+  const int ti = (It.d_in + kColTile - 1) / kColTile;
+  const int tile = blockIdx.x - It.blk_begin;
+  const int n0 = (tile / ti) * kColTile, i0 = (tile - (tile / ti) * ti) * kColTile;
+  const int H = It.H, W = It.W;
+  if (threadIdx.x < kColTile) {
+    const int i = i0 + threadIdx.x;
+    const int kk = It.k * It.k;
+    const int c = i / kk, rem = i - c * kk;
+    const int kh = rem / It.k, kw = rem - kh * It.k;
+    coff[threadIdx.x] = i < It.d_in ? (c * H + kh) * W + kw : -1;
+    ckh[threadIdx.x] = kh;
+    ckw[threadIdx.x] = kw;
+  }
+  __syncthreads();
+  const int lx = threadIdx.x & (kColTile - 1), ly = threadIdx.x >> 6;
+  // this thread reads row n0 + lx for columns i0 + ly + 4 j
+  {
+    const int n = n0 + lx;
+    const int nc = min(n, It.rows - 1);
+    const int P = It.Ho * It.Wo;
+    const int b = nc / P, p = nc - b * P;
+    const int ho = p / It.Wo, wo = p - ho * It.Wo;
+    const int hb = ho * It.stride - It.pad, wb = wo * It.stride - It.pad;
+    const float* xb = x + static_cast<int64_t>(b) * It.C * H * W + hb * W + wb;   // 32-bit offsets within one image
+    const bool nin = n < It.rows;
+    float v[kColTile / 4];
+#pragma unroll
+    for (int j = 0; j < kColTile / 4; ++j) {
+      const int e = ly + 4 * j;
+      const int h = hb + ckh[e], w = wb + ckw[e];
+      const bool in = nin && coff[e] >= 0 && h >= 0 && h < H && w >= 0 && w < W;
+      v[j] = in ? xb[coff[e]] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kColTile / 4; ++j) t[ly + 4 * j][lx] = v[j];
+  }
+  __syncthreads();
+  // and writes 4 consecutive columns of rows n0 + 16 q + (tid / 16)
+  const int i4 = (threadIdx.x & 15) * 4;
+  const int i = i0 + i4;
+  const bool vec = i + 4 <= It.d_in;   // rows have a pitch of 4 floats
+#pragma unroll
+  for (int q = 0; q < kColTile / 16; ++q) {
+    const int r = 16 * q + (threadIdx.x >> 4);
+    const int n = n0 + r;
+    if (n >= It.rows) continue;
+    float* o = X + static_cast<int64_t>(n) * It.ld + i;
+    if (vec) {
+      *reinterpret_cast<f32x4*>(o) = f32x4{t[i4][r], t[i4 + 1][r], t[i4 + 2][r], t[i4 + 3][r]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < It.d_in) o[e] = t[i4 + e][r];
+    }
+  }
+}
+
+kfac_status_t launch_im2col(const std::vector<ColItem>& items, hipStream_t st) {
+  for (size_t i0 = 0; i0 < items.size(); i0 += kMaxCols) {
+    ColTab tab{};
+    int blocks = 0;
+    for (size_t i = i0; i < items.size() && tab.n < kMaxCols; ++i) {
+      ColItem c = items[i];
+      c.blk_begin = blocks;
+      blocks += (c.rows + kColTile - 1) / kColTile * ((c.d_in + kColTile - 1) / kColTile);
+      tab.c[tab.n++] = c;
+    }
+    hipLaunchKernelGGL(im2col_kernel, dim3(blocks), dim3(256), 0, st, tab);
+    if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
+  }
+  return KFAC_OK;
+}
+
+// ---------------------------------------------------------------------------
 // damped Cholesky inverse, batched over matrices
 
 constexpr int kMaxMats = 40;
@@ -350,6 +457,8 @@ struct FullPlan {
   std::vector<float*> part;      // per layer and factor (2 li + which): split-K partials, or null
   std::vector<int> nsplit;       // per layer and factor
   std::vector<float*> T;         // per layer, d_out x d_a
+  std::vector<float*> xcol;      // per layer and factor: fp32 convolution tensor as [rows, width], or null
+  std::vector<int> xcol_ld;      // their row pitch (floats)
   std::vector<Mat> mats;         // inverse work per factor
 };
 
@@ -395,6 +504,16 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
     for (int which = 0; which < 2; ++which) {
+      const bool col = g.conv && fp32_factor(layers[li], which);
+      const int w = which == 0 ? g.d_in : g.d_out;
+      const int ld = (w + 3) / 4 * 4;
+      P.xcol_ld.push_back(col ? ld : 0);
+      P.xcol.push_back(col ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.rows) * ld * 4)) : nullptr);
+    }
+  }
+  for (int li = 0; li < n; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    for (int which = 0; which < 2; ++which) {
       const int d = which == 0 ? g.d_a : g.d_out;
       Mat m{};
       m.F = which == 0 ? layers[li].A : layers[li].G;
@@ -430,16 +549,17 @@ kfac_status_t launch_sym_reduce(const std::vector<SymRedItem>& items, hipStream_
   return KFAC_OK;
 }
 
-// FACTORS: every factor of the stack in a few batched launches, one per
-// operand kind (row-major fp32, implicit im2col, NCHW gradient, bf16), each
-// split into direct-EMA and split-K problems; then the batched split reduce.
+// FACTORS: convolution tensors laid out as rows (one batched im2col
+// launch), then every fp32 factor of the stack in batched row-major SYRK
+// launches (direct EMA, or split rows summed by the batched reduce
+// afterwards), and the bf16 factors on the bf16 SYRK.
 kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                             hipStream_t st) {
   const float eps = hp.ema_decay;
-  enum { K_MN = 0, K_IM2COL = 1, K_NCHW = 2 };
-  std::vector<GemmProb> probs[3];
+  std::vector<GemmProb> probs;
   std::vector<SymRedItem> reds;
   std::vector<SyrkBf16Prob> bf16;
+  std::vector<ColItem> cols;
   for (int li = 0; li < n; ++li) {
     const kfac_layer_t& L = layers[li];
     const LayerGeom g = geom_of(L);
@@ -469,18 +589,28 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
       p.ke = static_cast<int>(g.rows);
       p.tri = TRI_UPPER;
       p.a_special = p.b_special = special;
-      int kind;
       if (!g.conv) {
-        kind = K_MN;
         p.lda = p.ldb = which == 0 ? g.d_in : g.d_out;
-      } else if (which == 0) {
-        kind = K_IM2COL;
-        const int geo[8] = {g.c_in, g.h, g.w, g.kh, g.stride, g.pad, g.h_out, g.w_out};
-        for (int e = 0; e < 8; ++e) p.geo[e] = geo[e];
       } else {
-        kind = K_NCHW;
-        p.geo[0] = g.h_out * g.w_out;
-        p.geo[1] = g.d_out;
+        // the convolution tensor as rows first (im2col of the input; the
+        // output gradient transposed), then the same SYRK as a linear layer's
+        const int f = 2 * li + which;
+        ColItem c{};
+        c.x = static_cast<const float*>(X);
+        c.X = P.xcol[f];
+        if (which == 0) {
+          c.C = g.c_in; c.H = g.h; c.W = g.w; c.k = g.kh; c.stride = g.stride; c.pad = g.pad;
+          c.d_in = g.d_in;
+        } else {
+          c.C = g.d_out; c.H = g.h_out; c.W = g.w_out; c.k = 1; c.stride = 1; c.pad = 0;
+          c.d_in = g.d_out;
+        }
+        c.Ho = g.h_out; c.Wo = g.w_out;
+        c.ld = P.xcol_ld[f];
+        c.rows = static_cast<int32_t>(g.rows);
+        cols.push_back(c);
+        p.A = p.B = P.xcol[f];
+        p.lda = p.ldb = P.xcol_ld[f];
       }
       const int s = P.nsplit[2 * li + which];
       p.ldc = d;
@@ -489,12 +619,12 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         p.C = F;
         p.alpha = alpha;
         p.beta = eps;
-        probs[kind].push_back(p);
+        probs.push_back(p);
       } else {
         p.C = P.part[2 * li + which];
         p.split_stride = static_cast<int64_t>(d) * d;
         p.alpha = 1.0f;
-        probs[kind].push_back(p);
+        probs.push_back(p);
         SymRedItem r{};
         r.part = p.C;
         r.F = F;
@@ -507,11 +637,13 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
     }
   }
   GemmScalars sc{};
-  const int modes[3] = {OP_MN, OP_IM2COL, OP_NCHW};
   kfac_status_t r;
-  for (int kind = 0; kind < 3; ++kind) {
-    if (probs[kind].empty()) continue;
-    r = launch_gemm(probs[kind], modes[kind], modes[kind], EPI_SYRK, sc, st, TILES_SMALL);
+  if (!cols.empty()) {
+    r = launch_im2col(cols, st);
+    if (r != KFAC_OK) return r;
+  }
+  if (!probs.empty()) {
+    r = launch_gemm(probs, OP_MN, OP_MN, EPI_SYRK, sc, st, TILES_SMALL);
     if (r != KFAC_OK) return r;
   }
   if (!bf16.empty()) {
