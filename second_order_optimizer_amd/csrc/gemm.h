@@ -10,21 +10,12 @@ namespace kfac {
 
 constexpr int kTile = 128;     // output tile (both dimensions)
 constexpr int kTileK = 16;     // K step staged through LDS
-constexpr int kMaxGemmProbs = 18;
+constexpr int kMaxGemmProbs = 25;   // problem table of one launch (kernel arguments stay within 4 KB)
 
 // Operand layouts.  For A (M x K): OP_MN stores element (i, k) at
 // A[k * lda + i] (i contiguous), OP_K at A[i * lda + k] (k contiguous).
 // For B (K x N): OP_MN stores (k, j) at B[k * ldb + j], OP_K at B[j * ldb + k].
-// Two virtual layouts serve the factor SYRK of convolutions, with X the
-// [rows, columns] matrix whose Gram matrix is wanted (A = X^T, B = X):
-//   OP_IM2COL: X[n][i] is the im2col element of an NCHW input: n = (b, ho, wo),
-//              i = (c, kh, kw), zero in the padding (geometry in GemmProb.geo);
-//   OP_NCHW  : X[n][i] = g[b][i][p] of an NCHW output gradient, n = b * P + p.
-enum GemmOp : int { OP_MN = 0, OP_K = 1, OP_IM2COL = 2, OP_NCHW = 3 };
-
-// GemmProb.geo for OP_IM2COL: {C, H, W, k, stride, pad, Ho, Wo};
-// for OP_NCHW: {P (= Ho * Wo), channels, ...}.
-enum GemmGeo : int { GEO_C = 0, GEO_H, GEO_W, GEO_K, GEO_S, GEO_P, GEO_HO, GEO_WO };
+enum GemmOp : int { OP_MN = 0, OP_K = 1 };
 
 // Epilogues.
 enum GemmEpi : int {
@@ -62,7 +53,6 @@ struct GemmProb {
   int32_t nsplit;         // K splits (each writes C + s * split_stride)
   int32_t blk_begin;
   int32_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
-  int32_t geo[8];         // OP_IM2COL / OP_NCHW geometry (shared by both operands)
   float alpha, beta;
 };
 

@@ -51,32 +51,16 @@ struct Cfg {
   static constexpr int kItems = kTileK * kBT / 4 / kThreads;   // float4 groups per thread per operand
 };
 
-// LDS layout of an operand mode: [k][m] rows for i-contiguous (and im2col)
-// operands, [m][k] rows for k-contiguous (and NCHW-gradient) ones.
-__host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K || mode == OP_NCHW || mode == OP_IM2COL; }
-
-// Per-thread column decomposition of an im2col operand, fixed for the whole K
-// loop: for each of the thread's 4 * kItems columns, the offset of (c, kh, kw)
-// inside a sample and the (kh, kw) tap for the padding test.
-template <bool BIG>
-struct ColInfo {
-  int off[8];
-  int kh[8];
-  int kw[8];
-};
-
-// Per-thread row decomposition of an im2col operand: for each of the
-// thread's kItems rows n of the current K stage, (b, ho, wo); advanced by
-// kTileK rows per stage without division.
-struct RowState {
-  int b[2], ho[2], wo[2];
-};
+// LDS layout of an operand mode: [k][m] rows for i-contiguous operands,
+// [m][k] rows for k-contiguous ones.
+__host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K; }
 
 struct GemmBatch {
   GemmProb p[kMaxGemmProbs];
   int32_t n;
   GemmScalars sc;
 };
+static_assert(sizeof(GemmBatch) <= 4096, "kernel arguments");
 
 __device__ inline int find_prob(const GemmBatch& b, int blk) {
   int lo = 0, hi = b.n - 1;
@@ -90,63 +74,9 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
 // This thread's share of a 16 x BT operand slab (kItems groups of 4 floats).
 // MN layout: group g covers row kk = g / (BT/4), columns 4 (g % (BT/4)) .. +3.
 // K layout : group g covers column mm = g / 4, k = 4 (g % 4) .. +3.
-template <bool BIG, int MODE>
-__device__ inline void col_info(ColInfo<BIG>& ci, const int* geo, int m0, int mlim, int special) {
-  using C = Cfg<BIG>;
-  if (MODE != OP_IM2COL) return;
-  const int k = geo[GEO_K], HW = geo[GEO_H] * geo[GEO_W];
-#pragma unroll
-  for (int h = 0; h < C::kItems; ++h) {
-    const int mq = m0 + (threadIdx.x + h * C::kThreads) / 4;   // k-major: one column per item
-    const int c = mq / (k * k), r = mq - c * k * k;
-    const int kh = r / k, kw = r - (r / k) * k;
-    const bool real = mq < mlim && mq != special;
-    ci.off[h] = c * HW + kh * geo[GEO_W] + kw;
-    ci.kh[h] = real ? kh : -(1 << 20);   // never inside the image
-    ci.kw[h] = kw;
-  }
-}
-
-// k-major im2col items: item h of this thread covers rows n .. n+3 with
-// n = k0 + 4 (g % 4); the state holds (b, ho, wo) of n.
-template <bool BIG, int MODE>
-__device__ inline void row_init(RowState& rs, const int* geo, int k0) {
-  using C = Cfg<BIG>;
-  static_assert(C::kItems <= 2, "row state holds 2 rows");
-  if (MODE != OP_IM2COL) return;
-  const int HoWo = geo[GEO_HO] * geo[GEO_WO];
-#pragma unroll
-  for (int h = 0; h < C::kItems; ++h) {
-    const int n = k0 + ((threadIdx.x + h * C::kThreads) % 4) * 4;
-    rs.b[h] = n / HoWo;
-    const int rem = n - rs.b[h] * HoWo;
-    rs.ho[h] = rem / geo[GEO_WO];
-    rs.wo[h] = rem - rs.ho[h] * geo[GEO_WO];
-  }
-}
-
-__device__ inline void step_pos(int& b, int& ho, int& wo, int by, int Ho, int Wo) {
-  wo += by;
-  while (wo >= Wo) {
-    wo -= Wo;
-    if (++ho == Ho) {
-      ho = 0;
-      ++b;
-    }
-  }
-}
-
-template <bool BIG, int MODE>
-__device__ inline void row_advance(RowState& rs, const int* geo) {
-  if (MODE != OP_IM2COL) return;
-#pragma unroll
-  for (int h = 0; h < Cfg<BIG>::kItems; ++h) step_pos(rs.b[h], rs.ho[h], rs.wo[h], kTileK, geo[GEO_HO], geo[GEO_WO]);
-}
-
 template <bool BIG, int MODE, bool EXTRA>
 __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
-                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec,
-                                 const int* geo, const ColInfo<BIG>& ci, const RowState& rs) {
+                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec) {
   using C = Cfg<BIG>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
@@ -169,47 +99,6 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
           else if (m + q < mlim) v = p[q];
         }
         r[4 * h + q] = v;
-      }
-    } else if (MODE == OP_IM2COL) {
-      // column m of the unfolded input (tap (c, kh, kw) from the column
-      // info), rows n .. n+3 = consecutive output positions: for stride 1
-      // consecutive input addresses, so a wavefront's lanes read few lines
-      const int m = m0 + g / 4;
-      const int n = k0 + (g % 4) * 4;
-      const int H = geo[GEO_H], W = geo[GEO_W];
-      const int64_t CHW = static_cast<int64_t>(geo[GEO_C]) * H * W;
-      const bool special_col = m == special;
-      int b = rs.b[h], ho = rs.ho[h], wo = rs.wo[h];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned hh = static_cast<unsigned>(ho * geo[GEO_S] - geo[GEO_P] + ci.kh[h]);
-        const unsigned ww = static_cast<unsigned>(wo * geo[GEO_S] - geo[GEO_P] + ci.kw[h]);
-        float v = 0.f;
-        if (n + q < klim) {
-          if (special_col) v = 1.0f;
-          else if (hh < static_cast<unsigned>(H) && ww < static_cast<unsigned>(W))
-            v = base[b * CHW + ci.off[h] + (static_cast<int>(hh) - ci.kh[h]) * W + (static_cast<int>(ww) - ci.kw[h])];
-        }
-        r[4 * h + q] = v;
-        if (q < 3) step_pos(b, ho, wo, 1, geo[GEO_HO], geo[GEO_WO]);
-      }
-    } else if (MODE == OP_NCHW) {
-      // element (m = channel, n = b * P + p) at base[(b * channels + m) * P + p]
-      const int m = m0 + g / 4;
-      const int k = k0 + (g % 4) * 4;
-      const int P = geo[0], ch = geo[1];
-      const bool min_ = m < mlim;
-      const int b0 = k / P, p0 = k - b0 * P;
-      if (vec && min_ && k + 3 < klim && p0 + 3 < P) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(base + (static_cast<int64_t>(b0) * ch + m) * P + p0);
-        r[4 * h] = v[0]; r[4 * h + 1] = v[1]; r[4 * h + 2] = v[2]; r[4 * h + 3] = v[3];
-        continue;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = k + q;
-        const int b = n / P, p = n - b * P;
-        r[4 * h + q] = (min_ && n < klim) ? base[(static_cast<int64_t>(b) * ch + m) * P + p] : 0.f;
       }
     } else {
       const int m = m0 + g / 4;
@@ -314,17 +203,10 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   float ra[C::kItems * 4], rb[C::kItems * 4];
-  ColInfo<BIG> cia, cib;
-  col_info<BIG, AMODE>(cia, P.geo, i0, P.M, P.a_special);
-  col_info<BIG, BMODE>(cib, P.geo, j0, P.N, P.b_special);
-  // both operands of an im2col SYRK walk the same rows
-  RowState rs;
-  row_init<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo, kb);
   int buf = 0;
   if (kb < ke) {
-    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec, P.geo, cia, rs);
-    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec, P.geo, cib, rs);
-    row_advance<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo);
+    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec);
+    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec);
     store_slab<BIG, AMODE>(sA[0], ra);
     store_slab<BIG, BMODE>(sB[0], rb);
   }
@@ -335,11 +217,8 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   for (int k0 = kb; k0 < ke; k0 += kTileK) {
     const bool more = k0 + kTileK < ke;
     if (more) {
-      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec, P.geo,
-                                  cia, rs);
-      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec, P.geo, cib,
-                                   rs);
-      row_advance<BIG, AMODE == OP_IM2COL ? OP_IM2COL : BMODE>(rs, P.geo);
+      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec);
+      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec);
     }
     if constexpr (decltype(compute)::value) {
     const float* a = sA[buf];
@@ -485,8 +364,6 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_SUB)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYRK)
-  KFAC_GEMM_CASE(OP_IM2COL, OP_IM2COL, EPI_SYRK)
-  KFAC_GEMM_CASE(OP_NCHW, OP_NCHW, EPI_SYRK)
 #undef KFAC_GEMM_CASE
   return KFAC_ERR_UNSUPPORTED;
 }
@@ -524,7 +401,6 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
     p.tiles_n = (p.N + bt - 1) / bt;
     p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
     p.b_vec = (p.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(p.B) % 16) == 0 && (p.kb % 4) == 0;
-    if (amode == OP_NCHW) p.a_vec = p.b_vec = (p.geo[0] % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0;
     if (tiles_for(p, bt) > 0) ps.push_back(p);
   }
   // longest workgroups first, so a launch ends on short ones
