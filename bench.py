@@ -223,7 +223,7 @@ def run_full(cfg, args):
     ideal = fs / (syrk_peak * 1e12) + fp / (FP32_MFMA_TFLOPS * 1e12)
     phases["combined_mfma_frac"] = ideal / ((t_fac + t_upd) * 1e-3)
     dom = max(("factors", t_fac), ("precond_update", t_upd), ("invert", t_inv / k), key=lambda x: x[1])[0]
-    names = {"factors": "factor SYRK + EMA launches (syrk_bf16_kernel / gemm_f32_kernel, EPI_SYM_EMA)",
+    names = {"factors": "factor SYRK + EMA launches (im2col, syrk_bf16_kernel / gemm_f32_kernel EPI_SYRK, split reduce)",
              "precond_update": "preconditioning GEMMs (gemm_f32_kernel, STORE then fused UPDATE epilogue)",
              "invert": "blocked Cholesky inverse launches"}
     d = phases[dom]

@@ -31,6 +31,7 @@ constexpr int kMaxReds = 64;
 struct SymRedItem {
   const float* part;
   float* F;
+  const int32_t* fail;   // when set and nonzero, F is left as it is
   int32_t d, nsplit, blk_begin, pad_;
   float alpha, beta;
 };
@@ -47,6 +48,7 @@ __global__ void __launch_bounds__(256) sym_reduce_kernel(SymRedTab tab) {
     if (tab.r[mid].blk_begin <= static_cast<int>(blockIdx.x)) lo = mid; else hi = mid - 1;
   }
   const SymRedItem& R = tab.r[lo];
+  if (R.fail != nullptr && *R.fail != 0) return;
   const int T = (R.d + 31) / 32;
   int u = blockIdx.x - R.blk_begin, I = 0;
   while (u >= T - I) { u -= T - I; ++I; }
@@ -60,7 +62,7 @@ __global__ void __launch_bounds__(256) sym_reduce_kernel(SymRedTab tab) {
       const int64_t e = static_cast<int64_t>(i) * R.d + j;
       float sum = 0.f;
       for (int k = 0; k < R.nsplit; ++k) sum += R.part[k * dd + e];
-      o = R.beta * R.F[e] + R.alpha * sum;
+      o = R.beta != 0.f ? R.beta * R.F[e] + R.alpha * sum : R.alpha * sum;
       if (I != J || i <= j) R.F[e] = o;
     }
     t[r][tx] = o;
@@ -185,6 +187,7 @@ kfac_status_t launch_im2col(const std::vector<ColItem>& items, hipStream_t st) {
 // damped Cholesky inverse, batched over matrices
 
 constexpr int kMaxMats = 40;
+constexpr int kLauRows = 1024;   // rows of Z per pass of the final Z^T Z
 
 struct Mat {
   const float* F;     // factor (upper triangle read)
@@ -655,8 +658,11 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
 
 kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st) {
   const std::vector<Mat>& mats = P.mats;
-  int nblk_max = 0;
-  for (const Mat& m : mats) nblk_max = std::max<int>(nblk_max, static_cast<int>(nblk_of(m.d)));
+  int nblk_max = 0, d_max = 0;
+  for (const Mat& m : mats) {
+    nblk_max = std::max<int>(nblk_max, static_cast<int>(nblk_of(m.d)));
+    d_max = std::max(d_max, m.d);
+  }
   GemmScalars sc{};
   // runs `fn` on the matrices selected by `pred`, kMaxMats at a time
   auto tables = [&](auto pred, int k, auto fn) -> kfac_status_t {
@@ -799,28 +805,55 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
     }
   }
-  // inverse = Z^T Z (upper tiles, mirrored), written only for matrices that factored
-  std::vector<GemmProb> lau;
-  for (size_t mi = 0; mi < mats.size(); ++mi) {
-    const Mat& m = mats[mi];
-    GemmProb p{};
-    p.A = m.Z;
-    p.B = m.Z;
-    p.lda = p.ldb = m.d;
-    p.C = m.Finv;
-    p.ldc = m.d;
-    p.M = p.N = m.d;
-    p.kb = 0;
-    p.ke = m.d;
-    p.tri = TRI_UPPER;
-    p.k_from_diag = 1;
-    p.a_special = p.b_special = -1;
-    p.fail = m.fail;
-    p.nsplit = 1;
-    gemm_set_tiles(p);
-    lau.push_back(p);
+  // inverse = Z^T Z.  Z is lower triangular, so element (i, j) sums over
+  // rows k >= max(i, j); the product goes into L (free once Z is complete;
+  // upper tiles only) and the reduce writes it, mirrored, into the inverse of
+  // every matrix that factored.  The top-left tile of the largest factor sums
+  // all of its d_max rows; when that one workgroup would take a large share
+  // of the whole product (total d^3 / 3 below 2^26 d_max flops: few large
+  // factors), the rows are taken kLauRows at a time (the first pass stores,
+  // later passes add) so that no workgroup runs the whole height.
+  double lau_flops = 0.0;
+  for (const Mat& m : mats) lau_flops += static_cast<double>(m.d) * m.d * m.d / 3.0;
+  const bool by_rows = lau_flops < 67108864.0 * d_max;
+  const int rows_per_pass = by_rows ? kLauRows : d_max;
+  for (int k0 = 0; k0 < d_max; k0 += rows_per_pass) {
+    std::vector<GemmProb> lau;
+    for (const Mat& m : mats) {
+      if (m.d <= k0) continue;
+      GemmProb p{};
+      p.A = m.Z;
+      p.B = m.Z;
+      p.lda = p.ldb = m.d;
+      p.C = m.L;
+      p.ldc = m.d;
+      p.M = p.N = m.d;
+      p.kb = k0;
+      p.ke = std::min(m.d, k0 + rows_per_pass);
+      p.tri = TRI_UPPER;
+      p.k_from_diag = 1;
+      p.a_special = p.b_special = -1;
+      p.nsplit = 1;
+      p.alpha = k0 == 0 ? 1.f : -1.f;
+      gemm_set_tiles(p);
+      lau.push_back(p);
+    }
+    r = launch_gemm(lau, OP_MN, OP_MN, k0 == 0 ? EPI_STORE : EPI_SUB, sc, st, by_rows ? TILES_SMALL : TILES_AUTO);
+    if (r != KFAC_OK) return r;
   }
-  return launch_gemm(lau, OP_MN, OP_MN, EPI_SYM_IFOK, sc, st);
+  std::vector<SymRedItem> out;
+  for (const Mat& m : mats) {
+    SymRedItem it{};
+    it.part = m.L;
+    it.F = m.Finv;
+    it.fail = m.fail;
+    it.d = m.d;
+    it.nsplit = 1;
+    it.alpha = 1.f;
+    it.beta = 0.f;
+    out.push_back(it);
+  }
+  return launch_sym_reduce(out, st);
 }
 
 kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,

@@ -20,11 +20,10 @@ enum GemmOp : int { OP_MN = 0, OP_K = 1 };
 // Epilogues.
 enum GemmEpi : int {
   EPI_STORE = 0,      // C = alpha * acc
-  EPI_SUB = 1,        // C -= acc
-  EPI_SYM_EMA = 2,    // upper tiles; C = beta * C + alpha * acc, mirrored to the lower triangle
-  EPI_UPDATE = 3,     // P = acc; D = P + wd W; V = mu V + D; W -= lr V  (columns >= d_in go to b / mom_b)
-  EPI_SYM_IFOK = 4,   // upper tiles; C = acc mirrored, skipped when *fail != 0
-  EPI_SYRK = 5,       // upper tiles; nsplit == 1: as EPI_SYM_EMA, else C + split * split_stride = alpha * acc
+  EPI_SUB = 1,        // C -= alpha * acc
+  EPI_UPDATE = 2,     // P = acc; D = P + wd W; V = mu V + D; W -= lr V  (columns >= d_in go to b / mom_b)
+  EPI_SYRK = 3,       // upper tiles; nsplit == 1: C = beta * C + alpha * acc (C not read when beta == 0),
+                      // mirrored to the lower triangle; else C + split * split_stride = alpha * acc
 };
 
 // Tile grids.
@@ -39,7 +38,6 @@ struct GemmProb {
   float* Wb;
   float* V;
   float* Vb;
-  const int32_t* fail;    // EPI_SYM_IFOK
   int64_t split_stride;   // C offset between K splits (floats)
   int32_t lda, ldb, ldc;
   int32_t M, N;

@@ -272,11 +272,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   // trip per block row instead of one per element.
   // (the factor SYRK reads C in place: its EMA problems are few and the
   // staging registers would cost the far more numerous split problems)
-  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_SYM_EMA || EPI == EPI_UPDATE;
-  const bool ema = (EPI == EPI_SYM_EMA) || (EPI == EPI_SYRK && P.nsplit == 1);
+  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE;
+  const bool ema = EPI == EPI_SYRK && P.nsplit == 1;
   bool bad = false;
-  bool skip = false;
-  if (EPI == EPI_SYM_IFOK) skip = *P.fail != 0;
   // block rows by a compile-time index: a runtime one would place acc in scratch
   static_for<0, C::kBI>([&](auto si_c) {
     constexpr int si = decltype(si_c)::value;
@@ -295,7 +293,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
             const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
             c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
             c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
-          } else if (EPI == EPI_SUB || ema) {
+          } else {
             c0v[sj][r] = Cp[idx];
           }
         }
@@ -313,19 +311,14 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
         if (EPI == EPI_STORE) {
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SUB) {
-          Cp[idx] = c0v[sj][r] - v;
+          Cp[idx] = c0v[sj][r] - P.alpha * v;
         } else if (EPI == EPI_SYRK && !ema) {
           Cp[idx] = P.alpha * v;
-        } else if (EPI == EPI_SYM_EMA || EPI == EPI_SYRK) {
+        } else if (EPI == EPI_SYRK) {
           if (row <= col) {
-            const float o = P.beta * (EPI == EPI_SYRK ? Cp[idx] : c0v[sj][r]) + P.alpha * v;
+            const float o = P.beta != 0.f ? P.beta * Cp[idx] + P.alpha * v : P.alpha * v;
             Cp[idx] = o;
             if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
-          }
-        } else if (EPI == EPI_SYM_IFOK) {
-          if (row <= col && !skip) {
-            Cp[idx] = v;
-            if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = v;
           }
         } else if (EPI == EPI_UPDATE) {
           const bool wcol = col < P.d_in;
@@ -357,8 +350,9 @@ kfac_status_t launch_group(const GemmBatch& b, int blocks, bool big, hipStream_t
 kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm, int epi, hipStream_t s) {
 #define KFAC_GEMM_CASE(A_, B_, E_) \
   if (am == A_ && bm == B_ && epi == E_) return launch_group<A_, B_, E_>(b, blocks, big, s);
+  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_STORE)
+  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_UPDATE)
-  KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SYM_IFOK)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_STORE)
