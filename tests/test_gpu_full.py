@@ -51,10 +51,11 @@ def test_fp32_linear_split_k(gpu_lib):
 
 
 def test_conv_split_k_and_layouts(gpu_lib):
-    """Convolution factors gathered im2col-style inside the GEMM: a 7x7/2 stem
-    with more rows than one K split (16,900 rows -> 2 splits), an output plane
-    whose size is not a multiple of 4 (scalar gradient loads) and one that is
-    (vector loads), a conv with a bias column."""
+    """Convolution factors (im2col rows and transposed gradients, then the
+    row-major SYRK): a 7x7/2 stem with 16,900 rows (9 row splits summed by the
+    reduce) and 147 unfold columns (a ragged 64-column im2col tile), a 3x3
+    conv with 7 output channels (a ragged row pitch of 8), a strided conv with
+    a bias column."""
     L = [synth.conv("stem", 3, 8, 7, 2, 3, 4, 130),
          synth.conv("odd_plane", 5, 7, 3, 1, 1, 3, 7),
          synth.conv("even_plane", 6, 9, 3, 2, 1, 2, 16, bias=True)]
