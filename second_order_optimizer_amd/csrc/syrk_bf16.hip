@@ -224,19 +224,241 @@ syrk_bf16_kernel(Batch batch) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same SYRK for rows of a multiple of 8 elements (16-byte aligned), with
+// CDNA4's direct-to-LDS loads and transposing LDS reads.  X is staged
+// row-major, 32 rows per stage, in a 4-stage LDS ring filled by
+// buffer_load_dwordx4 ... lds (no registers; rows past the end read as zero
+// through the buffer's range check), so loads run 3 stages ahead of the
+// MFMAs.  An MFMA operand wants 8 consecutive rows of one column per lane:
+// two ds_read_b64_tr_b16 give it from the row-major tile (within 16 lanes,
+// lane i receives column c + i of the 4 rows the group addresses).  Each
+// row's 16-byte chunks are XOR-swizzled by 2 (row mod 4), which makes the
+// 4 rows x 32 bytes of a transposing read cover all 32 banks.  The workgroup
+// barrier carries no memory fence: a fence would wait for the loads still
+// in flight for later stages; each wavefront waits for its own loads of the
+// stage (vmcnt) before the barrier instead.
+
+constexpr int kRBK = 32;                  // rows of X per stage
+constexpr int kNS = 4;                    // stages in the LDS ring
+constexpr int kOpElems = kRBK * kBT;      // one operand of one stage (bf16 elements, 16 KB)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline bf16x8 tr_frag(const unsigned short* base, int off0, int off1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off1));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// element offset of this lane's first transposing read for the MFMA block
+// whose 32 columns start at cb0 (multiple of 32), k-step base ks (0 or 16);
+// the second read is 4 rows further (same swizzle: ks and 8 (g / 2) are
+// multiples of 8)
+__device__ inline int tr_off(int cb0, int ks, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = ks + 8 * (g >> 1) + (s >> 2);
+  const int chunk = (cb0 >> 3) + 2 * (g & 1) + ((s & 3) >> 1);
+  const int phys = chunk ^ ((row & 3) << 1);
+  return row * kBT + phys * 8 + 4 * (s & 1);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 16)
+#define KFAC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+syrk_bf16_dma_kernel(Batch batch) {
+  __shared__ __attribute__((aligned(16))) unsigned short ring[kNS][2][kOpElems];
+  const Prob& P = batch.p[find_prob(batch, blockIdx.x)];
+  int t = blockIdx.x - P.blk_begin;
+  int ti = 0;
+  while (t >= P.tiles - ti) { t -= P.tiles - ti; ++ti; }
+  const int tj = ti + t;
+  const bool diag = ti == tj;
+  const int i0 = ti * kBT, j0 = tj * kBT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = (wid >> 2) * 128, wn = (wid & 3) * 64;
+  const bool work = !(diag && wm > wn + 63);
+  const bool colsum = P.bias && diag && !work;
+  const int cs0 = (wid & 1) * 128;
+  const int width = P.width;
+  const int64_t rows = P.rows;
+  const int nops = diag ? 1 : 2;
+  // buffer resource: base, stride 0, num_records = the bytes of X (reads
+  // past them return 0), raw 32-bit data
+  const uint64_t xa = reinterpret_cast<uint64_t>(P.X);
+  const i32x4 rsrc = {static_cast<int>(xa & 0xffffffffu), static_cast<int>((xa >> 32) & 0xffffu),
+                      static_cast<int>(rows * width * 2), 0x00020000};
+
+  // this lane's chunk of each load: chunk p of the operand-stage buffer holds
+  // row p / 32, logical 16-byte chunk (p % 32) ^ 2 (row % 4)
+  uint32_t ld_off[2][2];
+#pragma unroll
+  for (int op = 0; op < 2; ++op)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = (wid * 2 + u) * 64 + lane;
+      const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 1);
+      ld_off[op][u] = static_cast<uint32_t>((static_cast<int64_t>(k) * width + (op ? j0 : i0) + 8 * c) * 2);
+    }
+  const uint32_t stage_bytes = static_cast<uint32_t>(kRBK) * width * 2;
+  const int64_t nst = (rows + kRBK - 1) / kRBK;
+  // loads of stage s into its ring slot: 16 bytes per lane straight into LDS
+  // at M0 + 16 lane.  Issued as assembly so that the compiler does not wait
+  // for them before every LDS read (it cannot tell ring slots apart); the
+  // per-stage vmcnt waits and the barrier below order them instead.
+  auto issue = [&](int64_t s) {
+    if (s >= nst) return;
+    const int slot = static_cast<int>(s % kNS);
+    const uint32_t so = static_cast<uint32_t>(s) * stage_bytes;
+#pragma unroll
+    for (int op = 0; op < 2; ++op) {
+      if (op >= nops) break;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) void*)(&ring[slot][op][(wid * 2 + u) * 512])));
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(so + ld_off[op][u]), "s"(rsrc)
+                     : "memory", "m0");
+      }
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
+
+  // per-lane operand offsets (element offsets inside an operand-stage buffer)
+  int oa[2][4], ob[2][2], oc[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      oa[h][i] = tr_off(wm + 32 * i, 16 * h, lane);
+      oc[h][i] = tr_off(cs0 + 32 * i, 16 * h, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ob[h][j] = tr_off(wn + 32 * j, 16 * h, lane);
+  }
+
+  for (int s = 0; s < kNS - 1; ++s) issue(s);
+  for (int64_t s = 0; s < nst; ++s) {
+    // this wavefront's loads of stage s are done once at most the loads of
+    // the stages issued after it remain; the barrier then covers everyone's
+    const int64_t after = (nst - 1 - s) < (kNS - 2) ? (nst - 1 - s) : (kNS - 2);
+    const int pending = static_cast<int>(after) * 2 * nops;
+    if (pending == 0) KFAC_WAIT_VM(0);
+    else if (pending == 2) KFAC_WAIT_VM(2);
+    else if (pending == 4) KFAC_WAIT_VM(4);
+    else KFAC_WAIT_VM(8);
+    __builtin_amdgcn_s_barrier();
+    issue(s + kNS - 1);   // into the slot stage s - 1 used; every wavefront is past it
+    const int slot = static_cast<int>(s % kNS);
+    const unsigned short* sa = ring[slot][0];
+    const unsigned short* sb = diag ? sa : ring[slot][1];
+    if (work) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 fa[4], fb[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = tr_frag(sa, oa[h][i], oa[h][i] + 4 * kBT);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = tr_frag(sb, ob[h][j], ob[h][j] + 4 * kBT);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    } else if (colsum) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 x = tr_frag(sa, oc[h][i], oc[h][i] + 4 * kBT);
+          acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, ones, acc[i][0], 0, 0, 0);
+        }
+      }
+    }
+    // every LDS read of this stage has returned before the next barrier, so
+    // the refill issued after it cannot overwrite data still being read
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  }
+
+  // accumulator r of block (i, j): row i0 + wm + 32 i + 8 (r/4) + 4 (lane/32) + r%4,
+  // column j0 + wn + 32 j + lane%32
+  float* F = P.F;
+  const int ldf = P.ldf;
+  if (work) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = j0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= width || col >= width || row > col) continue;
+          const int64_t idx = static_cast<int64_t>(row) * ldf + col;
+          const float o = P.beta * F[idx] + P.alpha * acc[i][j][r];
+          F[idx] = o;
+          if (row != col) F[static_cast<int64_t>(col) * ldf + row] = o;
+        }
+      }
+    }
+  }
+  if (colsum && (lane & 31) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = i0 + cs0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m >= width) continue;
+        const int64_t idx = static_cast<int64_t>(m) * ldf + width;
+        const float o = P.beta * F[idx] + P.alpha * acc[i][0][r];
+        F[idx] = o;
+        F[static_cast<int64_t>(width) * ldf + m] = o;
+      }
+    }
+    if (ti == 0 && cs0 == 0 && lane == 0) {
+      const int64_t c = static_cast<int64_t>(width) * ldf + width;
+      F[c] = P.beta * F[c] + P.alpha * static_cast<float>(rows);
+    }
+  }
+}
+
 }  // namespace
 
 kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream_t st) {
-  // vector loads need 16-byte aligned rows; problems are launched per kind
-  for (int vec = 0; vec < 2; ++vec) {
+  // kinds: 0 = ragged rows (scalar loads), 1 = 16-byte aligned rows whose
+  // byte offsets fit the buffer range (direct-to-LDS kernel), 2 = other
+  // aligned rows (register-staged vector loads)
+  auto kind_of = [](const SyrkBf16Prob& q) {
+    const bool v = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
+    if (!v) return 0;
+    return (q.rows + 2 * kRBK) * static_cast<int64_t>(q.width) * 2 < (int64_t(1) << 31) ? 1 : 2;
+  };
+  for (int vec = 0; vec < 3; ++vec) {
     size_t i = 0;
     while (i < probs.size()) {
       Batch b{};
       int blocks = 0;
       for (; i < probs.size() && b.n < kMaxProbs; ++i) {
         const SyrkBf16Prob& q = probs[i];
-        const bool v = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
-        if (v != (vec == 1)) continue;
+        if (kind_of(q) != vec) continue;
         Prob p{};
         p.X = q.X;
         p.F = q.F;
@@ -252,7 +474,8 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
         b.p[b.n++] = p;
       }
       if (b.n == 0) continue;
-      if (vec) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
+      if (vec == 1) hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3(blocks), dim3(512), 0, st, b);
+      else if (vec == 2) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
       else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3(blocks), dim3(512), 0, st, b);
       if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
     }
