@@ -243,6 +243,9 @@ constexpr int kRBK = 32;                  // rows of X per stage
 constexpr int kNS = 4;                    // stages in the LDS ring
 constexpr int kOpElems = kRBK * kBT;      // one operand of one stage (bf16 elements, 16 KB)
 
+// XOR swizzle of a row's 16-byte chunks
+__device__ inline int kSwz(int row) { return (row & 3) << 2; }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -262,7 +265,7 @@ __device__ inline int tr_off(int cb0, int ks, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int row = ks + 8 * (g >> 1) + (s >> 2);
   const int chunk = (cb0 >> 3) + 2 * (g & 1) + ((s & 3) >> 1);
-  const int phys = chunk ^ ((row & 3) << 1);
+  const int phys = chunk ^ kSwz(row);
   return row * kBT + phys * 8 + 4 * (s & 1);
 }
 
@@ -302,7 +305,7 @@ syrk_bf16_dma_kernel(Batch batch) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p = (wid * 2 + u) * 64 + lane;
-      const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 1);
+      const int k = p >> 5, c = (p & 31) ^ kSwz(k);
       ld_off[op][u] = static_cast<uint32_t>((static_cast<int64_t>(k) * width + (op ? j0 : i0) + 8 * c) * 2);
     }
   const uint32_t stage_bytes = static_cast<uint32_t>(kRBK) * width * 2;
