@@ -233,8 +233,9 @@ syrk_bf16_kernel(Batch batch) {
 // MFMAs.  An MFMA operand wants 8 consecutive rows of one column per lane:
 // two ds_read_b64_tr_b16 give it from the row-major tile (within 16 lanes,
 // lane i receives column c + i of the 4 rows the group addresses).  Each
-// row's 16-byte chunks are XOR-swizzled by 2 (row mod 4), which makes the
-// 4 rows x 32 bytes of a transposing read cover all 32 banks.  The workgroup
+// row's 16-byte chunks are XOR-swizzled by 4 (row mod 4): the 4 rows of a
+// transposing read then fall in distinct 64-byte windows of the 256-byte
+// bank cycle (no bank conflicts, by the SQ_LDS_BANK_CONFLICT counter).  The workgroup
 // barrier carries no memory fence: a fence would wait for the loads still
 // in flight for later stages; each wavefront waits for its own loads of the
 // stage (vmcnt) before the barrier instead.
