@@ -53,7 +53,6 @@ __device__ inline int find_prob(const Batch& b, int blk) {
 }
 
 // rows k .. k+7 of columns m .. m+7 (zero outside X)
-template <bool VEC>
 __device__ inline void load8(u16x8 (&v)[8], const uint16_t* __restrict__ X, int64_t rows, int width, int64_t k,
                              int m) {
 #pragma unroll
@@ -62,13 +61,9 @@ __device__ inline void load8(u16x8 (&v)[8], const uint16_t* __restrict__ X, int6
     u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
     if (row < rows) {
       const uint16_t* p = X + row * width + m;
-      if (VEC && m + 8 <= width) {
-        x = *reinterpret_cast<const u16x8*>(p);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (m + e < width) x[e] = p[e];
-      }
+      for (int e = 0; e < 8; ++e)
+        if (m + e < width) x[e] = p[e];
     }
     v[r] = x;
   }
@@ -85,7 +80,6 @@ __device__ inline void store_t(unsigned short* __restrict__ s, const u16x8 (&v)[
   }
 }
 
-template <bool VEC>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 syrk_bf16_kernel(Batch batch) {
   __shared__ __attribute__((aligned(16))) unsigned short sX[2][2][kBT * kLR];
@@ -128,14 +122,14 @@ syrk_bf16_kernel(Batch batch) {
   u16x8 v[8];
   const int64_t nst = (rows + kBK - 1) / kBK;
   if (stager) {
-    load8<VEC>(v, X, rows, width, kc * 8, mcol);
+    load8(v, X, rows, width, kc * 8, mcol);
     store_t(sX[0][half], v, mo, kc);
   }
   __syncthreads();
   int buf = 0;
   for (int64_t s = 0; s < nst; ++s) {
     const bool more = s + 1 < nst;
-    if (more && stager) load8<VEC>(v, X, rows, width, (s + 1) * kBK + kc * 8, mcol);
+    if (more && stager) load8(v, X, rows, width, (s + 1) * kBK + kc * 8, mcol);
     const unsigned short* sa = sX[buf][0];
     const unsigned short* sb = diag ? sa : sX[buf][1];
     if (work) {
@@ -447,44 +441,68 @@ syrk_bf16_dma_kernel(Batch batch) {
 }  // namespace
 
 kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream_t st) {
-  // kinds: 0 = ragged rows (scalar loads), 1 = 16-byte aligned rows whose
-  // byte offsets fit the buffer range (direct-to-LDS kernel), 2 = other
-  // aligned rows (register-staged vector loads)
-  auto kind_of = [](const SyrkBf16Prob& q) {
-    const bool v = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
-    if (!v) return 0;
-    return (q.rows + 2 * kRBK) * static_cast<int64_t>(q.width) * 2 < (int64_t(1) << 31) ? 1 : 2;
+  // Rows whose width is a multiple of 8 (16-byte aligned) go to the
+  // direct-to-LDS kernel, in row chunks whose byte offsets fit its 32-bit
+  // buffer range (chunk 0 applies the EMA, later chunks add: beta = 1);
+  // chunks of one factor run in successive launches.  Other widths go to the
+  // register-staged kernel with scalar loads.
+  struct Piece {
+    Prob p;
+    int pass;
   };
-  for (int vec = 0; vec < 3; ++vec) {
-    size_t i = 0;
-    while (i < probs.size()) {
-      Batch b{};
-      int blocks = 0;
-      for (; i < probs.size() && b.n < kMaxProbs; ++i) {
-        const SyrkBf16Prob& q = probs[i];
-        if (kind_of(q) != vec) continue;
-        Prob p{};
-        p.X = q.X;
-        p.F = q.F;
-        p.rows = q.rows;
-        p.width = q.width;
-        p.bias = q.bias;
-        p.ldf = q.width + (q.bias ? 1 : 0);
-        p.tiles = (q.width + kBT - 1) / kBT;
-        p.alpha = q.alpha;
-        p.beta = q.beta;
-        p.blk_begin = blocks;
-        blocks += p.tiles * (p.tiles + 1) / 2;
-        b.p[b.n++] = p;
-      }
-      if (b.n == 0) continue;
-      if (vec == 1) hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3(blocks), dim3(512), 0, st, b);
-      else if (vec == 2) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
-      else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3(blocks), dim3(512), 0, st, b);
-      if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
+  std::vector<Piece> dma, ragged;
+  for (const SyrkBf16Prob& q : probs) {
+    Prob p{};
+    p.X = q.X;
+    p.F = q.F;
+    p.rows = q.rows;
+    p.width = q.width;
+    p.bias = q.bias;
+    p.ldf = q.width + (q.bias ? 1 : 0);
+    p.tiles = (q.width + kBT - 1) / kBT;
+    p.alpha = q.alpha;
+    p.beta = q.beta;
+    const bool aligned = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
+    if (!aligned) {
+      ragged.push_back({p, 0});
+      continue;
+    }
+    const int64_t limit = ((int64_t(1) << 31) - 1) / (static_cast<int64_t>(q.width) * 2) - 2 * kRBK;
+    const int64_t chunk = std::max<int64_t>(kRBK, limit / kRBK * kRBK);
+    int pass = 0;
+    for (int64_t r0 = 0; r0 < q.rows; r0 += chunk, ++pass) {
+      Prob c = p;
+      c.X = q.X + r0 * q.width;
+      c.rows = std::min<int64_t>(chunk, q.rows - r0);
+      c.beta = pass == 0 ? q.beta : 1.0f;
+      dma.push_back({c, pass});
     }
   }
-  return KFAC_OK;
+  auto launch = [&](const std::vector<Piece>& pieces, bool use_dma) -> kfac_status_t {
+    int passes = 0;
+    for (const Piece& x : pieces) passes = std::max(passes, x.pass + 1);
+    for (int pass = 0; pass < passes; ++pass) {
+      size_t i = 0;
+      while (i < pieces.size()) {
+        Batch b{};
+        int blocks = 0;
+        for (; i < pieces.size() && b.n < kMaxProbs; ++i) {
+          if (pieces[i].pass != pass) continue;
+          Prob p = pieces[i].p;
+          p.blk_begin = blocks;
+          blocks += p.tiles * (p.tiles + 1) / 2;
+          b.p[b.n++] = p;
+        }
+        if (b.n == 0) continue;
+        if (use_dma) hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3(blocks), dim3(512), 0, st, b);
+        else hipLaunchKernelGGL(syrk_bf16_kernel, dim3(blocks), dim3(512), 0, st, b);
+        if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
+      }
+    }
+    return KFAC_OK;
+  };
+  kfac_status_t r = launch(dma, true);
+  return r != KFAC_OK ? r : launch(ragged, false);
 }
 
 }  // namespace kfac

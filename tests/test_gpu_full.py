@@ -221,3 +221,34 @@ def test_full_size_sampled(gpu_lib, name):
         assert e <= (2e-3 if cfg.act_dtype == "bf16" else 1e-3), (L.name, "update residual", e)
         assert max_rel(W1, W0 - hp["lr"] * V1) <= 1e-6
     say(f"{name} full-size worst:", {k: f"{v:.2e}" for k, v in worst.items()})
+
+
+def test_bf16_factor_row_chunks(gpu_lib):
+    """A bf16 factor whose input spans more than 2 GiB (140,000 rows x 8,192
+    columns) exceeds the 32-bit range of the direct-to-LDS loads: the SYRK
+    runs it as two row chunks (the EMA on the first, beta = 1 on the second).
+    FACTORS phase only; sampled entries of A, bias row included, vs the
+    oracle's column products, 2e-2."""
+    import torch
+    from second_order_optimizer_amd import PHASE_FACTORS
+    from second_order_optimizer_amd.stack import KfacStack
+    L = synth.linear("wide", 8192, 64, 140000, bias=True)
+    cfg = with_layers(synth.small_config("pair16k_bf16"), [L], steps=1)
+    hp = synth.hparams(cfg)
+    st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype)
+    st.set_state(0, synth.initial_state(cfg, 0))
+    inp = synth.step_inputs(cfg, 1, 0)
+    st.set_inputs(0, inp)
+    say("row-chunk layer resident")
+    st.step(st.hparams(hp, refresh=False, phase_mask=PHASE_FACTORS))
+    torch.cuda.synchronize()
+    assert st.flags() == 0
+    got = st.get_state(0)["A"]
+    eps = hp["ema_decay"]
+    rng = np.random.default_rng(3)
+    idx = np.unique(np.concatenate([[0, 8191, 8192], rng.integers(0, 8192, 5)]))
+    cols = {j: oracle.activation_column(L, inp["a"], j) for j in idx}
+    ref = np.array([[eps * (i == j) + (1 - eps) * cols[i] @ cols[j] / L.rows for j in idx] for i in idx])
+    e = max_rel(got[np.ix_(idx, idx)], ref)
+    say(f"row-chunk factor worst {e:.2e}")
+    assert e <= 2e-2
