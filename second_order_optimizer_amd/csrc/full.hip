@@ -746,64 +746,69 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
     }
   }
-  // Z = L^-1, block row by block row: Z_ik = Dinv_i R_ik (k < i), then
-  // R_jk -= L_ji Z_ik for the rows below (R starts at zero below the diagonal)
-  for (int i = 0; i < nblk_max; ++i) {
-    std::vector<GemmProb> fin, upd;
+  // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
+  // inverted diagonal blocks; at level s (128, 256, ...) each pair of
+  // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
+  // (r0, r0) with r0 = c0 + s, gives the block between them:
+  //   Z21 = -Z22 (L21 Z11)   (L21 = rows r0.., columns c0.. of L).
+  // T^T = Z11^T L21^T is staged in L's strict upper triangle at (c0, r0),
+  // which no later step reads (the Z^T Z pass overwrites L).  Z11 is lower
+  // triangular, so a tile of T^T needs rows k >= its first row of Z11; Z22
+  // is lower triangular, so a tile of Z21 needs k up to its last row.  The
+  // full-size pairs of one matrix and level form one strided problem (all
+  // three operands move by 2 s (d + 1) floats from pair to pair), the last,
+  // shorter pair another; every matrix advances one level per two launches.
+  for (int s = kNb; s < d_max; s *= 2) {
+    std::vector<GemmProb> g1, g2;
     for (const Mat& m : mats) {
       const int d = m.d;
-      const int nb = static_cast<int>(nblk_of(d));
-      if (nb <= i) continue;
-      const int r0 = i * kNb;
-      const int bk = std::min(kNb, d - r0);
-      if (i > 0) {
+      if (d <= s) continue;
+      const int npairs = (d - s + 2 * s - 1) / (2 * s);       // pairs with r0 = 2 p s + s < d
+      const int nfull = (d - 2 * s) >= 0 ? (d - 2 * s) / (2 * s) + 1 : 0;   // pairs with r0 + s <= d
+      for (int part = 0; part < 2; ++part) {
+        const int p0 = part == 0 ? 0 : nfull;
+        const int cnt = part == 0 ? nfull : npairs - nfull;
+        if (cnt <= 0) continue;
+        const int c0 = 2 * p0 * s, r0 = c0 + s;
+        const int m2 = part == 0 ? s : d - r0;
         GemmProb p{};
-        p.A = m.Dinv + static_cast<int64_t>(i) * kNb * kNb;
-        p.lda = kNb;
-        p.B = m.Z + static_cast<int64_t>(r0) * d;
+        p.A = m.Z + static_cast<int64_t>(c0) * d + c0;        // Z11, read as A[i][k] = Z11[k][i]
+        p.lda = d;
+        p.B = m.L + static_cast<int64_t>(r0) * d + c0;        // L21, read as B[k][j] = L21[j][k]
         p.ldb = d;
-        p.C = m.Z + static_cast<int64_t>(r0) * d;
+        p.C = m.L + static_cast<int64_t>(c0) * d + r0;        // T^T (s x m2) in L's upper triangle
         p.ldc = d;
-        p.M = bk;
-        p.N = r0;
+        p.M = s;
+        p.N = m2;
         p.kb = 0;
-        p.ke = bk;
+        p.ke = s;
         p.tri = TRI_FULL;
+        p.krange = KR_FROM_ROW;
         p.a_special = p.b_special = -1;
         p.alpha = 1.f;
         p.nsplit = 1;
+        p.nbatch = static_cast<int16_t>(cnt);
+        p.split_stride = static_cast<int64_t>(2 * s) * (d + 1);
         gemm_set_tiles(p);
-        fin.push_back(p);
-      }
-      if (nb > i + 1) {
-        const int r1 = r0 + kNb;
-        GemmProb q{};
-        q.A = m.L + static_cast<int64_t>(r1) * d + r0;
-        q.lda = d;
-        q.B = m.Z + static_cast<int64_t>(r0) * d;
-        q.ldb = d;
-        q.C = m.Z + static_cast<int64_t>(r1) * d;
-        q.ldc = d;
-        q.M = d - r1;
-        q.N = r1;
-        q.kb = 0;
-        q.ke = kNb;
-        q.tri = TRI_FULL;
-        q.a_special = q.b_special = -1;
-        q.alpha = 1.f;
-        q.nsplit = 1;
+        g1.push_back(p);
+        GemmProb q = p;
+        q.A = m.Z + static_cast<int64_t>(r0) * d + r0;        // Z22
+        q.B = m.L + static_cast<int64_t>(c0) * d + r0;        // T[k][j] = T^T[j][k]
+        q.C = m.Z + static_cast<int64_t>(r0) * d + c0;        // Z21
+        q.M = m2;
+        q.N = s;
+        q.ke = m2;
+        q.krange = KR_TO_ROW;
+        q.alpha = -1.f;
         gemm_set_tiles(q);
-        upd.push_back(q);
+        g2.push_back(q);
       }
     }
-    if (!fin.empty()) {
-      r = launch_gemm(fin, OP_K, OP_MN, EPI_STORE, sc, st);
-      if (r != KFAC_OK) return r;
-    }
-    if (!upd.empty()) {
-      r = launch_gemm(upd, OP_K, OP_MN, EPI_SUB, sc, st);
-      if (r != KFAC_OK) return r;
-    }
+    if (g1.empty()) break;
+    r = launch_gemm(g1, OP_MN, OP_K, EPI_STORE, sc, st);
+    if (r != KFAC_OK) return r;
+    r = launch_gemm(g2, OP_K, OP_K, EPI_STORE, sc, st);
+    if (r != KFAC_OK) return r;
   }
   // inverse = Z^T Z.  Z is lower triangular, so element (i, j) sums over
   // rows k >= max(i, j); the product goes into L (free once Z is complete;
@@ -831,7 +836,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       p.kb = k0;
       p.ke = std::min(m.d, k0 + rows_per_pass);
       p.tri = TRI_UPPER;
-      p.k_from_diag = 1;
+      p.krange = KR_FROM_DIAG;
       p.a_special = p.b_special = -1;
       p.nsplit = 1;
       p.alpha = k0 == 0 ? 1.f : -1.f;

@@ -10,7 +10,7 @@ namespace kfac {
 
 constexpr int kTile = 128;     // output tile (both dimensions)
 constexpr int kTileK = 16;     // K step staged through LDS
-constexpr int kMaxGemmProbs = 25;   // problem table of one launch (kernel arguments stay within 4 KB)
+constexpr int kMaxGemmProbs = 27;   // problem table of one launch (kernel arguments stay within 4 KB)
 
 // Operand layouts.  For A (M x K): OP_MN stores element (i, k) at
 // A[k * lda + i] (i contiguous), OP_K at A[i * lda + k] (k contiguous).
@@ -29,6 +29,14 @@ enum GemmEpi : int {
 // Tile grids.
 enum GemmTri : int { TRI_FULL = 0, TRI_UPPER = 1, TRI_LOWER = 2 };
 
+// Contraction range of one tile (i0, j0 = its first row and column).
+enum GemmKRange : int {
+  KR_ALL = 0,        // [kb, ke)
+  KR_FROM_DIAG = 1,  // from max(i0, j0): A[i][k] = 0 for k < i and B[k][j] = 0 for k < j
+  KR_FROM_ROW = 2,   // from i0: A[i][k] = 0 for k < i
+  KR_TO_ROW = 3,     // up to i0 + tile: A[i][k] = 0 for k > i
+};
+
 struct GemmProb {
   const void* A;
   const void* B;
@@ -38,19 +46,21 @@ struct GemmProb {
   float* Wb;
   float* V;
   float* Vb;
-  int64_t split_stride;   // C offset between K splits (floats)
+  int64_t split_stride;   // nsplit > 1: C offset between K splits; nbatch > 1: A, B and C offset between entries (floats)
   int32_t lda, ldb, ldc;
   int32_t M, N;
   int32_t kb, ke;         // contraction range [kb, ke)
   int32_t tiles_m, tiles_n;
-  int32_t tri;
-  int32_t k_from_diag;    // 1: a tile (ti, tj) starts its K loop at max(ti, tj) * kTile
   int32_t a_special;      // OP_MN: element i == a_special is 1.0 (bias column); OP_K: see A_extra; -1 none
   int32_t b_special;      // OP_MN: element j == b_special is 1.0; -1 none
   int32_t d_in;           // EPI_UPDATE: columns < d_in go to W / V
   int32_t nsplit;         // K splits (each writes C + s * split_stride)
   int32_t blk_begin;
-  int32_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
+  int16_t nbatch;         // identical problems at A, B, C + b * split_stride (b < nbatch; nsplit must be 1)
+  uint8_t tri;            // GemmTri
+  uint8_t krange;         // GemmKRange
+  uint8_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
+  uint8_t pad_[2];
   float alpha, beta;
 };
 

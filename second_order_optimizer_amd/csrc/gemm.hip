@@ -174,16 +174,27 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
   const int i0 = ti * C::kBT, j0 = tj * C::kBT;
   int kb = P.kb, ke = P.ke;
-  if (P.k_from_diag) kb = max(kb, max(i0, j0));
-  if (P.nsplit > 1) {
-    const int len = ((ke - kb + P.nsplit - 1) / P.nsplit + kTileK - 1) / kTileK * kTileK;
-    const int s0 = kb + split * len;
-    ke = min(ke, s0 + len);
-    kb = s0;
-  }
-  float* Cp = P.C + static_cast<int64_t>(split) * P.split_stride;
+  if (P.krange == KR_FROM_DIAG) kb = max(kb, max(i0, j0));
+  else if (P.krange == KR_FROM_ROW) kb = max(kb, i0);
+  else if (P.krange == KR_TO_ROW) ke = min(ke, i0 + C::kBT);
   const float* Ab = static_cast<const float*>(P.A);
   const float* Bb = static_cast<const float*>(P.B);
+  float* Cp = P.C;
+  if (P.nbatch > 1) {
+    // the tile grid index past one problem counts batch entries
+    const int64_t off = static_cast<int64_t>(split) * P.split_stride;
+    Ab += off;
+    Bb += off;
+    Cp += off;
+  } else {
+    if (P.nsplit > 1) {
+      const int len = ((ke - kb + P.nsplit - 1) / P.nsplit + kTileK - 1) / kTileK * kTileK;
+      const int s0 = kb + split * len;
+      ke = min(ke, s0 + len);
+      kb = s0;
+    }
+    Cp += static_cast<int64_t>(split) * P.split_stride;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -353,6 +364,7 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_MN, OP_MN, EPI_UPDATE)
+  KFAC_GEMM_CASE(OP_MN, OP_K, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_STORE)
   KFAC_GEMM_CASE(OP_K, OP_MN, EPI_SUB)
   KFAC_GEMM_CASE(OP_K, OP_K, EPI_STORE)
@@ -365,7 +377,7 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
 int tiles_for(const GemmProb& p, int bt) {
   const int tm = (p.M + bt - 1) / bt, tn = (p.N + bt - 1) / bt;
   const int per = p.tri == TRI_FULL ? tm * tn : tm * (tm + 1) / 2;
-  return per * std::max(1, p.nsplit);
+  return per * std::max(1, p.nsplit) * std::max<int>(1, p.nbatch);
 }
 
 }  // namespace
@@ -391,6 +403,7 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
   std::vector<GemmProb> ps;
   for (GemmProb p : probs) {
     if (p.nsplit < 1) p.nsplit = 1;
+    if (p.nbatch < 1) p.nbatch = 1;
     p.tiles_m = (p.M + bt - 1) / bt;
     p.tiles_n = (p.N + bt - 1) / bt;
     p.a_vec = (p.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(p.A) % 16) == 0 && (p.kb % 4) == 0;
