@@ -342,11 +342,12 @@ __device__ inline void factor_diag32(float* Ms, float* Zs, int c0, const DMat& M
     // B_jc = B_cj); finished columns keep their multipliers.  X lanes: row
     // operation on the whole row.
     const float t = (xl || c > j) ? v[j] * inv : 0.f;
+    // the whole column first (independent broadcasts), then the updates
+    float col[32];
 #pragma unroll
-    for (int r = j + 1; r < 32; ++r) {
-      const float col = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), j));
-      v[r] = fmaf(-col, t, v[r]);
-    }
+    for (int r = j + 1; r < 32; ++r) col[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), j));
+#pragma unroll
+    for (int r = j + 1; r < 32; ++r) v[r] = fmaf(-col[r], t, v[r]);
   }
   if (bad && lane == 0 && *M.fail == 0) {
     *M.fail = 1;
