@@ -10,6 +10,7 @@
 //             weight-decay / parameter write fused into the second GEMM's
 //             epilogue.
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -657,6 +658,30 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
   return reds.empty() ? KFAC_OK : launch_sym_reduce(reds, st);
 }
 
+// A second stream per device for the Cholesky look-ahead, with its events
+// (default priority; created on first use and kept for the process).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, main_done[2] = {nullptr, nullptr}, side_done[2] = {nullptr, nullptr};
+};
+
+kfac_status_t side_stream(SideStream** out) {
+  static std::mutex mu;
+  static std::vector<SideStream> per_device;
+  int dev = 0;
+  KFAC_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device.size() <= static_cast<size_t>(dev)) per_device.resize(dev + 1);
+  SideStream& S = per_device[dev];
+  if (!S.s) {
+    KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking));
+    hipEvent_t* evs[6] = {&S.fork, &S.join, &S.main_done[0], &S.main_done[1], &S.side_done[0], &S.side_done[1]};
+    for (hipEvent_t* e : evs) KFAC_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  }
+  *out = &S;
+  return KFAC_OK;
+}
+
 kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st) {
   const std::vector<Mat>& mats = P.mats;
   int nblk_max = 0, d_max = 0;
@@ -687,66 +712,127 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
   });
   if (r != KFAC_OK) return r;
-  // blocked right-looking Cholesky
-  for (int k = 0; k < nblk_max; ++k) {
-    {
-      DiagTab D{};
-      D.k = k;
-      D.flags = flags;
-      for (size_t mi = 0; mi <= mats.size(); ++mi) {
-        if (mi == mats.size() || D.n == kMaxDiagMats) {
-          if (D.n > 0) {
-            hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, st, D);
-            KFAC_HIP_TRY(hipGetLastError());
-          }
-          D.n = 0;
-          if (mi == mats.size()) break;
+  // Blocked right-looking Cholesky with a one-column look-ahead.  Step k
+  // factors diagonal block k (chol_diag), forms the panel L_ik = M_ik
+  // Dinv_k^T below it, and applies it to the trailing matrix.  The trailing
+  // update is split: column block k + 1 (U_next) goes on a second stream
+  // together with the next diagonal block and panel, while the rest (columns
+  // k + 2 on, U_rest) runs on the caller's stream, so the latency-bound
+  // diagonal factorisation overlaps the large update.  U_next(k) waits for
+  // U_rest(k - 1) (both subtract into column block k + 1); U_rest(k) waits for
+  // panel k.  Events alternate between two per direction so that each wait
+  // names the right step; the second stream forks from and joins the
+  // caller's stream, which keeps the whole step capturable in a graph.
+  SideStream* side = nullptr;
+  r = side_stream(&side);
+  if (r != KFAC_OK) return r;
+  hipStream_t ss = side->s;
+  auto diag_step = [&](int k) -> kfac_status_t {
+    DiagTab D{};
+    D.k = k;
+    D.flags = flags;
+    for (size_t mi = 0; mi <= mats.size(); ++mi) {
+      if (mi == mats.size() || D.n == kMaxDiagMats) {
+        if (D.n > 0) {
+          hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, ss, D);
+          KFAC_HIP_TRY(hipGetLastError());
         }
-        const Mat& m = mats[mi];
-        if (static_cast<int>(nblk_of(m.d)) <= k) continue;
-        D.m[D.n++] = DMat{m.L, m.Z, m.Dinv, m.fail, m.d, 0};
+        D.n = 0;
+        if (mi == mats.size()) break;
       }
+      const Mat& m = mats[mi];
+      if (static_cast<int>(nblk_of(m.d)) <= k) continue;
+      D.m[D.n++] = DMat{m.L, m.Z, m.Dinv, m.fail, m.d, 0};
     }
-    std::vector<GemmProb> panel, trail;
+    return KFAC_OK;
+  };
+  // panel k, and the update of column block c (c = k + 1) or of everything
+  // from column block k + 2 on (c < 0)
+  auto panel_of = [&](const Mat& m, int k) {
+    const int d = m.d, r1 = (k + 1) * kNb;
+    GemmProb p{};
+    p.A = m.L + static_cast<int64_t>(r1) * d + k * kNb;
+    p.lda = d;
+    p.B = m.Dinv + static_cast<int64_t>(k) * kNb * kNb;
+    p.ldb = kNb;
+    p.C = m.L + static_cast<int64_t>(r1) * d + k * kNb;
+    p.ldc = d;
+    p.M = d - r1;
+    p.N = kNb;
+    p.kb = 0;
+    p.ke = kNb;
+    p.tri = TRI_FULL;
+    p.a_special = p.b_special = -1;
+    p.alpha = 1.f;
+    p.nsplit = 1;
+    gemm_set_tiles(p);
+    return p;
+  };
+  auto update_of = [&](const Mat& m, int k, bool next) {
+    const int d = m.d;
+    const int r0 = (k + (next ? 1 : 2)) * kNb;   // first row (and column) updated
+    GemmProb q{};
+    q.A = m.L + static_cast<int64_t>(r0) * d + k * kNb;   // L_ik, rows r0..
+    q.lda = d;
+    q.B = q.A;                                            // L_jk^T
+    q.ldb = d;
+    q.C = m.L + static_cast<int64_t>(r0) * d + r0;
+    q.ldc = d;
+    q.M = d - r0;
+    q.N = next ? std::min(kNb, d - r0) : d - r0;
+    q.kb = 0;
+    q.ke = kNb;
+    q.tri = next ? TRI_FULL : TRI_LOWER;
+    q.a_special = q.b_special = -1;
+    q.alpha = 1.f;
+    q.nsplit = 1;
+    gemm_set_tiles(q);
+    return q;
+  };
+  // panel k (side stream) for every matrix with a block below k
+  auto panel_step = [&](int k) -> kfac_status_t {
+    std::vector<GemmProb> v;
+    for (const Mat& m : mats)
+      if (static_cast<int>(nblk_of(m.d)) > k + 1) v.push_back(panel_of(m, k));
+    return v.empty() ? KFAC_OK : launch_gemm(v, OP_K, OP_K, EPI_STORE, sc, ss);
+  };
+  KFAC_HIP_TRY(hipEventRecord(side->fork, st));
+  KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
+  r = diag_step(0);
+  if (r != KFAC_OK) return r;
+  r = panel_step(0);
+  if (r != KFAC_OK) return r;
+  KFAC_HIP_TRY(hipEventRecord(side->side_done[0], ss));
+  for (int k = 0; k + 1 < nblk_max; ++k) {
+    // caller's stream: U_rest(k), after panel k
+    std::vector<GemmProb> rest, next;
     for (const Mat& m : mats) {
-      const int d = m.d;
-      if (static_cast<int>(nblk_of(d)) <= k + 1) continue;
-      const int r1 = (k + 1) * kNb;
-      GemmProb p{};
-      // L_ik = M_ik Dinv_k^T for the rows below block k
-      p.A = m.L + static_cast<int64_t>(r1) * d + k * kNb;
-      p.lda = d;
-      p.B = m.Dinv + static_cast<int64_t>(k) * kNb * kNb;
-      p.ldb = kNb;
-      p.C = m.L + static_cast<int64_t>(r1) * d + k * kNb;
-      p.ldc = d;
-      p.M = d - r1;
-      p.N = kNb;
-      p.kb = 0;
-      p.ke = kNb;
-      p.tri = TRI_FULL;
-      p.a_special = p.b_special = -1;
-      p.alpha = 1.f;
-      p.nsplit = 1;
-      gemm_set_tiles(p);
-      panel.push_back(p);
-      // M_ij -= L_ik L_jk^T for k < j <= i
-      GemmProb q = p;
-      q.B = p.A;
-      q.ldb = d;
-      q.C = m.L + static_cast<int64_t>(r1) * d + r1;
-      q.N = d - r1;
-      q.tri = TRI_LOWER;
-      gemm_set_tiles(q);
-      trail.push_back(q);
+      const int nb = static_cast<int>(nblk_of(m.d));
+      if (nb > k + 2) rest.push_back(update_of(m, k, false));
+      if (nb > k + 1) next.push_back(update_of(m, k, true));
     }
-    if (!panel.empty()) {
-      r = launch_gemm(panel, OP_K, OP_K, EPI_STORE, sc, st);
-      if (r != KFAC_OK) return r;
-      r = launch_gemm(trail, OP_K, OP_K, EPI_SUB, sc, st);
+    KFAC_HIP_TRY(hipStreamWaitEvent(st, side->side_done[k & 1], 0));
+    if (!rest.empty()) {
+      r = launch_gemm(rest, OP_K, OP_K, EPI_SUB, sc, st);
       if (r != KFAC_OK) return r;
     }
+    KFAC_HIP_TRY(hipEventRecord(side->main_done[k & 1], st));
+    // second stream: U_next(k) after U_rest(k - 1), then diagonal block and
+    // panel k + 1
+    if (k > 0) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[(k - 1) & 1], 0));
+    if (!next.empty()) {
+      r = launch_gemm(next, OP_K, OP_K, EPI_SUB, sc, ss);
+      if (r != KFAC_OK) return r;
+    }
+    r = diag_step(k + 1);
+    if (r != KFAC_OK) return r;
+    r = panel_step(k + 1);
+    if (r != KFAC_OK) return r;
+    KFAC_HIP_TRY(hipEventRecord(side->side_done[(k + 1) & 1], ss));
   }
+  // join: everything on the second stream before anything after it here
+  KFAC_HIP_TRY(hipEventRecord(side->join, ss));
+  KFAC_HIP_TRY(hipStreamWaitEvent(st, side->join, 0));
   // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
   // inverted diagonal blocks; at level s (128, 256, ...) each pair of
   // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
