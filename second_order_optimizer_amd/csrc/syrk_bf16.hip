@@ -223,16 +223,18 @@ syrk_bf16_kernel(Batch batch) {
 // CDNA4's direct-to-LDS loads and transposing LDS reads.  X is staged
 // row-major, 32 rows per stage, in a 4-stage LDS ring filled by
 // buffer_load_dwordx4 ... lds (no registers; rows past the end read as zero
-// through the buffer's range check), so loads run 3 stages ahead of the
-// MFMAs.  An MFMA operand wants 8 consecutive rows of one column per lane:
+// through the buffer's range check).  Stages go in pairs: one wait and one
+// barrier cover two stages, whose MFMAs run while the next pair loads into
+// the other half of the 4-slot ring; inside a pair the fragments of each
+// 16-row half-step are read while the MFMAs of the previous one run.  An MFMA operand wants 8 consecutive rows of one column per lane:
 // two ds_read_b64_tr_b16 give it from the row-major tile (within 16 lanes,
 // lane i receives column c + i of the 4 rows the group addresses).  Each
 // row's 16-byte chunks are XOR-swizzled by 4 (row mod 4): the 4 rows of a
 // transposing read then fall in distinct 64-byte windows of the 256-byte
 // bank cycle (no bank conflicts, by the SQ_LDS_BANK_CONFLICT counter).  The workgroup
-// barrier carries no memory fence: a fence would wait for the loads still
-// in flight for later stages; each wavefront waits for its own loads of the
-// stage (vmcnt) before the barrier instead.
+// barrier carries no memory fence (a fence is not needed for LDS the
+// loads write directly); each wavefront waits for its own loads of the pair
+// (vmcnt) before the barrier instead.
 
 constexpr int kRBK = 32;                  // rows of X per stage
 constexpr int kNS = 4;                    // stages in the LDS ring
@@ -308,9 +310,12 @@ syrk_bf16_dma_kernel(Batch batch) {
   // loads of stage s into its ring slot: 16 bytes per lane straight into LDS
   // at M0 + 16 lane.  Issued as assembly so that the compiler does not wait
   // for them before every LDS read (it cannot tell ring slots apart); the
-  // per-stage vmcnt waits and the barrier below order them instead.
+  // vmcnt waits and the barrier below order them instead.
+  // stages are consumed in pairs; an odd count gets one more stage past the
+  // end of X, which the range check fills with zeros
+  const int64_t nst2 = (nst + 1) & ~int64_t(1);
   auto issue = [&](int64_t s) {
-    if (s >= nst) return;
+    if (s >= nst2) return;
     const int slot = static_cast<int>(s % kNS);
     const uint32_t so = static_cast<uint32_t>(s) * stage_bytes;
 #pragma unroll
@@ -352,47 +357,67 @@ syrk_bf16_dma_kernel(Batch batch) {
     for (int j = 0; j < 2; ++j) ob[h][j] = tr_off(wn + 32 * j, 16 * h, lane);
   }
 
-  for (int s = 0; s < kNS - 1; ++s) issue(s);
-  for (int64_t s = 0; s < nst; ++s) {
-    // this wavefront's loads of stage s are done once at most the loads of
-    // the stages issued after it remain; the barrier then covers everyone's
-    const int64_t after = (nst - 1 - s) < (kNS - 2) ? (nst - 1 - s) : (kNS - 2);
-    const int pending = static_cast<int>(after) * 2 * nops;
-    if (pending == 0) KFAC_WAIT_VM(0);
-    else if (pending == 2) KFAC_WAIT_VM(2);
-    else if (pending == 4) KFAC_WAIT_VM(4);
-    else KFAC_WAIT_VM(8);
+  // two stages per barrier: stages s, s + 1 (slots s % 4, s % 4 + 1) are
+  // waited for together; the slots of s - 2, s - 1 are then refilled with
+  // s + 2, s + 3
+  issue(0);
+  issue(1);
+  for (int64_t s = 0; s < nst2; s += 2) {
+    KFAC_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
-    issue(s + kNS - 1);   // into the slot stage s - 1 used; every wavefront is past it
-    const int slot = static_cast<int>(s % kNS);
-    const unsigned short* sa = ring[slot][0];
-    const unsigned short* sb = diag ? sa : ring[slot][1];
+    issue(s + 2);
+    issue(s + 3);
+    const int slot0 = static_cast<int>(s & 3);
     if (work) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 fa[4], fb[2];
+      // four half-steps t (stage s + t / 2, k half t % 2); the fragments of
+      // t + 1 are read while the MFMAs of t run
+      auto frags = [&](int t, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+        const unsigned short* sa = ring[slot0 + (t >> 1)][0];
+        const unsigned short* sb = diag ? sa : ring[slot0 + (t >> 1)][1];
+        const int h = t & 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = tr_frag(sa, oa[h][i], oa[h][i] + 4 * kBT);
 #pragma unroll
         for (int j = 0; j < 2; ++j) fb[j] = tr_frag(sb, ob[h][j], ob[h][j] + 4 * kBT);
+      };
+      bf16x8 fa[2][4], fb[2][2];
+      frags(0, fa[0], fb[0]);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int cur = t & 1;
+        if (t < 3) frags(t + 1, fa[cur ^ 1], fb[cur ^ 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        if (t < 3) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+        }
       }
     } else if (colsum) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int t = 0; t < 4; ++t) {
+        const unsigned short* sa = ring[slot0 + (t >> 1)][0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16x8 x = tr_frag(sa, oc[h][i], oc[h][i] + 4 * kBT);
+          const bf16x8 x = tr_frag(sa, oc[t & 1][i], oc[t & 1][i] + 4 * kBT);
           acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, ones, acc[i][0], 0, 0, 0);
         }
       }
     }
-    // every LDS read of this stage has returned before the next barrier, so
-    // the refill issued after it cannot overwrite data still being read
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   }
 
