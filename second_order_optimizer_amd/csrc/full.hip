@@ -22,6 +22,7 @@ namespace kfac {
 namespace {
 
 constexpr int kNb = kTile;   // Cholesky block size = GEMM tile
+constexpr int kOuter = 4;     // Cholesky blocks per outer panel
 
 // ---------------------------------------------------------------------------
 // Split-K SYRK finish, batched over factors: F[i][j] = beta F[i][j] +
@@ -712,17 +713,21 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
   });
   if (r != KFAC_OK) return r;
-  // Blocked right-looking Cholesky with a one-column look-ahead.  Step k
-  // factors diagonal block k (chol_diag), forms the panel L_ik = M_ik
-  // Dinv_k^T below it, and applies it to the trailing matrix.  The trailing
-  // update is split: column block k + 1 (U_next) goes on a second stream
-  // together with the next diagonal block and panel, while the rest (columns
-  // k + 2 on, U_rest) runs on the caller's stream, so the latency-bound
-  // diagonal factorisation overlaps the large update.  U_next(k) waits for
-  // U_rest(k - 1) (both subtract into column block k + 1); U_rest(k) waits for
-  // panel k.  Events alternate between two per direction so that each wait
-  // names the right step; the second stream forks from and joins the
-  // caller's stream, which keeps the whole step capturable in a graph.
+  // Blocked right-looking Cholesky in two levels.  Inner step k factors
+  // diagonal block k (chol_diag) and forms the panel L_ik = M_ik Dinv_k^T
+  // below it.  Blocks are grouped kOuter at a time into outer panels; the
+  // inner steps of an outer panel apply their rank-128 updates only to the
+  // panel's own remaining columns (U_in), and the rest of the trailing matrix
+  // takes the whole outer panel at once, a 512-deep product instead of four
+  // 128-deep ones.  That far update is split: the columns of the next outer
+  // panel (F_next) run on a second stream ahead of that panel's inner steps,
+  // the remainder (F_rest) on the caller's stream beside them, so the
+  // latency-bound inner chain overlaps the large update.  F_next(K) waits for
+  // F_rest(K - 1) (both subtract into outer panel K + 1); F_rest(K) waits for
+  // the last panel of outer panel K.  Events alternate between two per
+  // direction so that each wait names the right step; the second stream forks
+  // from and joins the caller's stream, which keeps the whole step
+  // capturable in a graph.
   SideStream* side = nullptr;
   r = side_stream(&side);
   if (r != KFAC_OK) return r;
@@ -768,21 +773,23 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     gemm_set_tiles(p);
     return p;
   };
-  auto update_of = [&](const Mat& m, int k, bool next) {
+  // lower part of the trailing matrix from row and column r0 on, ncols
+  // columns wide, minus the product of L's columns c .. c + depth with their
+  // own transpose (rows r0..)
+  auto update_of = [&](const Mat& m, int r0, int ncols, int c, int depth, uint8_t tri) {
     const int d = m.d;
-    const int r0 = (k + (next ? 1 : 2)) * kNb;   // first row (and column) updated
     GemmProb q{};
-    q.A = m.L + static_cast<int64_t>(r0) * d + k * kNb;   // L_ik, rows r0..
+    q.A = m.L + static_cast<int64_t>(r0) * d + c;   // L_ik, rows r0..
     q.lda = d;
-    q.B = q.A;                                            // L_jk^T
+    q.B = q.A;                                      // L_jk^T
     q.ldb = d;
     q.C = m.L + static_cast<int64_t>(r0) * d + r0;
     q.ldc = d;
     q.M = d - r0;
-    q.N = next ? std::min(kNb, d - r0) : d - r0;
+    q.N = ncols;
     q.kb = 0;
-    q.ke = kNb;
-    q.tri = next ? TRI_FULL : TRI_LOWER;
+    q.ke = depth;
+    q.tri = tri;
     q.a_special = q.b_special = -1;
     q.alpha = 1.f;
     q.nsplit = 1;
@@ -798,37 +805,55 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   };
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
   KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
-  r = diag_step(0);
-  if (r != KFAC_OK) return r;
-  r = panel_step(0);
-  if (r != KFAC_OK) return r;
-  KFAC_HIP_TRY(hipEventRecord(side->side_done[0], ss));
-  for (int k = 0; k + 1 < nblk_max; ++k) {
-    // caller's stream: U_rest(k), after panel k
-    std::vector<GemmProb> rest, next;
-    for (const Mat& m : mats) {
-      const int nb = static_cast<int>(nblk_of(m.d));
-      if (nb > k + 2) rest.push_back(update_of(m, k, false));
-      if (nb > k + 1) next.push_back(update_of(m, k, true));
+  const int nouter = (nblk_max + kOuter - 1) / kOuter;
+  for (int K = 0; K < nouter; ++K) {
+    const int k0 = K * kOuter, k1 = k0 + kOuter;   // blocks of outer panel K
+    // second stream: F_next(K - 1) after F_rest(K - 2), then the inner steps
+    if (K > 0) {
+      if (K > 1) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[K & 1], 0));
+      std::vector<GemmProb> fn;
+      for (const Mat& m : mats)
+        if (static_cast<int>(nblk_of(m.d)) > k0) {
+          const int r0 = k0 * kNb;
+          fn.push_back(update_of(m, r0, std::min(k1 * kNb, m.d) - r0, (k0 - kOuter) * kNb, kOuter * kNb, TRI_FULL));
+        }
+      if (!fn.empty()) {
+        r = launch_gemm(fn, OP_K, OP_K, EPI_SUB, sc, ss);
+        if (r != KFAC_OK) return r;
+      }
     }
-    KFAC_HIP_TRY(hipStreamWaitEvent(st, side->side_done[k & 1], 0));
-    if (!rest.empty()) {
-      r = launch_gemm(rest, OP_K, OP_K, EPI_SUB, sc, st);
+    for (int k = k0; k < k1 && k < nblk_max; ++k) {
+      r = diag_step(k);
+      if (r != KFAC_OK) return r;
+      r = panel_step(k);
+      if (r != KFAC_OK) return r;
+      if (k + 1 < k1) {
+        std::vector<GemmProb> ui;
+        for (const Mat& m : mats)
+          if (static_cast<int>(nblk_of(m.d)) > k + 1) {
+            const int r0 = (k + 1) * kNb;
+            ui.push_back(update_of(m, r0, std::min(k1 * kNb, m.d) - r0, k * kNb, kNb, TRI_FULL));
+          }
+        if (!ui.empty()) {
+          r = launch_gemm(ui, OP_K, OP_K, EPI_SUB, sc, ss);
+          if (r != KFAC_OK) return r;
+        }
+      }
+    }
+    KFAC_HIP_TRY(hipEventRecord(side->side_done[K & 1], ss));
+    // caller's stream: F_rest(K), after the last panel of outer panel K
+    std::vector<GemmProb> fr;
+    for (const Mat& m : mats)
+      if (static_cast<int>(nblk_of(m.d)) > k1 + kOuter) {
+        const int r0 = (k1 + kOuter) * kNb;
+        fr.push_back(update_of(m, r0, m.d - r0, k0 * kNb, kOuter * kNb, TRI_LOWER));
+      }
+    KFAC_HIP_TRY(hipStreamWaitEvent(st, side->side_done[K & 1], 0));
+    if (!fr.empty()) {
+      r = launch_gemm(fr, OP_K, OP_K, EPI_SUB, sc, st);
       if (r != KFAC_OK) return r;
     }
-    KFAC_HIP_TRY(hipEventRecord(side->main_done[k & 1], st));
-    // second stream: U_next(k) after U_rest(k - 1), then diagonal block and
-    // panel k + 1
-    if (k > 0) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[(k - 1) & 1], 0));
-    if (!next.empty()) {
-      r = launch_gemm(next, OP_K, OP_K, EPI_SUB, sc, ss);
-      if (r != KFAC_OK) return r;
-    }
-    r = diag_step(k + 1);
-    if (r != KFAC_OK) return r;
-    r = panel_step(k + 1);
-    if (r != KFAC_OK) return r;
-    KFAC_HIP_TRY(hipEventRecord(side->side_done[(k + 1) & 1], ss));
+    KFAC_HIP_TRY(hipEventRecord(side->main_done[K & 1], st));
   }
   // join: everything on the second stream before anything after it here
   KFAC_HIP_TRY(hipEventRecord(side->join, ss));
