@@ -465,7 +465,14 @@ struct FullPlan {
   std::vector<float*> T;         // per layer, d_out x d_a
   std::vector<float*> xcol;      // per layer and factor: fp32 convolution tensor as [rows, width], or null
   std::vector<int> xcol_ld;      // their row pitch (floats)
-  std::vector<Mat> mats;         // inverse work per factor
+  std::vector<Mat> mats;         // inverse work per factor (2 layer + which)
+  // runs of equal-size factors whose work areas sit at a constant stride
+  struct Group {
+    int first;                   // index into mats of the lowest address
+    int count;
+    int64_t stride;              // floats between neighbouring work areas
+  };
+  std::vector<Group> groups;
 };
 
 size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
@@ -517,20 +524,39 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
       P.xcol.push_back(col ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.rows) * ld * 4)) : nullptr);
     }
   }
+  // Cholesky work areas: one contiguous chunk per factor (L, Z, Dinv, fail),
+  // factors of equal size side by side, so that the chunks of one size lie
+  // at a constant stride and every size is one batched GEMM problem
+  P.mats.resize(2 * static_cast<size_t>(n));
+  std::vector<int> order(P.mats.size());
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
     for (int which = 0; which < 2; ++which) {
-      const int d = which == 0 ? g.d_a : g.d_out;
-      Mat m{};
+      Mat& m = P.mats[2 * li + which];
       m.F = which == 0 ? layers[li].A : layers[li].G;
       m.Finv = which == 0 ? layers[li].A_inv : layers[li].G_inv;
-      m.d = d;
-      m.L = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
-      m.Z = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
-      m.Dinv = reinterpret_cast<float*>(carve(nblk_of(d) * kNb * kNb * 4));
-      m.fail = reinterpret_cast<int32_t*>(carve(4));
-      P.mats.push_back(m);
+      m.d = which == 0 ? g.d_a : g.d_out;
+      order[2 * li + which] = 2 * li + which;
     }
+  }
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return P.mats[a].d > P.mats[b].d; });
+  std::vector<size_t> start(order.size());
+  for (size_t i = 0; i < order.size(); ++i) {
+    Mat& m = P.mats[order[i]];
+    const int d = m.d;
+    start[i] = off;
+    m.L = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
+    m.Z = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
+    m.Dinv = reinterpret_cast<float*>(carve(nblk_of(d) * kNb * kNb * 4));
+    m.fail = reinterpret_cast<int32_t*>(carve(4));
+  }
+  for (size_t i = 0; i < order.size();) {
+    size_t j = i + 1;
+    while (j < order.size() && P.mats[order[j]].d == P.mats[order[i]].d) ++j;
+    FullPlan::Group gr{order[i], static_cast<int>(j - i), 0};
+    if (j - i > 1) gr.stride = static_cast<int64_t>((start[i + 1] - start[i]) / 4);
+    P.groups.push_back(gr);
+    i = j;
   }
   (void)phases;
   (void)refresh;
@@ -796,11 +822,20 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     gemm_set_tiles(q);
     return q;
   };
+  // one problem for a run of equal-size factors (their work areas lie at a
+  // constant stride)
+  auto batched = [](GemmProb p, const FullPlan::Group& g) {
+    if (g.count > 1) {
+      p.nbatch = static_cast<int16_t>(g.count);
+      p.split_stride = g.stride;
+    }
+    return p;
+  };
   // panel k (side stream) for every matrix with a block below k
   auto panel_step = [&](int k) -> kfac_status_t {
     std::vector<GemmProb> v;
-    for (const Mat& m : mats)
-      if (static_cast<int>(nblk_of(m.d)) > k + 1) v.push_back(panel_of(m, k));
+    for (const FullPlan::Group& g : P.groups)
+      if (static_cast<int>(nblk_of(mats[g.first].d)) > k + 1) v.push_back(batched(panel_of(mats[g.first], k), g));
     return v.empty() ? KFAC_OK : launch_gemm(v, OP_K, OP_K, EPI_STORE, sc, ss);
   };
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
@@ -812,11 +847,14 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     if (K > 0) {
       if (K > 1) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[K & 1], 0));
       std::vector<GemmProb> fn;
-      for (const Mat& m : mats)
+      for (const FullPlan::Group& g : P.groups) {
+        const Mat& m = mats[g.first];
         if (static_cast<int>(nblk_of(m.d)) > k0) {
           const int r0 = k0 * kNb;
-          fn.push_back(update_of(m, r0, std::min(k1 * kNb, m.d) - r0, (k0 - kOuter) * kNb, kOuter * kNb, TRI_FULL));
+          fn.push_back(batched(
+              update_of(m, r0, std::min(k1 * kNb, m.d) - r0, (k0 - kOuter) * kNb, kOuter * kNb, TRI_FULL), g));
         }
+      }
       if (!fn.empty()) {
         r = launch_gemm(fn, OP_K, OP_K, EPI_SUB, sc, ss);
         if (r != KFAC_OK) return r;
@@ -829,11 +867,13 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
       if (k + 1 < k1) {
         std::vector<GemmProb> ui;
-        for (const Mat& m : mats)
+        for (const FullPlan::Group& g : P.groups) {
+          const Mat& m = mats[g.first];
           if (static_cast<int>(nblk_of(m.d)) > k + 1) {
             const int r0 = (k + 1) * kNb;
-            ui.push_back(update_of(m, r0, std::min(k1 * kNb, m.d) - r0, k * kNb, kNb, TRI_FULL));
+            ui.push_back(batched(update_of(m, r0, std::min(k1 * kNb, m.d) - r0, k * kNb, kNb, TRI_FULL), g));
           }
+        }
         if (!ui.empty()) {
           r = launch_gemm(ui, OP_K, OP_K, EPI_SUB, sc, ss);
           if (r != KFAC_OK) return r;
@@ -843,11 +883,13 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     KFAC_HIP_TRY(hipEventRecord(side->side_done[K & 1], ss));
     // caller's stream: F_rest(K), after the last panel of outer panel K
     std::vector<GemmProb> fr;
-    for (const Mat& m : mats)
+    for (const FullPlan::Group& g : P.groups) {
+      const Mat& m = mats[g.first];
       if (static_cast<int>(nblk_of(m.d)) > k1 + kOuter) {
         const int r0 = (k1 + kOuter) * kNb;
-        fr.push_back(update_of(m, r0, m.d - r0, k0 * kNb, kOuter * kNb, TRI_LOWER));
+        fr.push_back(batched(update_of(m, r0, m.d - r0, k0 * kNb, kOuter * kNb, TRI_LOWER), g));
       }
+    }
     KFAC_HIP_TRY(hipStreamWaitEvent(st, side->side_done[K & 1], 0));
     if (!fr.empty()) {
       r = launch_gemm(fr, OP_K, OP_K, EPI_SUB, sc, st);
@@ -936,7 +978,8 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   const int rows_per_pass = by_rows ? kLauRows : d_max;
   for (int k0 = 0; k0 < d_max; k0 += rows_per_pass) {
     std::vector<GemmProb> lau;
-    for (const Mat& m : mats) {
+    for (const FullPlan::Group& g : P.groups) {
+      const Mat& m = mats[g.first];
       if (m.d <= k0) continue;
       GemmProb p{};
       p.A = m.Z;
@@ -953,7 +996,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       p.nsplit = 1;
       p.alpha = k0 == 0 ? 1.f : -1.f;
       gemm_set_tiles(p);
-      lau.push_back(p);
+      lau.push_back(batched(p, g));
     }
     r = launch_gemm(lau, OP_MN, OP_MN, k0 == 0 ? EPI_STORE : EPI_SUB, sc, st, by_rows ? TILES_SMALL : TILES_AUTO);
     if (r != KFAC_OK) return r;
