@@ -422,23 +422,46 @@ syrk_bf16_dma_kernel(Batch batch) {
   }
 
   // accumulator r of block (i, j): row i0 + wm + 32 i + 8 (r/4) + 4 (lane/32) + r%4,
-  // column j0 + wn + 32 j + lane%32
+  // column j0 + wn + 32 j + lane%32.  Per 32 x 32 block: the 16 reads of F
+  // issue together, the EMA result goes to the upper triangle row-wise and,
+  // transposed through a 32 x 33 LDS staging tile of this wavefront (the ring
+  // is idle once every wavefront has left the loop), to the lower triangle
+  // in 128-byte row pieces.
   float* F = P.F;
   const int ldf = P.ldf;
+  __syncthreads();
+  float* stg = reinterpret_cast<float*>(&ring[0][0][0]) + wid * (32 * 33);
   if (work) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int col = j0 + wn + 32 * j + (lane & 31);
+        const int r0 = i0 + wm + 32 * i, c0 = j0 + wn + 32 * j;
+        if (r0 > c0 + 31 || r0 >= width || c0 >= width) continue;   // no upper element in the block
+        const int col = c0 + (lane & 31);
+        // unconditional loads (an element outside the upper triangle reads the
+        // block's first element, which is inside it) keep them in one batch
+        float o[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = i0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row >= width || col >= width || row > col) continue;
-          const int64_t idx = static_cast<int64_t>(row) * ldf + col;
-          const float o = P.beta * F[idx] + P.alpha * acc[i][j][r];
-          F[idx] = o;
-          if (row != col) F[static_cast<int64_t>(col) * ldf + row] = o;
+          const int row = r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const bool in = row < width && col < width && row <= col;
+          o[r] = F[in ? static_cast<int64_t>(row) * ldf + col : static_cast<int64_t>(r0) * ldf + c0];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = r0 + rr;
+          const bool in = row < width && col < width && row <= col;
+          const float v = P.beta * o[r] + P.alpha * acc[i][j][r];
+          if (in) F[static_cast<int64_t>(row) * ldf + col] = v;
+          stg[(lane & 31) * 33 + rr] = v;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int cc = 2 * q + (lane >> 5), rr = lane & 31;
+          const int row = r0 + rr, mcol = c0 + cc;
+          if (row < mcol && mcol < width) F[static_cast<int64_t>(mcol) * ldf + row] = stg[cc * 33 + rr];
         }
       }
     }
