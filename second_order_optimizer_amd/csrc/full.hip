@@ -471,6 +471,7 @@ struct FullPlan {
     int first;                   // index into mats of the lowest address
     int count;
     int64_t stride;              // floats between neighbouring work areas
+    std::vector<int> members;    // indices into mats, by address
   };
   std::vector<Group> groups;
 };
@@ -553,8 +554,9 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   for (size_t i = 0; i < order.size();) {
     size_t j = i + 1;
     while (j < order.size() && P.mats[order[j]].d == P.mats[order[i]].d) ++j;
-    FullPlan::Group gr{order[i], static_cast<int>(j - i), 0};
+    FullPlan::Group gr{order[i], static_cast<int>(j - i), 0, {}};
     if (j - i > 1) gr.stride = static_cast<int64_t>((start[i + 1] - start[i]) / 4);
+    for (size_t q = i; q < j; ++q) gr.members.push_back(order[q]);
     P.groups.push_back(gr);
     i = j;
   }
@@ -688,8 +690,10 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
 // A second stream per device for the Cholesky look-ahead, with its events
 // (default priority; created on first use and kept for the process).
 struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, main_done[2] = {nullptr, nullptr}, side_done[2] = {nullptr, nullptr};
+  hipStream_t s = nullptr;   // Cholesky inner chain
+  hipStream_t f = nullptr;   // inverse assembly of factors whose Cholesky is complete
+  hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, main_done[2] = {nullptr, nullptr},
+             side_done[2] = {nullptr, nullptr};
 };
 
 kfac_status_t side_stream(SideStream** out) {
@@ -702,7 +706,9 @@ kfac_status_t side_stream(SideStream** out) {
   SideStream& S = per_device[dev];
   if (!S.s) {
     KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking));
-    hipEvent_t* evs[6] = {&S.fork, &S.join, &S.main_done[0], &S.main_done[1], &S.side_done[0], &S.side_done[1]};
+    KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.f, hipStreamNonBlocking));
+    hipEvent_t* evs[7] = {&S.fork,         &S.join,         &S.fjoin,       &S.main_done[0],
+                          &S.main_done[1], &S.side_done[0], &S.side_done[1]};
     for (hipEvent_t* e : evs) KFAC_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
   }
   *out = &S;
@@ -838,8 +844,137 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (static_cast<int>(nblk_of(mats[g.first].d)) > k + 1) v.push_back(batched(panel_of(mats[g.first], k), g));
     return v.empty() ? KFAC_OK : launch_gemm(v, OP_K, OP_K, EPI_STORE, sc, ss);
   };
+  // The triangular inverse, Z^T Z and the output of the factors in `gs`
+  // (complete Cholesky factors), on stream fs.
+  auto finish = [&](const std::vector<const FullPlan::Group*>& gs, hipStream_t fs) -> kfac_status_t {
+    std::vector<Mat> ms;
+    int dm = 0;
+    for (const FullPlan::Group* g : gs)
+      for (int mi : g->members) {
+        ms.push_back(mats[mi]);
+        dm = std::max(dm, mats[mi].d);
+      }
+    // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
+    // inverted diagonal blocks; at level s (128, 256, ...) each pair of
+    // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
+    // (r0, r0) with r0 = c0 + s, gives the block between them:
+    //   Z21 = -Z22 (L21 Z11)   (L21 = rows r0.., columns c0.. of L).
+    // T^T = Z11^T L21^T is staged in L's strict upper triangle at (c0, r0),
+    // which no later step reads (the Z^T Z pass overwrites L).  Z11 is lower
+    // triangular, so a tile of T^T needs rows k >= its first row of Z11; Z22
+    // is lower triangular, so a tile of Z21 needs k up to its last row.  The
+    // full-size pairs of one matrix and level form one strided problem (all
+    // three operands move by 2 s (d + 1) floats from pair to pair), the last,
+    // shorter pair another; every matrix advances one level per two launches.
+    for (int s = kNb; s < dm; s *= 2) {
+      std::vector<GemmProb> g1, g2;
+      for (const Mat& m : ms) {
+        const int d = m.d;
+        if (d <= s) continue;
+        const int npairs = (d - s + 2 * s - 1) / (2 * s);       // pairs with r0 = 2 p s + s < d
+        const int nfull = (d - 2 * s) >= 0 ? (d - 2 * s) / (2 * s) + 1 : 0;   // pairs with r0 + s <= d
+        for (int part = 0; part < 2; ++part) {
+          const int p0 = part == 0 ? 0 : nfull;
+          const int cnt = part == 0 ? nfull : npairs - nfull;
+          if (cnt <= 0) continue;
+          const int c0 = 2 * p0 * s, r0 = c0 + s;
+          const int m2 = part == 0 ? s : d - r0;
+          GemmProb p{};
+          p.A = m.Z + static_cast<int64_t>(c0) * d + c0;        // Z11, read as A[i][k] = Z11[k][i]
+          p.lda = d;
+          p.B = m.L + static_cast<int64_t>(r0) * d + c0;        // L21, read as B[k][j] = L21[j][k]
+          p.ldb = d;
+          p.C = m.L + static_cast<int64_t>(c0) * d + r0;        // T^T (s x m2) in L's upper triangle
+          p.ldc = d;
+          p.M = s;
+          p.N = m2;
+          p.kb = 0;
+          p.ke = s;
+          p.tri = TRI_FULL;
+          p.krange = KR_FROM_ROW;
+          p.a_special = p.b_special = -1;
+          p.alpha = 1.f;
+          p.nsplit = 1;
+          p.nbatch = static_cast<int16_t>(cnt);
+          p.split_stride = static_cast<int64_t>(2 * s) * (d + 1);
+          gemm_set_tiles(p);
+          g1.push_back(p);
+          GemmProb q = p;
+          q.A = m.Z + static_cast<int64_t>(r0) * d + r0;        // Z22
+          q.B = m.L + static_cast<int64_t>(c0) * d + r0;        // T[k][j] = T^T[j][k]
+          q.C = m.Z + static_cast<int64_t>(r0) * d + c0;        // Z21
+          q.M = m2;
+          q.N = s;
+          q.ke = m2;
+          q.krange = KR_TO_ROW;
+          q.alpha = -1.f;
+          gemm_set_tiles(q);
+          g2.push_back(q);
+        }
+      }
+      if (g1.empty()) break;
+      kfac_status_t r = launch_gemm(g1, OP_MN, OP_K, EPI_STORE, sc, fs);
+      if (r != KFAC_OK) return r;
+      r = launch_gemm(g2, OP_K, OP_K, EPI_STORE, sc, fs);
+      if (r != KFAC_OK) return r;
+    }
+    // inverse = Z^T Z.  Z is lower triangular, so element (i, j) sums over
+    // rows k >= max(i, j); the product goes into L (free once Z is complete;
+    // upper tiles only) and the reduce writes it, mirrored, into the inverse of
+    // every matrix that factored.  The top-left tile of the largest factor sums
+    // all of its d_max rows; when that one workgroup would take a large share
+    // of the whole product (total d^3 / 3 below 2^26 d_max flops: few large
+    // factors), the rows are taken kLauRows at a time (the first pass stores,
+    // later passes add) so that no workgroup runs the whole height.
+    double lau_flops = 0.0;
+    for (const Mat& m : ms) lau_flops += static_cast<double>(m.d) * m.d * m.d / 3.0;
+    const bool by_rows = lau_flops < 67108864.0 * dm;
+    const int rows_per_pass = by_rows ? kLauRows : dm;
+    for (int k0 = 0; k0 < dm; k0 += rows_per_pass) {
+      std::vector<GemmProb> lau;
+      for (const FullPlan::Group* gp : gs) {
+        const FullPlan::Group& g = *gp;
+        const Mat& m = mats[g.first];
+        if (m.d <= k0) continue;
+        GemmProb p{};
+        p.A = m.Z;
+        p.B = m.Z;
+        p.lda = p.ldb = m.d;
+        p.C = m.L;
+        p.ldc = m.d;
+        p.M = p.N = m.d;
+        p.kb = k0;
+        p.ke = std::min(m.d, k0 + rows_per_pass);
+        p.tri = TRI_UPPER;
+        p.krange = KR_FROM_DIAG;
+        p.a_special = p.b_special = -1;
+        p.nsplit = 1;
+        p.alpha = k0 == 0 ? 1.f : -1.f;
+        gemm_set_tiles(p);
+        lau.push_back(batched(p, g));
+      }
+      kfac_status_t r =
+          launch_gemm(lau, OP_MN, OP_MN, k0 == 0 ? EPI_STORE : EPI_SUB, sc, fs, by_rows ? TILES_SMALL : TILES_AUTO);
+      if (r != KFAC_OK) return r;
+    }
+    std::vector<SymRedItem> out;
+    for (const Mat& m : ms) {
+      SymRedItem it{};
+      it.part = m.L;
+      it.F = m.Finv;
+      it.fail = m.fail;
+      it.d = m.d;
+      it.nsplit = 1;
+      it.alpha = 1.f;
+      it.beta = 0.f;
+      out.push_back(it);
+    }
+    return launch_sym_reduce(out, fs);
+  };
+  hipStream_t fs = side->f;
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
   KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
+  KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->fork, 0));
   const int nouter = (nblk_max + kOuter - 1) / kOuter;
   for (int K = 0; K < nouter; ++K) {
     const int k0 = K * kOuter, k1 = k0 + kOuter;   // blocks of outer panel K
@@ -896,124 +1031,23 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
     }
     KFAC_HIP_TRY(hipEventRecord(side->main_done[K & 1], st));
+    // factors whose last block is in outer panel K are complete: their
+    // inverse is assembled on a third stream beside the remaining steps
+    std::vector<const FullPlan::Group*> done;
+    for (const FullPlan::Group& g : P.groups)
+      if ((static_cast<int>(nblk_of(mats[g.first].d)) - 1) / kOuter == K) done.push_back(&g);
+    if (!done.empty()) {
+      KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->side_done[K & 1], 0));
+      r = finish(done, fs);
+      if (r != KFAC_OK) return r;
+    }
   }
   // join: everything on the second stream before anything after it here
   KFAC_HIP_TRY(hipEventRecord(side->join, ss));
   KFAC_HIP_TRY(hipStreamWaitEvent(st, side->join, 0));
-  // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
-  // inverted diagonal blocks; at level s (128, 256, ...) each pair of
-  // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
-  // (r0, r0) with r0 = c0 + s, gives the block between them:
-  //   Z21 = -Z22 (L21 Z11)   (L21 = rows r0.., columns c0.. of L).
-  // T^T = Z11^T L21^T is staged in L's strict upper triangle at (c0, r0),
-  // which no later step reads (the Z^T Z pass overwrites L).  Z11 is lower
-  // triangular, so a tile of T^T needs rows k >= its first row of Z11; Z22
-  // is lower triangular, so a tile of Z21 needs k up to its last row.  The
-  // full-size pairs of one matrix and level form one strided problem (all
-  // three operands move by 2 s (d + 1) floats from pair to pair), the last,
-  // shorter pair another; every matrix advances one level per two launches.
-  for (int s = kNb; s < d_max; s *= 2) {
-    std::vector<GemmProb> g1, g2;
-    for (const Mat& m : mats) {
-      const int d = m.d;
-      if (d <= s) continue;
-      const int npairs = (d - s + 2 * s - 1) / (2 * s);       // pairs with r0 = 2 p s + s < d
-      const int nfull = (d - 2 * s) >= 0 ? (d - 2 * s) / (2 * s) + 1 : 0;   // pairs with r0 + s <= d
-      for (int part = 0; part < 2; ++part) {
-        const int p0 = part == 0 ? 0 : nfull;
-        const int cnt = part == 0 ? nfull : npairs - nfull;
-        if (cnt <= 0) continue;
-        const int c0 = 2 * p0 * s, r0 = c0 + s;
-        const int m2 = part == 0 ? s : d - r0;
-        GemmProb p{};
-        p.A = m.Z + static_cast<int64_t>(c0) * d + c0;        // Z11, read as A[i][k] = Z11[k][i]
-        p.lda = d;
-        p.B = m.L + static_cast<int64_t>(r0) * d + c0;        // L21, read as B[k][j] = L21[j][k]
-        p.ldb = d;
-        p.C = m.L + static_cast<int64_t>(c0) * d + r0;        // T^T (s x m2) in L's upper triangle
-        p.ldc = d;
-        p.M = s;
-        p.N = m2;
-        p.kb = 0;
-        p.ke = s;
-        p.tri = TRI_FULL;
-        p.krange = KR_FROM_ROW;
-        p.a_special = p.b_special = -1;
-        p.alpha = 1.f;
-        p.nsplit = 1;
-        p.nbatch = static_cast<int16_t>(cnt);
-        p.split_stride = static_cast<int64_t>(2 * s) * (d + 1);
-        gemm_set_tiles(p);
-        g1.push_back(p);
-        GemmProb q = p;
-        q.A = m.Z + static_cast<int64_t>(r0) * d + r0;        // Z22
-        q.B = m.L + static_cast<int64_t>(c0) * d + r0;        // T[k][j] = T^T[j][k]
-        q.C = m.Z + static_cast<int64_t>(r0) * d + c0;        // Z21
-        q.M = m2;
-        q.N = s;
-        q.ke = m2;
-        q.krange = KR_TO_ROW;
-        q.alpha = -1.f;
-        gemm_set_tiles(q);
-        g2.push_back(q);
-      }
-    }
-    if (g1.empty()) break;
-    r = launch_gemm(g1, OP_MN, OP_K, EPI_STORE, sc, st);
-    if (r != KFAC_OK) return r;
-    r = launch_gemm(g2, OP_K, OP_K, EPI_STORE, sc, st);
-    if (r != KFAC_OK) return r;
-  }
-  // inverse = Z^T Z.  Z is lower triangular, so element (i, j) sums over
-  // rows k >= max(i, j); the product goes into L (free once Z is complete;
-  // upper tiles only) and the reduce writes it, mirrored, into the inverse of
-  // every matrix that factored.  The top-left tile of the largest factor sums
-  // all of its d_max rows; when that one workgroup would take a large share
-  // of the whole product (total d^3 / 3 below 2^26 d_max flops: few large
-  // factors), the rows are taken kLauRows at a time (the first pass stores,
-  // later passes add) so that no workgroup runs the whole height.
-  double lau_flops = 0.0;
-  for (const Mat& m : mats) lau_flops += static_cast<double>(m.d) * m.d * m.d / 3.0;
-  const bool by_rows = lau_flops < 67108864.0 * d_max;
-  const int rows_per_pass = by_rows ? kLauRows : d_max;
-  for (int k0 = 0; k0 < d_max; k0 += rows_per_pass) {
-    std::vector<GemmProb> lau;
-    for (const FullPlan::Group& g : P.groups) {
-      const Mat& m = mats[g.first];
-      if (m.d <= k0) continue;
-      GemmProb p{};
-      p.A = m.Z;
-      p.B = m.Z;
-      p.lda = p.ldb = m.d;
-      p.C = m.L;
-      p.ldc = m.d;
-      p.M = p.N = m.d;
-      p.kb = k0;
-      p.ke = std::min(m.d, k0 + rows_per_pass);
-      p.tri = TRI_UPPER;
-      p.krange = KR_FROM_DIAG;
-      p.a_special = p.b_special = -1;
-      p.nsplit = 1;
-      p.alpha = k0 == 0 ? 1.f : -1.f;
-      gemm_set_tiles(p);
-      lau.push_back(batched(p, g));
-    }
-    r = launch_gemm(lau, OP_MN, OP_MN, k0 == 0 ? EPI_STORE : EPI_SUB, sc, st, by_rows ? TILES_SMALL : TILES_AUTO);
-    if (r != KFAC_OK) return r;
-  }
-  std::vector<SymRedItem> out;
-  for (const Mat& m : mats) {
-    SymRedItem it{};
-    it.part = m.L;
-    it.F = m.Finv;
-    it.fail = m.fail;
-    it.d = m.d;
-    it.nsplit = 1;
-    it.alpha = 1.f;
-    it.beta = 0.f;
-    out.push_back(it);
-  }
-  return launch_sym_reduce(out, st);
+  KFAC_HIP_TRY(hipEventRecord(side->fjoin, fs));
+  KFAC_HIP_TRY(hipStreamWaitEvent(st, side->fjoin, 0));
+  return KFAC_OK;
 }
 
 kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
