@@ -9,7 +9,6 @@
 namespace kfac {
 
 constexpr int kTile = 128;     // output tile (both dimensions)
-constexpr int kTileK = 16;     // K step staged through LDS
 constexpr int kMaxGemmProbs = 27;   // problem table of one launch (kernel arguments stay within 4 KB)
 
 // Operand layouts.  For A (M x K): OP_MN stores element (i, k) at

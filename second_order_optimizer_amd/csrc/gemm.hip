@@ -37,18 +37,25 @@ __device__ inline void static_for(F&& f) {
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <bool BIG>
+// K depth of one LDS stage: 32 (fewer barriers per MFMA), except for the
+// factor SYRK, whose 128 x 128 tiles keep more workgroups per CU with 16
+// (both measured).
+constexpr int kTileKDeep = 32;
+constexpr int kTileKSyrk = 16;
+
+template <bool BIG, int TK>
 struct Cfg {
+  static constexpr int kTK = TK;
   static constexpr int kThreads = BIG ? 512 : 256;
   static constexpr int kBT = BIG ? 256 : 128;          // output tile
   static constexpr int kRow = kBT + kLdsPad;           // MN operand: LDS row of one k (floats)
-  static constexpr int kKRow = kTileK + 1;             // K operand: LDS row of one m (odd: conflict-free reads)
-  static constexpr int kSlab = (kTileK * kRow > kBT * kKRow) ? kTileK * kRow : kBT * kKRow;
+  static constexpr int kKRow = TK + 1;             // K operand: LDS row of one m (odd: conflict-free reads)
+  static constexpr int kSlab = (TK * kRow > kBT * kKRow) ? TK * kRow : kBT * kKRow;
   static constexpr int kWavesN = BIG ? 4 : 2;
   static constexpr int kWM = BIG ? 128 : 64;           // wavefront tile rows
   static constexpr int kWN = 64;                       // wavefront tile cols
   static constexpr int kBI = kWM / 32, kBJ = kWN / 32; // MFMA blocks per wavefront
-  static constexpr int kItems = kTileK * kBT / 4 / kThreads;   // float4 groups per thread per operand
+  static constexpr int kItems = TK * kBT / 4 / kThreads;   // float4 groups per thread per operand
 };
 
 // LDS layout of an operand mode: [k][m] rows for i-contiguous operands,
@@ -71,13 +78,17 @@ __device__ inline int find_prob(const GemmBatch& b, int blk) {
   return lo;
 }
 
-// This thread's share of a 16 x BT operand slab (kItems groups of 4 floats).
+// registers of one thread's share of a slab
+template <bool BIG, int TK>
+using SlabRegs = float[Cfg<BIG, TK>::kItems * 4];
+
+// This thread's share of a TK x BT operand slab (kItems groups of 4 floats).
 // MN layout: group g covers row kk = g / (BT/4), columns 4 (g % (BT/4)) .. +3.
-// K layout : group g covers column mm = g / 4, k = 4 (g % 4) .. +3.
-template <bool BIG, int MODE, bool EXTRA>
-__device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* __restrict__ base, int ld, int m0,
-                                 int mlim, int k0, int klim, int special, const float* __restrict__ extra, bool vec) {
-  using C = Cfg<BIG>;
+// K layout : group g covers column mm = g / (TK/4), k = 4 (g % (TK/4)) .. +3.
+template <bool BIG, int TK, int MODE, bool EXTRA>
+__device__ inline void load_slab(SlabRegs<BIG, TK>& r, const float* __restrict__ base, int ld, int m0, int mlim,
+                                  int k0, int klim, int special, const float* __restrict__ extra, bool vec) {
+  using C = Cfg<BIG, TK>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
     const int g = threadIdx.x + h * C::kThreads;
@@ -101,8 +112,8 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
         r[4 * h + q] = v;
       }
     } else {
-      const int m = m0 + g / 4;
-      const int k = k0 + (g % 4) * 4;
+      const int m = m0 + g / (TK / 4);
+      const int k = k0 + (g % (TK / 4)) * 4;
       const bool min_ = m < mlim;
       const float* p = base + static_cast<int64_t>(m) * ld + k;
       if (vec && min_ && k + 3 < klim && (!EXTRA || special < k || special > k + 3)) {
@@ -123,9 +134,9 @@ __device__ inline void load_slab(float (&r)[Cfg<BIG>::kItems * 4], const float* 
   }
 }
 
-template <bool BIG, int MODE>
-__device__ inline void store_slab(float* __restrict__ s, const float (&r)[Cfg<BIG>::kItems * 4]) {
-  using C = Cfg<BIG>;
+template <bool BIG, int TK, int MODE>
+__device__ inline void store_slab(float* __restrict__ s, const SlabRegs<BIG, TK>& r) {
+  using C = Cfg<BIG, TK>;
 #pragma unroll
   for (int h = 0; h < C::kItems; ++h) {
     const int g = threadIdx.x + h * C::kThreads;
@@ -135,8 +146,8 @@ __device__ inline void store_slab(float* __restrict__ s, const float (&r)[Cfg<BI
       f32x4 v = {r[4 * h], r[4 * h + 1], r[4 * h + 2], r[4 * h + 3]};
       *reinterpret_cast<f32x4*>(s + kk * C::kRow + mm) = v;
     } else {
-      const int mm = g / 4;
-      const int kq = (g % 4) * 4;
+      const int mm = g / (TK / 4);
+      const int kq = (g % (TK / 4)) * 4;
 #pragma unroll
       for (int q = 0; q < 4; ++q) s[mm * C::kKRow + kq + q] = r[4 * h + q];
     }
@@ -165,8 +176,9 @@ __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti
 }
 
 template <int AMODE, int BMODE, int EPI, bool BIG>
-__global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch batch) {
-  using C = Cfg<BIG>;
+__global__ void __launch_bounds__((Cfg<BIG, kTileKDeep>::kThreads)) gemm_f32_kernel(GemmBatch batch) {
+  constexpr int TK = EPI == EPI_SYRK ? kTileKSyrk : kTileKDeep;
+  using C = Cfg<BIG, TK>;
   __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
   __shared__ __attribute__((aligned(16))) float sB[2][C::kSlab];
   const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
@@ -188,7 +200,7 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     Cp += off;
   } else {
     if (P.nsplit > 1) {
-      const int len = ((ke - kb + P.nsplit - 1) / P.nsplit + kTileK - 1) / kTileK * kTileK;
+      const int len = ((ke - kb + P.nsplit - 1) / P.nsplit + TK - 1) / TK * TK;
       const int s0 = kb + split * len;
       ke = min(ke, s0 + len);
       kb = s0;
@@ -216,20 +228,20 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
   float ra[C::kItems * 4], rb[C::kItems * 4];
   int buf = 0;
   if (kb < ke) {
-    load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec);
-    load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec);
-    store_slab<BIG, AMODE>(sA[0], ra);
-    store_slab<BIG, BMODE>(sB[0], rb);
+    load_slab<BIG, TK, AMODE, true>(ra, Ab, P.lda, i0, P.M, kb, ke, P.a_special, P.A_extra, P.a_vec);
+    load_slab<BIG, TK, BMODE, false>(rb, Bb, P.ldb, j0, P.N, kb, ke, P.b_special, Bb, P.b_vec);
+    store_slab<BIG, TK, AMODE>(sA[0], ra);
+    store_slab<BIG, TK, BMODE>(sB[0], rb);
   }
   __syncthreads();
   // The main loop is instantiated twice: wavefronts without output run it
   // without MFMAs (a branch inside one loop costs the others registers).
   auto main_loop = [&](auto compute) {
-  for (int k0 = kb; k0 < ke; k0 += kTileK) {
-    const bool more = k0 + kTileK < ke;
+  for (int k0 = kb; k0 < ke; k0 += TK) {
+    const bool more = k0 + TK < ke;
     if (more) {
-      load_slab<BIG, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + kTileK, ke, P.a_special, P.A_extra, P.a_vec);
-      load_slab<BIG, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + kTileK, ke, P.b_special, Bb, P.b_vec);
+      load_slab<BIG, TK, AMODE, true>(ra, Ab, P.lda, i0, P.M, k0 + TK, ke, P.a_special, P.A_extra, P.a_vec);
+      load_slab<BIG, TK, BMODE, false>(rb, Bb, P.ldb, j0, P.N, k0 + TK, ke, P.b_special, Bb, P.b_vec);
     }
     if constexpr (decltype(compute)::value) {
     const float* a = sA[buf];
@@ -252,9 +264,9 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     frag(0, af[0], bf[0]);
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, C::kBI + C::kBJ, 0);
 #pragma unroll
-    for (int kk = 0; kk < kTileK; kk += 2) {
+    for (int kk = 0; kk < TK; kk += 2) {
       const int cur = (kk >> 1) & 1;
-      if (kk + 2 < kTileK) frag(kk + 2, af[cur ^ 1], bf[cur ^ 1]);
+      if (kk + 2 < TK) frag(kk + 2, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < C::kBI; ++i)
 #pragma unroll
@@ -266,8 +278,8 @@ __global__ void __launch_bounds__(Cfg<BIG>::kThreads) gemm_f32_kernel(GemmBatch 
     }
     }
     if (more) {
-      store_slab<BIG, AMODE>(sA[buf ^ 1], ra);
-      store_slab<BIG, BMODE>(sB[buf ^ 1], rb);
+      store_slab<BIG, TK, AMODE>(sA[buf ^ 1], ra);
+      store_slab<BIG, TK, BMODE>(sB[buf ^ 1], rb);
     }
     __syncthreads();
     buf ^= 1;
