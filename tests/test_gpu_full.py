@@ -255,11 +255,12 @@ def test_bf16_factor_row_chunks(gpu_lib):
 
 
 def test_graph_replays_match_eager(gpu_lib):
-    """One full step (factors, the Cholesky look-ahead on the library's second
-    stream, inverse, update) captured in a HIP graph through torch.cuda.graph
-    on ResNet-50 layer kinds (factors of up to 9 Cholesky blocks); three
-    replays, each followed by eager work and a synchronisation, match three
-    eager steps on the same inputs bitwise."""
+    """One full step (factors; the two-level Cholesky with its far updates
+    and the early inverse assembly on the library's side streams; update)
+    captured in a HIP graph through torch.cuda.graph on ResNet-50 layer kinds
+    (factors of up to 9 Cholesky blocks, three outer panels); three replays,
+    each followed by eager work and a synchronisation, match three eager steps
+    on the same inputs bitwise."""
     import torch
     from second_order_optimizer_amd.stack import KfacStack
     cfg = synth.small_config("resnet50_kfac")
@@ -274,7 +275,7 @@ def test_graph_replays_match_eager(gpu_lib):
 
     eager, graphed = make(), make()
     warm = make()
-    warm.step(H)              # the library's second stream and events exist before the capture
+    warm.step(H)              # the library's side streams and events exist before the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
