@@ -51,11 +51,18 @@ struct ColTasks {
   int32_t n;
 };
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 512;
+constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kMaxFinTasks = 44;
-constexpr int kMaxTpb = 16;    // taps per finishing block
+constexpr int kMaxTab = 2048;        // plane rows / columns covered by the LDS tap-mask tables
+constexpr int kFinPxPerLane = 16;    // team size target: about this many pixels per lane
 
 enum FinKind : int32_t { FIN_WINDOW = 0, FIN_CHUNKSUM = 1 };
+
+// Kernel rows handled by one window item for a k x k kernel: all of them for
+// k <= 3 (at most 9 taps per pixel), two for k = 4, one above (each item then
+// visits only the rows its kernel row reaches, stepping by the stride).
+__host__ __device__ constexpr int fin_nkh(int k) { return k <= 3 ? k : (k == 4 ? 2 : 1); }
 
 struct FinTask {
   const float* src;
@@ -66,8 +73,7 @@ struct FinTask {
   int32_t blk_begin;
   float scale;
   int32_t bias_index;                       // >= 0: dst[bias_index] = 1
-  int32_t tpb;                              // FIN_WINDOW: taps per unit (channel, tap group)
-  int32_t upw;                              // FIN_WINDOW: 0 = one unit per block, else units per wavefront
+  int32_t team;                             // FIN_WINDOW: wavefronts per item (1, 2, 4 or 8)
 };
 struct FinTasks {
   FinTask t[kMaxFinTasks];
@@ -164,10 +170,142 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Bit t of the result is set when input row (or column) x is reached by
+// kernel row (column) t from some output position: x = o * stride + t - pad
+// with 0 <= o < n_out.
+__device__ inline uint32_t tap_mask(int x, int k, int pad, int stride, int n_out) {
+  uint32_t m = 0;
+  for (int t = 0; t < k; ++t) {
+    const int y = x + pad - t;
+    if (y >= 0 && y % stride == 0 && y / stride < n_out) m |= 1u << t;
+  }
+  return m;
+}
+
+// One window item: channel c, kernel rows [kh0, kh0 + nk).  The team's lanes
+// walk the rows these kernel rows reach (every row, or every stride-th one
+// for a single kernel row) along the columns, VEC consecutive pixels per
+// load; a pixel adds its value to every tap (kh, kw) of the item whose masks
+// say it lies in that tap's window.  Each pixel of S is read once per item.
+template <int K, int VEC>
+__device__ __forceinline__ void fin_window(const FinTask& T, int c, int kh0, int nk, int tix, int nthr,
+                                           const uint8_t* rowtab, const uint8_t* coltab, bool tabs,
+                                           float (&acc)[fin_nkh(K) * K]) {
+  constexpr int NKH = fin_nkh(K);
+#pragma unroll
+  for (int t = 0; t < NKH * K; ++t) acc[t] = 0.f;
+  // rows reached by the item's kernel rows
+  int hfirst = 1 << 30, hlast = -1;
+  for (int r = 0; r < nk; ++r) {
+    const int kh = kh0 + r;
+    const int o0 = max(0, (T.pad - kh + T.stride - 1) / T.stride);          // first o with o*s + kh - pad >= 0
+    const int o1 = min(T.Ho - 1, (T.H - 1 + T.pad - kh) / T.stride);        // last o with o*s + kh - pad < H
+    if (T.H - 1 + T.pad - kh < 0 || o0 > o1) continue;
+    hfirst = min(hfirst, o0 * T.stride + kh - T.pad);
+    hlast = max(hlast, o1 * T.stride + kh - T.pad);
+  }
+  if (hlast < hfirst) return;
+  const int hstep = nk == 1 ? T.stride : 1;
+  const int nrows = (hlast - hfirst) / hstep + 1;
+  const int wv = T.W / VEC;                       // loads per row
+  const int nld = nrows * wv;
+  const float* S = T.src + static_cast<int64_t>(c) * T.H * T.W;
+  const uint32_t rsel = (1u << nk) - 1;
+  // lane position (row i, load column x), stepped by nthr loads without division
+  const int di = nthr / wv, dx = nthr - (nthr / wv) * wv;
+  int i = tix / wv, x = tix - (tix / wv) * wv;
+  for (int q0 = tix; q0 < nld; q0 += 8 * nthr) {
+    float v[8][VEC];
+    int hh[8], ww[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = q0 + u * nthr < nld;
+      hh[u] = ok ? hfirst + i * hstep : -1;
+      ww[u] = x * VEC;
+      if (ok) {
+        const float* ptr = S + static_cast<int64_t>(hh[u]) * T.W + ww[u];
+        if constexpr (VEC == 4) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(ptr);
+          v[u][0] = t4[0]; v[u][1] = t4[1]; v[u][2] = t4[2]; v[u][3] = t4[3];
+        } else {
+          v[u][0] = *ptr;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[u][e] = 0.f;
+      }
+      i += di;
+      x += dx;
+      if (x >= wv) { x -= wv; ++i; }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (hh[u] < 0) continue;
+      const uint32_t rm = (tabs ? rowtab[hh[u]] : tap_mask(hh[u], K, T.pad, T.stride, T.Ho)) >> kh0 & rsel;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t cm = tabs ? coltab[ww[u] + e] : tap_mask(ww[u] + e, K, T.pad, T.stride, T.Wo);
+#pragma unroll
+        for (int r = 0; r < NKH; ++r)
+#pragma unroll
+          for (int kw = 0; kw < K; ++kw)
+            acc[r * K + kw] += ((rm >> r) & (cm >> kw) & 1u) ? v[u][e] : 0.f;
+      }
+    }
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void fin_window_block(const FinTask& T, int b, float (*red)[16], uint8_t* rowtab,
+                                                 uint8_t* coltab) {
+  constexpr int NKH = fin_nkh(K);
+  const bool tabs = T.H <= kMaxTab && T.W <= kMaxTab;
+  if (tabs) {
+    for (int h = threadIdx.x; h < T.H; h += kFinThreads) rowtab[h] = tap_mask(h, K, T.pad, T.stride, T.Ho);
+    for (int w = threadIdx.x; w < T.W; w += kFinThreads) coltab[w] = tap_mask(w, K, T.pad, T.stride, T.Wo);
+  }
+  __syncthreads();
+  const int groups = (K + NKH - 1) / NKH;
+  const int items = T.C * groups;
+  const int teams = kFinWaves / T.team;
+  const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int team = wid / T.team, tw = wid - team * T.team;
+  const int item = b * teams + team;
+  const int nthr = T.team * kWave, tix = tw * kWave + lane;
+  const int c = item / groups, kh0 = (item - c * groups) * NKH, nk = min(NKH, K - kh0);
+  float acc[NKH * K];
+  if (item < items) {
+    const bool vec4 = (T.W & 3) == 0;   // plane starts and rows 16-byte aligned (S is 256-byte aligned)
+    if (vec4) fin_window<K, 4>(T, c, kh0, nk, tix, nthr, rowtab, coltab, tabs, acc);
+    else fin_window<K, 1>(T, c, kh0, nk, tix, nthr, rowtab, coltab, tabs, acc);
+  } else {
+#pragma unroll
+    for (int t = 0; t < NKH * K; ++t) acc[t] = 0.f;
+  }
+  float* out = T.dst + static_cast<int64_t>(c) * K * K + kh0 * K;
+#pragma unroll
+  for (int t = 0; t < NKH * K; ++t) {
+    const float v = wave_sum(acc[t]);
+    if (T.team == 1) {
+      if (lane == 0 && item < items && t < nk * K) out[t] = v * T.scale;
+    } else if (lane == 0) {
+      red[wid][t] = v;
+    }
+  }
+  if (T.team == 1) return;
+  __syncthreads();
+  if (tw == 0 && lane < nk * K && item < items) {
+    float v = 0.f;
+    for (int w = 0; w < T.team; ++w) v += red[team * T.team + w][lane];
+    out[lane] = v * T.scale;
+  }
+}
+
 __global__ void __launch_bounds__(kFinThreads) diag_finish_kernel(FinTasks tasks) {
-  __shared__ float red[kFinThreads / kWave][kMaxTpb];
+  __shared__ float red[kFinWaves][16];
+  __shared__ uint8_t rowtab[kMaxTab], coltab[kMaxTab];
   const int ti = find_task(tasks.t, tasks.n, blockIdx.x);  // uniform per block
-  const FinTask& T = tasks.t[ti];
+  const FinTask T = tasks.t[ti];   // by value: the helpers take its address
   const int b = blockIdx.x - T.blk_begin;
   if (T.bias_index >= 0 && b == 0 && threadIdx.x == 0) T.dst[T.bias_index] = 1.0f;
   if (T.kind == FIN_CHUNKSUM) {
@@ -179,83 +317,16 @@ __global__ void __launch_bounds__(kFinThreads) diag_finish_kernel(FinTasks tasks
     }
     return;
   }
-  // FIN_WINDOW.  A unit is (channel c, tap group of `tpb` taps): the sum of S
-  // at each tap's input pixel over all output positions.  Large units take a
-  // block each (positions spread over 256 threads, block reduction); small
-  // units (few output positions) go to single wavefronts, `upw` each, with a
-  // shuffle reduction and no block barrier.
-  const int k = T.k, taps = k * k, tpb = T.tpb;
-  const int groups = (taps + tpb - 1) / tpb;
-  const int units = T.C * groups;
-  const int npos = T.Ho * T.Wo;
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int nthr = T.upw ? kWave : kFinThreads;
-  const int tix = T.upw ? lane : threadIdx.x;
-  const int ubeg = T.upw ? (b * (kFinThreads / kWave) + wid) * T.upw : b;
-  const int uend = T.upw ? min(units, ubeg + T.upw) : b + 1;
-  for (int unit = ubeg; unit < uend; ++unit) {
-    const int c = unit / groups, tg = unit - c * groups;
-    const int t0 = tg * tpb, nt = min(tpb, taps - t0);
-    const float* S = T.src + static_cast<int64_t>(c) * T.H * T.W;
-    float acc[kMaxTpb];
-    int dh[kMaxTpb], dw[kMaxTpb];
-#pragma unroll
-    for (int t = 0; t < kMaxTpb; ++t) {
-      acc[t] = 0.f;
-      const int tap = t0 + (t < nt ? t : 0);
-      dh[t] = tap / k - T.pad;
-      dw[t] = tap % k - T.pad;
-    }
-    // 8 independent loads in flight per thread per tap; the thread's output
-    // position advances by nthr each time, (ho, wo) stepped without division
-    const int sh = nthr / T.Wo, sw = nthr - sh * T.Wo;
-    int ho = tix / T.Wo, wo = tix - (tix / T.Wo) * T.Wo;
-    for (int q0 = tix; q0 < npos; q0 += nthr * 8) {
-      int hb[8], wb[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        hb[u] = q0 + u * nthr < npos ? ho * T.stride : -(1 << 20);   // out of range -> every tap invalid
-        wb[u] = wo * T.stride;
-        ho += sh;
-        wo += sw;
-        if (wo >= T.Wo) { wo -= T.Wo; ++ho; }
-      }
-#pragma unroll
-      for (int t = 0; t < kMaxTpb; ++t) {
-        if (t >= nt) break;
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int hh = hb[u] + dh[t], ww = wb[u] + dw[t];
-          v[u] = (hh >= 0 && hh < T.H && ww >= 0 && ww < T.W) ? S[hh * T.W + ww] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[t] += v[u];
-      }
-    }
-    float* out = T.dst + static_cast<int64_t>(c) * taps + t0;
-    if (T.upw) {
-#pragma unroll
-      for (int t = 0; t < kMaxTpb; ++t) {
-        if (t >= nt) break;
-        const float v = wave_sum(acc[t]);
-        if (lane == 0) out[t] = v * T.scale;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kMaxTpb; ++t) {
-        if (t >= nt) break;
-        const float v = wave_sum(acc[t]);
-        if (lane == 0) red[wid][t] = v;
-      }
-      __syncthreads();
-      if (threadIdx.x < nt) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < kFinThreads / kWave; ++w) v += red[w][threadIdx.x];
-        out[threadIdx.x] = v * T.scale;
-      }
-    }
+  // FIN_WINDOW: dA[c, kh, kw] = scale * sum over output positions of
+  // S[c, ho * stride + kh - pad, wo * stride + kw - pad] (zero outside)
+  switch (T.k) {
+    case 1: fin_window_block<1>(T, b, red, rowtab, coltab); break;
+    case 2: fin_window_block<2>(T, b, red, rowtab, coltab); break;
+    case 3: fin_window_block<3>(T, b, red, rowtab, coltab); break;
+    case 4: fin_window_block<4>(T, b, red, rowtab, coltab); break;
+    case 5: fin_window_block<5>(T, b, red, rowtab, coltab); break;
+    case 6: fin_window_block<6>(T, b, red, rowtab, coltab); break;
+    default: fin_window_block<7>(T, b, red, rowtab, coltab); break;
   }
 }
 
@@ -295,7 +366,15 @@ __global__ void __launch_bounds__(kUpdThreads) diag_update_kernel(Segs segs) {
     for (int u = 0; u < kUpdUnroll; ++u) {
       if (e[u] >= S.n) continue;
       float tgt[4];
-      if (S.dA) {
+      if (S.dA && (S.cols & 3) == 0) {
+        // the 4 elements share a row: one dG entry, 4 adjacent dA entries
+        const int o = e[u] / S.cols;
+        const int j = e[u] - o * S.cols;
+        const float dg = S.dG[o];
+        const f32x4 da = *reinterpret_cast<const f32x4*>(S.dA + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tgt[q] = dg * da[q];
+      } else if (S.dA) {
         int o = e[u] / S.cols;
         int j = e[u] - o * S.cols;
 #pragma unroll
@@ -347,27 +426,23 @@ struct DiagPlan {
   size_t ws_bytes = kFlagBytes;
 };
 
-// Taps per unit: about 4096 position-taps of work per unit.
-int window_tpb(int k, int positions) {
-  const int taps = k * k;
-  int tpb = std::max(1, 4096 / std::max(1, positions));
-  return std::min(std::min(tpb, kMaxTpb), taps);
-}
-
-// Units per wavefront for small units (<= 1024 output positions): each unit
-// costs a load round trip, so a wavefront takes at most 4; 0 = one unit per
-// block.
-int window_upw(int tpb, int positions) {
-  if (positions > 1024) return 0;
-  return std::min(4, std::max(1, 4096 / std::max(1, tpb * positions)));
+// Wavefronts per window item: the smallest team (1, 2, 4 or 8 wavefronts)
+// whose lanes see at most about kFinPxPerLane pixels each.
+int window_team(int k, int stride, int H, int W, int Ho) {
+  const int nkh = fin_nkh(k);
+  const int64_t rows = nkh == 1 ? std::min<int64_t>(H, Ho) : H;
+  const int64_t px = rows * W;
+  int team = 1;
+  while (team < kFinWaves && px > static_cast<int64_t>(kWave) * team * kFinPxPerLane) team *= 2;
+  (void)stride;
+  return team;
 }
 
 int fin_blocks(const FinTask& t) {
   if (t.kind == FIN_WINDOW) {
-    const int units = t.C * ((t.k * t.k + t.tpb - 1) / t.tpb);
-    if (t.upw == 0) return units;
-    const int per_block = t.upw * (kFinThreads / kWave);
-    return (units + per_block - 1) / per_block;
+    const int items = t.C * ((t.k + fin_nkh(t.k) - 1) / fin_nkh(t.k));
+    const int per_block = kFinWaves / t.team;
+    return (items + per_block - 1) / per_block;
   }
   return t.chunks > 1 ? (t.K + kFinThreads - 1) / kFinThreads : 1;
 }
@@ -415,8 +490,7 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
       fx.src = Sx; fx.dst = L.dA; fx.kind = FIN_WINDOW;
       fx.C = g.c_in; fx.H = g.h; fx.W = g.w; fx.k = g.kh; fx.stride = g.stride; fx.pad = g.pad;
       fx.Ho = g.h_out; fx.Wo = g.w_out; fx.scale = invN; fx.bias_index = g.bias ? g.d_in : -1;
-      fx.tpb = window_tpb(g.kh, g.h_out * g.w_out);
-      fx.upw = window_upw(fx.tpb, g.h_out * g.w_out);
+      fx.team = window_team(g.kh, g.stride, g.h, g.w, g.h_out);
       add_fin(fx, fin_blocks(fx));
       const int Kg = g.d_out * g.h_out * g.w_out;
       float* Sg = carve(Kg);
@@ -425,8 +499,7 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
       fg.src = Sg; fg.dst = L.dG; fg.kind = FIN_WINDOW;
       fg.C = g.d_out; fg.H = g.h_out; fg.W = g.w_out; fg.k = 1; fg.stride = 1; fg.pad = 0;
       fg.Ho = g.h_out; fg.Wo = g.w_out; fg.scale = invN; fg.bias_index = -1;
-      fg.tpb = 1;
-      fg.upw = window_upw(1, g.h_out * g.w_out);
+      fg.team = window_team(1, 1, g.h_out, g.w_out, g.h_out);
       add_fin(fg, fin_blocks(fg));
     } else {
       const int64_t R = g.rows;

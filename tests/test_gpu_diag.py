@@ -35,6 +35,21 @@ def test_diag_edge_shapes(gpu_lib):
     lockstep(cfg, cfg.steps, TOL, DIAG_KEYS)
 
 
+def test_diag_window_kernel_sizes(gpu_lib):
+    """Every kernel size the ABI accepts besides 1, 3 and 7 (2, 4, 5, 6, with
+    strides 1-3 and padding beyond the kernel's half-width), a plane large
+    enough for eight wavefronts per window item, and a plane wider than
+    2048 columns (tap masks computed per pixel instead of from tables)."""
+    L = [synth.conv("k2", 3, 4, 2, 2, 0, 2, 9, 11),
+         synth.conv("k4", 2, 3, 4, 1, 2, 2, 8),
+         synth.conv("k5", 3, 2, 5, 3, 2, 2, 13, 10),
+         synth.conv("k6", 2, 5, 6, 2, 3, 2, 9, 7),
+         synth.conv("big_plane", 2, 3, 3, 1, 1, 2, 96, 100),
+         synth.conv("wide", 1, 2, 3, 2, 1, 2, 3, 2100, bias=True)]
+    cfg = with_layers(synth.small_config("resnet18_diag"), L, steps=2)
+    lockstep(cfg, cfg.steps, TOL, DIAG_KEYS)
+
+
 def test_diag_phase_split_equals_fused(gpu_lib):
     """FACTORS then UPDATE as two calls gives the same bits as one call."""
     import torch
