@@ -458,11 +458,135 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
 // ---------------------------------------------------------------------------
 // planning
 
+// ---------------------------------------------------------------------------
+// Bias column of the preconditioned gradient.  With a bias, d_a = d_in + 1;
+// when d_in is a whole number of GEMM tiles, a (d_in + 1)-wide tile grid would
+// end in a column of tiles with one valid column, which costs as much as a
+// full one.  Those layers run both preconditioning GEMMs over the first d_in
+// columns, and the last column as two matrix-vector products, batched over
+// layers (HBM-bound: every matrix entry is read once):
+//   stage 0: t[i] = sum_k [grad_w | grad_b][i][k] A_inv[k][d_in]
+//   stage 1: p[i] = sum_k G_inv[i][k] t[k]; D = p + wd b; V = mu V + D; b -= lr V
+// A_inv and G_inv are symmetric, so contiguous rows stand in for columns.
+bool bias_column_split(const LayerGeom& g) { return g.bias && g.d_in % kTile == 0; }
+
+constexpr int kBcThreads = 256;
+constexpr int kBcRowsPerWave = 4;
+constexpr int kBcRowsPerBlock = kBcThreads / kWave * kBcRowsPerWave;
+constexpr int kMaxBcProbs = 48;   // kernel arguments stay within 4 KB
+
+struct BcProb {
+  const float* M;       // row i at M + i * ld, kmain entries
+  const float* extra;   // stage 0: entry kmain of row i is extra[i]; stage 1: null
+  const float* x;       // kmain (+1 with extra) entries
+  float* y;             // stage 0: t
+  float* b;             // stage 1: bias and its momentum, updated in place
+  float* mb;
+  int32_t rows, ld, kmain, blk_begin, vec, pad_;
+};
+struct BcTab {
+  BcProb p[kMaxBcProbs];
+  int32_t n, stage;
+  float lr, momentum, weight_decay;
+  uint32_t* flags;
+};
+
+__device__ inline float bc_wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__global__ void __launch_bounds__(kBcThreads) bias_col_kernel(BcTab tab) {
+  int lo = 0, hi = tab.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.p[mid].blk_begin <= static_cast<int>(blockIdx.x)) lo = mid; else hi = mid - 1;
+  }
+  const BcProb P = tab.p[lo];
+  const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int row0 = (blockIdx.x - P.blk_begin) * kBcRowsPerBlock + wid * kBcRowsPerWave;
+  if (row0 >= P.rows) return;
+  const float* m[kBcRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kBcRowsPerWave; ++r)
+    m[r] = P.M + static_cast<int64_t>(min(row0 + r, P.rows - 1)) * P.ld;   // clamped rows are discarded
+  float acc[kBcRowsPerWave] = {};
+  int k = 0;
+  if (P.vec) {   // 16-byte loads: ld, kmain multiples of 4 and aligned bases
+    const int kv = P.kmain & ~(8 * kWave - 1);
+    for (k = 8 * lane; k < kv; k += 8 * kWave) {   // two float4 per row in flight per lane
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(P.x + k);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(P.x + k + 4);
+      f32x4 a0[kBcRowsPerWave], a1[kBcRowsPerWave];
+#pragma unroll
+      for (int r = 0; r < kBcRowsPerWave; ++r) {
+        a0[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m[r] + k));
+        a1[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m[r] + k + 4));
+      }
+#pragma unroll
+      for (int r = 0; r < kBcRowsPerWave; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r] = fmaf(a0[r][e], x0[e], fmaf(a1[r][e], x1[e], acc[r]));
+    }
+    k = kv;
+  }
+  for (k += lane; k < P.kmain; k += kWave) {
+    const float xv = P.x[k];
+#pragma unroll
+    for (int r = 0; r < kBcRowsPerWave; ++r) acc[r] = fmaf(m[r][k], xv, acc[r]);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < kBcRowsPerWave; ++r) {
+    const float v = bc_wave_sum(acc[r]);
+    const int row = row0 + r;
+    if (lane != 0 || row >= P.rows) continue;
+    if (tab.stage == 0) {
+      P.y[row] = P.extra ? fmaf(P.extra[row], P.x[P.kmain], v) : v;
+    } else {
+      const float w = P.b[row];
+      const float d = fmaf(tab.weight_decay, w, v);
+      const float vn = fmaf(tab.momentum, P.mb[row], d);
+      const float wn = fmaf(-tab.lr, vn, w);
+      P.mb[row] = vn;
+      P.b[row] = wn;
+      bad |= !(isfinite(vn) && isfinite(wn));
+    }
+  }
+  if (bad) raise_flag(tab.flags, KFAC_FLAG_NONFINITE);
+}
+
+// Launches one stage of the bias-column products for every listed problem.
+kfac_status_t launch_bias_col(std::vector<BcProb>& probs, int stage, const kfac_hparams_t& hp, uint32_t* flags,
+                              hipStream_t st) {
+  for (size_t g0 = 0; g0 < probs.size(); g0 += kMaxBcProbs) {
+    const size_t g1 = std::min(probs.size(), g0 + kMaxBcProbs);
+    BcTab T{};
+    int blocks = 0;
+    for (size_t i = g0; i < g1; ++i) {
+      T.p[i - g0] = probs[i];
+      T.p[i - g0].blk_begin = blocks;
+      blocks += (probs[i].rows + kBcRowsPerBlock - 1) / kBcRowsPerBlock;
+    }
+    T.n = static_cast<int>(g1 - g0);
+    T.stage = stage;
+    T.lr = hp.lr;
+    T.momentum = hp.momentum;
+    T.weight_decay = hp.weight_decay;
+    T.flags = flags;
+    hipLaunchKernelGGL(bias_col_kernel, dim3(blocks), dim3(kBcThreads), 0, st, T);
+    KFAC_HIP_TRY(hipGetLastError());
+  }
+  return KFAC_OK;
+}
+
 struct FullPlan {
   size_t ws_bytes = kFlagBytes;
   std::vector<float*> part;      // per layer and factor (2 li + which): split-K partials, or null
   std::vector<int> nsplit;       // per layer and factor
   std::vector<float*> T;         // per layer, d_out x d_a
+  std::vector<float*> tb;        // per layer: column d_in of T (bias-column layers), else null
   std::vector<float*> xcol;      // per layer and factor: fp32 convolution tensor as [rows, width], or null
   std::vector<int> xcol_ld;      // their row pitch (floats)
   std::vector<Mat> mats;         // inverse work per factor (2 layer + which)
@@ -514,6 +638,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
     P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * g.d_a * 4)));
+    P.tb.push_back(bias_column_split(g) ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * 4)) : nullptr);
   }
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
@@ -1053,9 +1178,35 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
 kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                            uint32_t* flags, hipStream_t st) {
   std::vector<GemmProb> g1, g2;
+  std::vector<BcProb> b0, b1;
+  auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   for (int li = 0; li < n; ++li) {
     const kfac_layer_t& L = layers[li];
     const LayerGeom g = geom_of(L);
+    const bool split = bias_column_split(g);
+    const int ncols = split ? g.d_in : g.d_a;   // columns the GEMMs produce
+    if (split) {
+      BcProb s0{};
+      s0.M = static_cast<const float*>(L.grad_w);
+      s0.extra = L.grad_b;
+      s0.x = L.A_inv + static_cast<int64_t>(g.d_in) * g.d_a;
+      s0.y = P.tb[li];
+      s0.rows = g.d_out;
+      s0.ld = g.d_in;
+      s0.kmain = g.d_in;
+      s0.vec = g.d_in % 4 == 0 && aligned16(s0.M) && aligned16(s0.x);
+      b0.push_back(s0);
+      BcProb s1{};
+      s1.M = L.G_inv;
+      s1.x = P.tb[li];
+      s1.b = L.b;
+      s1.mb = L.mom_b;
+      s1.rows = g.d_out;
+      s1.ld = g.d_out;
+      s1.kmain = g.d_out;
+      s1.vec = g.d_out % 4 == 0 && aligned16(s1.M) && aligned16(s1.x);
+      b1.push_back(s1);
+    }
     GemmProb p{};
     // T = [grad_w | grad_b] A_inv
     p.A = L.grad_w;
@@ -1068,7 +1219,7 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     p.C = P.T[li];
     p.ldc = g.d_a;
     p.M = g.d_out;
-    p.N = g.d_a;
+    p.N = ncols;
     p.kb = 0;
     p.ke = g.d_a;
     p.tri = TRI_FULL;
@@ -1085,7 +1236,7 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     q.ldb = g.d_a;
     q.b_special = -1;
     q.M = g.d_out;
-    q.N = g.d_a;
+    q.N = ncols;
     q.kb = 0;
     q.ke = g.d_out;
     q.tri = TRI_FULL;
@@ -1099,7 +1250,11 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     g2.push_back(q);
   }
   GemmScalars sc{hp.lr, hp.momentum, hp.weight_decay, flags};
-  kfac_status_t r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
+  kfac_status_t r = launch_bias_col(b0, 0, hp, flags, st);
+  if (r != KFAC_OK) return r;
+  r = launch_bias_col(b1, 1, hp, flags, st);
+  if (r != KFAC_OK) return r;
+  r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
   if (r != KFAC_OK) return r;
   return launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
 }

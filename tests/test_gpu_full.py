@@ -50,6 +50,19 @@ def test_fp32_linear_split_k(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
+def test_bias_column_layers(gpu_lib):
+    """Biased layers whose d_in is a whole number of 128-wide tiles: the
+    preconditioning GEMMs cover the weight columns and the bias column is two
+    matrix-vector products (16-byte loads when d_out is a multiple of 4,
+    scalar loads otherwise), beside a layer of the same kind without the
+    split (d_in = 200)."""
+    L = [synth.linear("vec", 256, 300, 900, bias=True),
+         synth.linear("scalar", 384, 130, 700, bias=True),
+         synth.linear("nosplit", 200, 128, 500, bias=True)]
+    cfg = with_layers(synth.full_config("fc64"), L, steps=3, act_std=1.0, grad_std=1e-2)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
 def test_conv_split_k_and_layouts(gpu_lib):
     """Convolution factors (im2col rows and transposed gradients, then the
     row-major SYRK): a 7x7/2 stem with 16,900 rows (9 row splits summed by the
@@ -63,13 +76,15 @@ def test_conv_split_k_and_layouts(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
-def test_sgd_reduction_update_phase(gpu_lib):
+@pytest.mark.parametrize("d_in", [150, 256])
+def test_sgd_reduction_update_phase(gpu_lib, d_in):
     """UPDATE phase alone with identity inverses: the step is SGD with momentum
-    and weight decay (closed form from the oracle's update)."""
+    and weight decay (closed form from the oracle's update); d_in = 256 takes
+    the bias-column matrix-vector path."""
     import torch
     from second_order_optimizer_amd import PHASE_UPDATE
     from second_order_optimizer_amd.stack import KfacStack
-    cfg = with_layers(synth.full_config("fc64"), [synth.linear("fc", 150, 70, 8, bias=True)])
+    cfg = with_layers(synth.full_config("fc64"), [synth.linear("fc", d_in, 70, 8, bias=True)])
     L = cfg.layers[0]
     st = KfacStack(cfg.layers, "full")
     s0 = synth.initial_state(cfg, 0)
