@@ -31,7 +31,8 @@ namespace kfac {
 namespace {
 
 constexpr int kColThreads = 256;
-constexpr int kColTile = kColThreads * 4;   // columns per workgroup
+constexpr int kColWaves = kColThreads / 64;
+constexpr int kColTile = 64 * 4;            // columns per workgroup (4 per lane; the wavefronts split the rows)
 constexpr int kRowChunk = 512;              // rows per workgroup before chunking
 constexpr int kMaxColTasks = 64;
 
@@ -115,6 +116,7 @@ __device__ inline int find_task(const T (&t)[N], int n, int blk) {
 }
 
 __global__ void __launch_bounds__(kColThreads) diag_colsq_kernel(ColTasks tasks) {
+  __shared__ f32x4 part[kColWaves - 1][64];
   const int ti = find_task(tasks.t, tasks.n, blockIdx.x);
   const ColTask& T = tasks.t[ti];
   const int b = blockIdx.x - T.blk_begin;
@@ -122,45 +124,59 @@ __global__ void __launch_bounds__(kColThreads) diag_colsq_kernel(ColTasks tasks)
   const int chunk = b / T.tiles;
   const int64_t r0 = static_cast<int64_t>(chunk) * T.rc;
   const int64_t r1 = min(T.R, r0 + T.rc);
-  const int c0 = tile * kColTile + threadIdx.x * 4;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int c0 = tile * kColTile + lane * 4;
   const int K = T.K;
-  if (c0 >= K) return;
   float* out = T.chunks == 1 ? T.dst : T.dst + static_cast<int64_t>(chunk) * K;
   const float s = T.chunks == 1 ? T.scale : 1.0f;
-  if ((K & 3) == 0) {
-    const float* p = T.src + r0 * K + c0;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-    int64_t r = r0;
-    for (; r + 16 <= r1; r += 16) {
-      f32x4 v[16];
+  // wavefront w sums rows r0 + w, r0 + w + 4, ...; the four partial sums
+  // are added in wavefront order (deterministic)
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (c0 < K) {
+    if ((K & 3) == 0) {
+      const int64_t stride = static_cast<int64_t>(kColWaves) * K;
+      const float* p = T.src + (r0 + wid) * K + c0;
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+      int64_t r = r0 + wid;
+      for (; r + 15 * kColWaves < r1; r += 16 * kColWaves) {
+        f32x4 v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + u * static_cast<int64_t>(K)));
+        for (int u = 0; u < 16; ++u)
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + u * stride));
 #pragma unroll
-      for (int u = 0; u < 16; u += 2) {
-        acc0 += v[u] * v[u];
-        acc1 += v[u + 1] * v[u + 1];
+        for (int u = 0; u < 16; u += 2) {
+          acc0 += v[u] * v[u];
+          acc1 += v[u + 1] * v[u + 1];
+        }
+        p += 16 * stride;
       }
-      p += 16 * static_cast<int64_t>(K);
-    }
-    for (; r < r1; ++r) {
-      f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-      acc0 += v * v;
-      p += K;
-    }
-    f32x4 acc = acc0 + acc1;
-    *reinterpret_cast<f32x4*>(out + c0) = acc * s;
-  } else {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t r = r0; r < r1; ++r) {
-      const float* p = T.src + r * K;
+      for (; r < r1; r += kColWaves) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        acc0 += v * v;
+        p += stride;
+      }
+      acc = acc0 + acc1;
+    } else {
+      for (int64_t r = r0 + wid; r < r1; r += kColWaves) {
+        const float* p = T.src + r * K;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (c0 + q < K) acc[q] = fmaf(p[c0 + q], p[c0 + q], acc[q]);
+        for (int q = 0; q < 4; ++q)
+          if (c0 + q < K) acc[q] = fmaf(p[c0 + q], p[c0 + q], acc[q]);
+      }
     }
+  }
+  if (wid > 0) part[wid - 1][lane] = acc;
+  __syncthreads();
+  if (wid != 0 || c0 >= K) return;
+#pragma unroll
+  for (int w = 0; w < kColWaves - 1; ++w) acc += part[w][lane];
+  acc *= s;
+  if ((K & 3) == 0) {
+    *reinterpret_cast<f32x4*>(out + c0) = acc;
+  } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (c0 + q < K) out[c0 + q] = acc[q] * s;
+      if (c0 + q < K) out[c0 + q] = acc[q];
   }
 }
 
