@@ -101,7 +101,10 @@ enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
  * Full method:  A, A_inv : [d_a, d_a]; G, G_inv : [d_out, d_out]  (float32,
  *               symmetric; the library reads the upper triangle of A and G and
  *               writes both triangles).  A, G are updated in place every step;
- *               A_inv, G_inv are written on refresh steps and read every step.
+ *               A_inv, G_inv are written on refresh steps and read every step;
+ *               the UPDATE phase reads them as symmetric matrices (either
+ *               triangle, rows in place of columns), so inverses a caller
+ *               supplies must be symmetric too.
  * Diag method:  F_w, F_b updated in place; dA [d_a], dG [d_out] are written by
  *               the FACTORS phase and read by the UPDATE phase.
  * Pointers a method does not use may be NULL.  w, mom_w, b, mom_b are updated
