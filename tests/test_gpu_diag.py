@@ -171,3 +171,14 @@ def test_diag_resnet18_full_size_sampled(gpu_lib):
     say("full-size sampled worst:", {k: f"{v:.2e}" for k, v in worst.items()})
     for k, v in worst.items():
         assert v <= 1e-4, (k, v)
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_diag_degenerate_shapes_and_ema_limits(gpu_lib, beta):
+    """1 -> 1 and single-row layers and a 1 x 1 single-channel conv at EMA
+    decay 0 (F is this batch's dG dA) and 1 (F is kept)."""
+    L = [synth.linear("one_one", 1, 1, 6, bias=True),
+         synth.linear("one_row", 5, 4, 1, bias=True),
+         synth.conv("pointwise", 1, 1, 1, 1, 0, 2, 3)]
+    cfg = with_layers(synth.small_config("resnet18_diag"), L, steps=2, ema_decay=beta)
+    lockstep(cfg, cfg.steps, TOL, DIAG_KEYS)

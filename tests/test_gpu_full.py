@@ -307,3 +307,18 @@ def test_graph_replays_match_eager(gpu_lib):
             for k in a:
                 assert np.array_equal(a[k], b[k]), (rep, cfg.layers[li].name, k)
     say("graph replays match eager steps bitwise")
+
+
+@pytest.mark.parametrize("ema", [0.0, 1.0])
+def test_degenerate_shapes_and_ema_limits(gpu_lib, ema):
+    """A 1 -> 1 layer with a bias (2 x 2 and 1 x 1 factors), a single-row
+    layer (rank-one batch factor), a 3 -> 2 layer without a bias and a 1 x 1
+    single-channel conv, at EMA decay 0 (the factor is this batch's alone and
+    the old one is not read) and 1 (the factor is kept); inverse every step."""
+    L = [synth.linear("one_one", 1, 1, 6, bias=True),
+         synth.linear("one_row", 5, 4, 1, bias=True),
+         synth.linear("tiny", 3, 2, 5, bias=False),
+         synth.conv("pointwise", 1, 1, 1, 1, 0, 2, 3)]
+    cfg = with_layers(synth.full_config("fc64"), L, steps=2, act_std=1.0, grad_std=1e-2, ema_decay=ema,
+                      refresh_every=1)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
