@@ -322,3 +322,12 @@ def test_degenerate_shapes_and_ema_limits(gpu_lib, ema):
     cfg = with_layers(synth.full_config("fc64"), L, steps=2, act_std=1.0, grad_std=1e-2, ema_decay=ema,
                       refresh_every=1)
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
+def test_bf16_factor_xcd_runs(gpu_lib):
+    """Ten bf16 layers 1024 -> 768 with a bias: one factor launch of 160
+    tiles, whose first 128 go to the XCDs in runs of 16 consecutive tiles and
+    the rest in order; every factor entry checked against the oracle."""
+    L = synth.mlp_layers(5, 1024, 768, 64)
+    cfg = with_layers(synth.small_config("mlp24_bf16"), L, steps=2, refresh_every=1)
+    lockstep(cfg, cfg.steps, TOL16, FULL_KEYS)
