@@ -471,7 +471,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
 bool bias_column_split(const LayerGeom& g) { return g.bias && g.d_in % kTile == 0; }
 
 constexpr int kBcThreads = 256;
-constexpr int kBcRowsPerWave = 4;
+constexpr int kBcRowsPerWave = 2;
 constexpr int kBcRowsPerBlock = kBcThreads / kWave * kBcRowsPerWave;
 constexpr int kMaxBcProbs = 48;   // kernel arguments stay within 4 KB
 
@@ -497,6 +497,9 @@ __device__ inline float bc_wave_sum(float v) {
   return v;
 }
 
+// Kept small (two rows per wavefront, one 16-byte load per row in flight,
+// about two dozen VGPRs) so that its wavefronts fit beside the 256 x 256 GEMM
+// workgroups, which leave 32-48 VGPRs per SIMD lane, and run alongside them.
 __global__ void __launch_bounds__(kBcThreads) bias_col_kernel(BcTab tab) {
   int lo = 0, hi = tab.n - 1;
   while (lo < hi) {
@@ -507,39 +510,33 @@ __global__ void __launch_bounds__(kBcThreads) bias_col_kernel(BcTab tab) {
   const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int row0 = (blockIdx.x - P.blk_begin) * kBcRowsPerBlock + wid * kBcRowsPerWave;
   if (row0 >= P.rows) return;
-  const float* m[kBcRowsPerWave];
-#pragma unroll
-  for (int r = 0; r < kBcRowsPerWave; ++r)
-    m[r] = P.M + static_cast<int64_t>(min(row0 + r, P.rows - 1)) * P.ld;   // clamped rows are discarded
-  float acc[kBcRowsPerWave] = {};
+  const float* m0 = P.M + static_cast<int64_t>(row0) * P.ld;
+  const float* m1 = P.M + static_cast<int64_t>(min(row0 + 1, P.rows - 1)) * P.ld;   // a clamped row is discarded
+  float acc0 = 0.f, acc1 = 0.f;
   int k = 0;
   if (P.vec) {   // 16-byte loads: ld, kmain multiples of 4 and aligned bases
-    const int kv = P.kmain & ~(8 * kWave - 1);
-    for (k = 8 * lane; k < kv; k += 8 * kWave) {   // two float4 per row in flight per lane
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(P.x + k);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(P.x + k + 4);
-      f32x4 a0[kBcRowsPerWave], a1[kBcRowsPerWave];
+    const int kv = P.kmain & ~(4 * kWave - 1);
+    for (k = 4 * lane; k < kv; k += 4 * kWave) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(P.x + k);
+      const f32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m0 + k));
+      const f32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m1 + k));
 #pragma unroll
-      for (int r = 0; r < kBcRowsPerWave; ++r) {
-        a0[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m[r] + k));
-        a1[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m[r] + k + 4));
+      for (int e = 0; e < 4; ++e) {
+        acc0 = fmaf(a0[e], xv[e], acc0);
+        acc1 = fmaf(a1[e], xv[e], acc1);
       }
-#pragma unroll
-      for (int r = 0; r < kBcRowsPerWave; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[r] = fmaf(a0[r][e], x0[e], fmaf(a1[r][e], x1[e], acc[r]));
     }
     k = kv;
   }
   for (k += lane; k < P.kmain; k += kWave) {
     const float xv = P.x[k];
-#pragma unroll
-    for (int r = 0; r < kBcRowsPerWave; ++r) acc[r] = fmaf(m[r][k], xv, acc[r]);
+    acc0 = fmaf(m0[k], xv, acc0);
+    acc1 = fmaf(m1[k], xv, acc1);
   }
   bool bad = false;
 #pragma unroll
   for (int r = 0; r < kBcRowsPerWave; ++r) {
-    const float v = bc_wave_sum(acc[r]);
+    const float v = bc_wave_sum(r == 0 ? acc0 : acc1);
     const int row = row0 + r;
     if (lane != 0 || row >= P.rows) continue;
     if (tab.stage == 0) {
@@ -818,7 +815,7 @@ struct SideStream {
   hipStream_t s = nullptr;   // Cholesky inner chain
   hipStream_t f = nullptr;   // inverse assembly of factors whose Cholesky is complete
   hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, main_done[2] = {nullptr, nullptr},
-             side_done[2] = {nullptr, nullptr};
+             side_done[2] = {nullptr, nullptr}, ufork = nullptr, ujoin = nullptr;
 };
 
 kfac_status_t side_stream(SideStream** out) {
@@ -832,8 +829,8 @@ kfac_status_t side_stream(SideStream** out) {
   if (!S.s) {
     KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking));
     KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.f, hipStreamNonBlocking));
-    hipEvent_t* evs[7] = {&S.fork,         &S.join,         &S.fjoin,       &S.main_done[0],
-                          &S.main_done[1], &S.side_done[0], &S.side_done[1]};
+    hipEvent_t* evs[9] = {&S.fork,          &S.join,          &S.fjoin, &S.main_done[0], &S.main_done[1],
+                          &S.side_done[0], &S.side_done[1], &S.ufork, &S.ujoin};
     for (hipEvent_t* e : evs) KFAC_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
   }
   *out = &S;
@@ -1250,13 +1247,28 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     g2.push_back(q);
   }
   GemmScalars sc{hp.lr, hp.momentum, hp.weight_decay, flags};
-  kfac_status_t r = launch_bias_col(b0, 0, hp, flags, st);
-  if (r != KFAC_OK) return r;
-  r = launch_bias_col(b1, 1, hp, flags, st);
-  if (r != KFAC_OK) return r;
+  // The bias-column products (HBM-bound) run on the side stream beside the
+  // two GEMMs (MFMA-bound): they read what the GEMMs read and write only t,
+  // b and mom_b, which the GEMMs do not touch.
+  kfac_status_t r;
+  SideStream* side = nullptr;
+  if (!b0.empty()) {
+    r = side_stream(&side);
+    if (r != KFAC_OK) return r;
+    KFAC_HIP_TRY(hipEventRecord(side->ufork, st));
+    KFAC_HIP_TRY(hipStreamWaitEvent(side->s, side->ufork, 0));
+    r = launch_bias_col(b0, 0, hp, flags, side->s);
+    if (r != KFAC_OK) return r;
+    r = launch_bias_col(b1, 1, hp, flags, side->s);
+    if (r != KFAC_OK) return r;
+    KFAC_HIP_TRY(hipEventRecord(side->ujoin, side->s));
+  }
   r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
   if (r != KFAC_OK) return r;
-  return launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
+  r = launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
+  if (r != KFAC_OK) return r;
+  if (side) KFAC_HIP_TRY(hipStreamWaitEvent(st, side->ujoin, 0));
+  return KFAC_OK;
 }
 
 }  // namespace

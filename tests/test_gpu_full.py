@@ -273,12 +273,14 @@ def test_graph_replays_match_eager(gpu_lib):
     """One full step (factors; the two-level Cholesky with its far updates
     and the early inverse assembly on the library's side streams; update)
     captured in a HIP graph through torch.cuda.graph on ResNet-50 layer kinds
-    (factors of up to 9 Cholesky blocks, three outer panels); three replays,
-    each followed by eager work and a synchronisation, match three eager steps
-    on the same inputs bitwise."""
+    (factors of up to 9 Cholesky blocks, three outer panels) plus a biased
+    256-input layer (its bias column on the side stream beside the update
+    GEMMs); three replays, each followed by eager work and a synchronisation,
+    match three eager steps on the same inputs bitwise."""
     import torch
     from second_order_optimizer_amd.stack import KfacStack
-    cfg = synth.small_config("resnet50_kfac")
+    base = synth.small_config("resnet50_kfac")
+    cfg = with_layers(base, list(base.layers) + [synth.linear("fc_split", 256, 96, 32, bias=True)])
     H = KfacStack.hparams(synth.hparams(cfg), refresh=True)
 
     def make():
