@@ -401,12 +401,16 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   }
   __syncthreads();
 
-  for (int p = 0; p < kNb / 32; ++p) {
+  // Only the first np 32-column sub-blocks hold the factor (bk rows); the
+  // rest of the working block is identity, is never read by them and is not
+  // written out, so a ragged last block skips it.
+  const int np = (bk + 31) / 32;
+  for (int p = 0; p < np; ++p) {
     const int c0 = 32 * p;
     if (wid == 0) factor_diag32(Ms, Zs, c0, M, T.flags, lane);
     __syncthreads();
     // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
-    if (wid < kNb / 32 - 1 - p) {
+    if (wid < np - 1 - p) {
       const int q = p + 1 + wid;
       f32x16 acc = {};
       mma_nt(acc, Ms, 32 * q, c0, Zs, c0, c0, 1.f, lane);
@@ -414,7 +418,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
     }
     __syncthreads();
     // trailing lower tiles (ib, jb), p < jb <= ib: M_ij -= L_ip L_jp^T
-    const int nr = kNb / 32 - 1 - p;
+    const int nr = np - 1 - p;
     for (int t = wid; t < nr * (nr + 1) / 2; t += 4) {
       int ib = 0, u = t;
       while (u > ib) { u -= ib + 1; ++ib; }
@@ -428,7 +432,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   }
 
   // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj
-  for (int i = 1; i < kNb / 32; ++i) {
+  for (int i = 1; i < np; ++i) {
     if (wid < i) {
       const int j = wid;
       f32x16 acc = {};
@@ -886,14 +890,14 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   r = side_stream(&side);
   if (r != KFAC_OK) return r;
   hipStream_t ss = side->s;
-  auto diag_step = [&](int k) -> kfac_status_t {
+  auto diag_step = [&](int k, hipStream_t ds) -> kfac_status_t {
     DiagTab D{};
     D.k = k;
     D.flags = flags;
     for (size_t mi = 0; mi <= mats.size(); ++mi) {
       if (mi == mats.size() || D.n == kMaxDiagMats) {
         if (D.n > 0) {
-          hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, ss, D);
+          hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, ds, D);
           KFAC_HIP_TRY(hipGetLastError());
         }
         D.n = 0;
@@ -1093,6 +1097,15 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     }
     return launch_sym_reduce(out, fs);
   };
+  if (nblk_max == 1) {
+    // every factor is one diagonal block: no chain to overlap, so the same
+    // launches run in order on the caller's stream (no fork, no events)
+    r = diag_step(0, st);
+    if (r != KFAC_OK) return r;
+    std::vector<const FullPlan::Group*> all;
+    for (const FullPlan::Group& g : P.groups) all.push_back(&g);
+    return finish(all, st);
+  }
   hipStream_t fs = side->f;
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
   KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
@@ -1118,7 +1131,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       }
     }
     for (int k = k0; k < k1 && k < nblk_max; ++k) {
-      r = diag_step(k);
+      r = diag_step(k, ss);
       if (r != KFAC_OK) return r;
       r = panel_step(k);
       if (r != KFAC_OK) return r;

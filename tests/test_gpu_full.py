@@ -106,19 +106,21 @@ def test_sgd_reduction_update_phase(gpu_lib, d_in):
         assert max_rel(got["mom_w"], v[:, :-1]) <= 1e-5 and max_rel(got["mom_b"], v[:, -1]) <= 1e-5
 
 
-def test_not_pd_keeps_inverse(gpu_lib):
+@pytest.mark.parametrize("d_in,d_out,bad", [(200, 140, 150), (100, 40, 50)])
+def test_not_pd_keeps_inverse(gpu_lib, d_in, d_out, bad):
     """A factor with a negative eigenvalue (EMA decay 1 keeps it) fails the
     Cholesky: KFAC_FLAG_NOT_PD is raised and that inverse is left unchanged,
-    while the positive definite G is still inverted."""
+    while the positive definite G is still inverted; with multi-block factors
+    and with factors of one diagonal block (the single-stream schedule)."""
     import torch
     from second_order_optimizer_amd import FLAG_NOT_PD, PHASE_FACTORS, PHASE_INVERT
     from second_order_optimizer_amd.stack import KfacStack
-    cfg = with_layers(synth.full_config("fc64"), [synth.linear("fc", 200, 140, 16, bias=True)])
+    cfg = with_layers(synth.full_config("fc64"), [synth.linear("fc", d_in, d_out, 16, bias=True)])
     L = cfg.layers[0]
     st = KfacStack(cfg.layers, "full")
     s0 = synth.initial_state(cfg, 0)
     A = np.eye(L.d_a, dtype=np.float32)
-    A[150, 150] = -10 * cfg.damping
+    A[bad, bad] = -10 * cfg.damping
     s0["A"] = A
     s0["A_inv"] = np.full((L.d_a, L.d_a), 7.0, np.float32)
     st.set_state(0, s0)
