@@ -258,11 +258,12 @@ def measured_traffic():
 
 def traffic_probe(args):
     """What the FETCH_SIZE / WRITE_SIZE passes profile: a plain 1 GiB device
-    copy (calibration of the counters) and `--steps` FACTORS-only diagonal
-    calls on ResNet-18 @ 128 (each one launch of diag_colsq_kernel)."""
+    copy (calibration of the counters), then `--steps` FACTORS-only diagonal
+    calls on ResNet-18 @ 128 (each one launch of diag_colsq_kernel) and
+    `--steps` UPDATE-only calls (diag_finish_kernel, diag_update_kernel)."""
     import torch
     import synth
-    from second_order_optimizer_amd import PHASE_FACTORS
+    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_UPDATE
     from second_order_optimizer_amd.stack import KfacStack
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -279,8 +280,12 @@ def traffic_probe(args):
     for _ in range(args.steps):
         st.step(H)
     torch.cuda.synchronize()
+    Hu = st.hparams(synth.hparams(cfg), phase_mask=PHASE_UPDATE)
+    for _ in range(args.steps):
+        st.step(Hu)
+    torch.cuda.synchronize()
     print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES, "factor_calls": args.steps,
-                      "diag_src_sha256": source_sha256(DIAG_SRC)}), flush=True)
+                      "update_calls": args.steps, "diag_src_sha256": source_sha256(DIAG_SRC)}), flush=True)
 
 
 def run_diag(cfg, args):
