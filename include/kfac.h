@@ -44,7 +44,9 @@
  *    non-finite parameter) is reported through device flags, never through a
  *    return code, because it is only known once the kernels have run.
  *  - Calls on different workspaces and streams may be made from different
- *    host threads.
+ *    host threads.  Full-method calls on one device share the library's side
+ *    streams there, so they are enqueued one at a time (an internal lock);
+ *    their GPU work on those streams then runs in call order.
  */
 #ifndef KFAC_H
 #define KFAC_H

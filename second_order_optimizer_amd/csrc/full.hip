@@ -10,6 +10,7 @@
 //             weight-decay / parameter write fused into the second GEMM's
 //             epilogue.
 #include <algorithm>
+#include <deque>
 #include <mutex>
 #include <vector>
 
@@ -824,7 +825,7 @@ struct SideStream {
 
 kfac_status_t side_stream(SideStream** out) {
   static std::mutex mu;
-  static std::vector<SideStream> per_device;
+  static std::deque<SideStream> per_device;   // growing keeps the addresses of existing entries
   int dev = 0;
   KFAC_HIP_TRY(hipGetDevice(&dev));
   std::lock_guard<std::mutex> lock(mu);
@@ -1294,6 +1295,21 @@ kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
                            hipStream_t st, int phases) {
   FullPlan P = plan_full(layers, n, ws, phases, hp.refresh != 0);
   if (P.ws_bytes > ws_bytes) return KFAC_ERR_WORKSPACE;
+  // The side streams and their events are shared by every call on a device:
+  // a whole step is enqueued under the device's lock, so that each of its
+  // event waits names this call's own record (the streams then keep calls
+  // from different host threads in order).
+  static std::deque<std::mutex> dev_mu;   // growing keeps existing mutexes in place
+  static std::mutex table_mu;
+  int dev = 0;
+  KFAC_HIP_TRY(hipGetDevice(&dev));
+  std::mutex* mu;
+  {
+    std::lock_guard<std::mutex> t(table_mu);
+    while (dev_mu.size() <= static_cast<size_t>(dev)) dev_mu.emplace_back();
+    mu = &dev_mu[dev];
+  }
+  std::lock_guard<std::mutex> lock(*mu);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
   kfac_status_t r;
   if (phases & KFAC_PHASE_FACTORS) {

@@ -335,3 +335,49 @@ def test_bf16_factor_xcd_runs(gpu_lib):
     L = synth.mlp_layers(5, 1024, 768, 64)
     cfg = with_layers(synth.small_config("mlp24_bf16"), L, steps=2, refresh_every=1)
     lockstep(cfg, cfg.steps, TOL16, FULL_KEYS)
+
+
+def test_full_steps_from_two_threads(gpu_lib):
+    """Two host threads each run three full steps (factors, inverse on the
+    library's side streams, update) on their own stack and stream at the same
+    time on one device; the results equal the same steps run one thread after
+    the other, bitwise."""
+    import threading
+    import torch
+    from second_order_optimizer_amd.stack import KfacStack
+    base = synth.small_config("resnet50_kfac")
+    cfg = with_layers(base, list(base.layers) + [synth.linear("fc_split", 256, 96, 32, bias=True)])
+    H = KfacStack.hparams(synth.hparams(cfg), refresh=True)
+
+    def make(seed_step):
+        st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype)
+        for li in range(len(cfg.layers)):
+            st.set_state(li, synth.initial_state(cfg, li))
+            st.set_inputs(li, synth.step_inputs(cfg, seed_step, li))
+        return st
+
+    def run(st, stream):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                st.step(H, stream=stream)
+
+    ref = [make(1), make(2)]
+    s0 = torch.cuda.Stream()
+    for st in ref:
+        run(st, s0)
+        torch.cuda.synchronize()
+    par = [make(1), make(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=run, args=(par[i], streams[i])) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for a_st, b_st in zip(ref, par):
+        assert a_st.flags() == 0 and b_st.flags() == 0
+        for li in range(len(cfg.layers)):
+            a, b = a_st.get_state(li), b_st.get_state(li)
+            for k in a:
+                assert np.array_equal(a[k], b[k]), (cfg.layers[li].name, k)
