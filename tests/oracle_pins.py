@@ -137,6 +137,96 @@ def pin_conv_rows(O, seed=4) -> bool:
     return grows.shape == (B * Ho * Wo, Co) and np.allclose(gw, ref.reshape(Co, -1), rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# single columns (the full-size checks build single factor entries from them)
+
+# (B, C, H, W, k, stride, pad): kernel sizes 1, 2, 3 and 7, strides 1-3, and
+# paddings up to 3, beyond half the kernel (taps that lie wholly in the padding
+# for the first and last output rows)
+COLUMN_GEOMS = [(2, 3, 5, 6, 1, 2, 1), (2, 2, 5, 5, 2, 1, 3), (1, 2, 7, 6, 3, 3, 2), (2, 2, 6, 5, 3, 1, 0),
+                (1, 2, 9, 8, 7, 2, 3), (2, 1, 4, 4, 7, 1, 3), (1, 3, 8, 7, 3, 2, 3)]
+
+
+def pin_unfold_column_library(O, seed=14) -> bool:
+    """Every column of unfold_column equals that column of the library im2col
+    (torch unfold, float64 CPU) and of the conv loops' input index
+    x[b, c, ho s - p + kh, wo s - p + kw] (zero outside the image), bit for bit,
+    for fp32 inputs."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for (B, C, H, W, k, s, p) in COLUMN_GEOMS:
+        x = rng.standard_normal((B, C, H, W)).astype(np.float32)
+        ref = torch.nn.functional.unfold(torch.from_numpy(x.astype(np.float64)), k, padding=p, stride=s)
+        ref = ref.permute(0, 2, 1).reshape(-1, C * k * k).numpy()
+        Ho, Wo = (H + 2 * p - k) // s + 1, (W + 2 * p - k) // s + 1
+        for j in range(C * k * k):
+            col = O.unfold_column(x, k, s, p, j)
+            ok &= col.dtype == np.float64 and col.shape == (B * Ho * Wo,) and np.array_equal(col, ref[:, j])
+        # one column by the index formula, written as loops
+        j = rng.integers(0, C * k * k)
+        c, kh, kw = j // (k * k), (j // k) % k, j % k
+        loop = np.zeros(B * Ho * Wo)
+        for b, ho, wo in itertools.product(range(B), range(Ho), range(Wo)):
+            hi, wi = ho * s - p + kh, wo * s - p + kw
+            if 0 <= hi < H and 0 <= wi < W:
+                loop[(b * Ho + ho) * Wo + wo] = x[b, c, hi, wi]
+        ok &= np.array_equal(O.unfold_column(x, k, s, p, j), loop)
+    return bool(ok)
+
+
+def pin_layer_columns(O, seed=15) -> bool:
+    """activation_column / gradient_column give exactly the columns of the rows
+    the factors are built from: the conv input's unfold (torch im2col) with the
+    constant-1 bias column last, and the output gradient with one row per
+    (sample, output position) by explicit loops; linear layers' columns of a
+    and g (fp32 and bf16 bit patterns) and the bias column of ones."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for (B, C, H, W, k, s, p), bias in zip(COLUMN_GEOMS, (True, False, True, True, False, True, False)):
+        geo = Geo("conv", bias, k, s, p)
+        Ho, Wo = (H + 2 * p - k) // s + 1, (W + 2 * p - k) // s + 1
+        Co = 3
+        x = rng.standard_normal((B, C, H, W)).astype(np.float32)
+        g = rng.standard_normal((B, Co, Ho, Wo)).astype(np.float32)
+        U = torch.nn.functional.unfold(torch.from_numpy(x.astype(np.float64)), k, padding=p, stride=s)
+        U = U.permute(0, 2, 1).reshape(-1, C * k * k).numpy()
+        d_in = C * k * k
+        for j in range(d_in + int(bias)):
+            ref = U[:, j] if j < d_in else np.ones(B * Ho * Wo)
+            ok &= np.array_equal(O.activation_column(_ColGeo(geo, d_in), x, j), ref)
+        for o in range(Co):
+            ref = np.zeros(B * Ho * Wo)
+            for b, ho, wo in itertools.product(range(B), range(Ho), range(Wo)):
+                ref[(b * Ho + ho) * Wo + wo] = g[b, o, ho, wo]
+            ok &= np.array_equal(O.gradient_column(geo, g, o), ref)
+    for bias, bf16 in ((True, False), (False, False), (True, True)):
+        N, d_in, d_out = 9, 5, 4
+        a = rng.standard_normal((N, d_in)).astype(np.float32)
+        g = rng.standard_normal((N, d_out)).astype(np.float32)
+        if bf16:   # truncated bf16 patterns: their float32 value is the pattern shifted up 16 bits
+            a = (a.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+            g = (g.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+            af = (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+            gf = (g.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+        else:
+            af, gf = a.astype(np.float64), g.astype(np.float64)
+        geo = _ColGeo(Geo("linear", bias), d_in)
+        for j in range(d_in + int(bias)):
+            ref = af[:, j] if j < d_in else np.ones(N)
+            ok &= np.array_equal(O.activation_column(geo, a, j), ref)
+        for o in range(d_out):
+            ok &= np.array_equal(O.gradient_column(geo, g, o), gf[:, o])
+    return bool(ok)
+
+
+class _ColGeo(Geo):
+    """Geo plus the unfolded input width (the column helpers need d_in)."""
+
+    def __init__(self, geo, d_in):
+        super().__init__(geo.kind, geo.has_bias, geo.k, geo.stride, geo.pad)
+        self.d_in = d_in
+
+
 def pin_bf16_widen(O) -> bool:
     """bf16 patterns widen to the float32 whose upper half they are."""
     bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x3E00, 0x7F7F], np.uint16)
@@ -469,7 +559,7 @@ def pin_full_step_exact_rational(O) -> bool:
 
 
 ALL_PINS = [pin_full_step_exact_rational, pin_unfold_direct_conv, pin_unfold_library, pin_factor_outer_products, pin_factor_hadamard,
-            pin_bias_column, pin_conv_rows, pin_bf16_widen, pin_ema_closed_form,
+            pin_bias_column, pin_conv_rows, pin_unfold_column_library, pin_layer_columns, pin_bf16_widen, pin_ema_closed_form,
             pin_inverse_sherman_morrison, pin_inverse_diagonal_and_residual, pin_inverse_not_pd_raises,
             pin_kronecker_identity, pin_full_step_hadamard, pin_sgd_reduction,
             pin_momentum_constant_direction, pin_diag_is_factor_diagonal, pin_diag_conv_window_sums,

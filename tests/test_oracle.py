@@ -117,10 +117,38 @@ def _mut_widen_low_half(M):
                          if np.asarray(x).dtype == np.uint16 else np.asarray(x).astype(np.float64))
 
 
+def _mut_unfold_column_kh_kw(M):
+    def unfold_column(x, k, stride, pad, j):
+        c, kw, kh = j // (k * k), (j // k) % k, j % k     # kernel row and column swapped
+        return M.unfold_column.__wrapped__(x, k, stride, pad, (c * k + kh) * k + kw)
+    unfold_column.__wrapped__ = M.unfold_column
+    M.unfold_column = unfold_column
+
+
+def _mut_gradient_column_order(M):
+    orig = M.gradient_column
+
+    def gradient_column(layer, g, o):
+        if layer.kind == "conv":
+            return M.widen(np.asarray(g)[:, o].transpose(0, 2, 1)).reshape(-1)   # positions column-major
+        return orig(layer, g, o)
+    M.gradient_column = gradient_column
+
+
+def _mut_activation_column_bias(M):
+    orig = M.activation_column
+
+    def activation_column(layer, a, j):
+        col = orig(layer, a, j)
+        return col * 0.0 if (layer.has_bias and j == layer.d_in) else col
+    M.activation_column = activation_column
+
+
 MUTANTS = [_mut_unfold_order, _mut_unfold_no_pad_shift, _mut_factor_norm, _mut_factor_transpose,
            _mut_ema_swap, _mut_inverse_no_damping, _mut_inverse_wrong_product, _mut_precond_drop_A,
            _mut_precond_squared, _mut_wd_sign, _mut_dampening, _mut_nesterov, _mut_bias_first,
-           _mut_diag_abs, _mut_widen_low_half]
+           _mut_diag_abs, _mut_widen_low_half, _mut_unfold_column_kh_kw,
+           _mut_gradient_column_order, _mut_activation_column_bias]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
