@@ -38,15 +38,27 @@
  *    caller once before first use (the library never clears it on its own).
  *  - `stream` is a hipStream_t (NULL = the default stream).  The step entry
  *    points only enqueue work on it and return; they never synchronise.
- *  - Arguments are validated on the host before anything is enqueued: on any
- *    error status no kernel runs and no buffer is touched.
+ *  - Arguments are validated on the host before anything is enqueued: on a
+ *    validation error (KFAC_ERR_ARG, _DTYPE, _ALIGN, _WORKSPACE,
+ *    _UNSUPPORTED) no kernel runs and no buffer is touched.  KFAC_ERR_HIP
+ *    means a HIP call failed while the step was being enqueued: part of the
+ *    step may have been enqueued (the library's side streams are still joined
+ *    back into `stream` before the call returns), so the buffers are then in
+ *    an unspecified state.
  *  - Numerical trouble (a damped factor that is not positive definite, a
  *    non-finite parameter) is reported through device flags, never through a
  *    return code, because it is only known once the kernels have run.
  *  - Calls on different workspaces and streams may be made from different
- *    host threads.  Full-method calls on one device share the library's side
- *    streams there, so they are enqueued one at a time (an internal lock);
- *    their GPU work on those streams then runs in call order.
+ *    host threads.  A full-method step forks work onto two side streams of
+ *    the library and joins it back into `stream`; those side streams belong
+ *    to the pair (device, `stream`): they are created at the first full step
+ *    on that stream and kept until the process ends, and calls on the same
+ *    stream are enqueued one at a time (an internal lock).  Steps on other
+ *    streams never use them, so a step captured into a graph on one stream
+ *    and steps run on other streams meanwhile stay apart.  The first full
+ *    step on a stream must not be made while that stream is capturing (the
+ *    side streams and events cannot be created then): it returns
+ *    KFAC_ERR_UNSUPPORTED.
  */
 #ifndef KFAC_H
 #define KFAC_H
@@ -80,11 +92,11 @@ enum { KFAC_MODE_FULL = 0, KFAC_MODE_DIAG = 1 };
 /* kfac_hparams_t.phase_mask bits; 0 means all phases.
  *   full: FACTORS = factor construction + EMA, INVERT = damped inverses
  *         (only when refresh != 0), UPDATE = precondition + momentum/decay/write
- *   diag: FACTORS = the streaming reduction of a and g (sums of squares) into
- *         the workspace; UPDATE = dA/dG formed from that reduction (written to
- *         the descriptor's dA/dG) followed by the fused elementwise step.  An
- *         UPDATE-only call reads the reduction the last FACTORS call on the
- *         same workspace and layers left there. */
+ *   diag: FACTORS = dA, dG of this batch (a streaming reduction of a and g
+ *         through the workspace), written to the descriptor's dA / dG for
+ *         every layer kind; UPDATE = the fused elementwise step, which reads
+ *         dA / dG from those buffers (so an UPDATE-only call uses whatever
+ *         they hold, e.g. the last FACTORS call's result). */
 enum { KFAC_PHASE_FACTORS = 1, KFAC_PHASE_INVERT = 2, KFAC_PHASE_UPDATE = 4, KFAC_PHASE_ALL = 7 };
 /* sticky device flags */
 enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
@@ -98,6 +110,8 @@ enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
  *            width), rows = batch * h_out * w_out; dilation 1, groups 1.
  *   d_a = d_in + (has_bias ? 1 : 0)   (the bias acts as a constant-1 input,
  *                                      appended as the last column)
+ *   Full method: a layer with float32 a or g, and every conv2d layer, has at
+ *   most INT32_MAX rows (KFAC_ERR_UNSUPPORTED otherwise).
  *   grad_w, w, mom_w, F_w : [d_out, d_in] float32
  *   grad_b, b, mom_b, F_b : [d_out] float32, NULL iff has_bias == 0
  * Full method:  A, A_inv : [d_a, d_a]; G, G_inv : [d_out, d_out]  (float32,
@@ -170,10 +184,9 @@ kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const
                              void* workspace, size_t ws_bytes, void* stream);
 
 /* Enqueue one diagonal step for all layers on `stream`:
- *   [FACTORS] sums of squares of a and g down their rows, into the workspace
- *   [UPDATE]  dA[j] = mean_n a_bar[n, j]^2 (conv: over the unfolded rows,
- *             which are never materialised), dG[o] = mean_n g[n, o]^2; then in
- *             one pass F = beta F + (1 - beta) dG[o] dA[j];
+ *   [FACTORS] dA[j] = mean_n a_bar[n, j]^2 (conv: over the unfolded rows,
+ *             which are never materialised), dG[o] = mean_n g[n, o]^2
+ *   [UPDATE]  in one pass F = beta F + (1 - beta) dG[o] dA[j];
  *             P = grad / (F + damping); D = P + wd W; V = mu V + D; W = W - lr V */
 kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                              void* workspace, size_t ws_bytes, void* stream);

@@ -61,6 +61,12 @@ kfac_status_t check_shape(const kfac_layer_t& L, int mode) {
     // the diagonal reduction streams float32 inputs
     if (L.act_dtype != KFAC_F32 || L.grad_dtype != KFAC_F32) return KFAC_ERR_DTYPE;
   }
+  if (mode == KFAC_MODE_FULL) {
+    // the fp32 factor contractions (and the conv row layout) count rows in
+    // 32 bits; bf16 factors are split into row chunks and have no such limit
+    const bool fp32_rows = L.kind == KFAC_CONV2D || L.act_dtype == KFAC_F32 || L.grad_dtype == KFAC_F32;
+    if (fp32_rows && L.rows > INT32_MAX) return KFAC_ERR_UNSUPPORTED;
+  }
   return KFAC_OK;
 }
 

@@ -4,8 +4,9 @@
 // (CAFIN briefing, "Introduction" and "Kernel Fusion Strategy").
 //
 // Three launches per step, all HBM-streaming.  The FACTORS phase is the first
-// (the streaming reduction, into the workspace); the UPDATE phase is the other
-// two (dA / dG from the reduction, then the parameter pass).
+// two (the streaming reduction into the workspace, then dA / dG from it,
+// written to the descriptor's buffers for every layer kind); the UPDATE phase
+// is the parameter pass, which reads dA / dG from those buffers.
 //   diag_colsq_kernel   sum of squares down the rows of row-major matrices.
 //                       Every reduction of the step is one of these: linear
 //                       a [N, d_in] and g [N, d_out] give dA / dG directly; a
@@ -581,8 +582,6 @@ kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
       hipLaunchKernelGGL(diag_colsq_kernel, dim3(blocks), dim3(kColThreads), 0, stream, T);
       KFAC_HIP_TRY(hipGetLastError());
     }
-  }
-  if (phases & KFAC_PHASE_UPDATE) {
     for (size_t g0 = 0; g0 < P.fin.size(); g0 += kMaxFinTasks) {
       const size_t g1 = std::min(P.fin.size(), g0 + kMaxFinTasks);
       FinTasks T{};
@@ -597,6 +596,8 @@ kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
       hipLaunchKernelGGL(diag_finish_kernel, dim3(blocks), dim3(kFinThreads), 0, stream, T);
       KFAC_HIP_TRY(hipGetLastError());
     }
+  }
+  if (phases & KFAC_PHASE_UPDATE) {
     for (size_t g0 = 0; g0 < P.seg.size(); g0 += kMaxSegs) {
       const size_t g1 = std::min(P.seg.size(), g0 + kMaxSegs);
       Segs S{};

@@ -1,8 +1,9 @@
 // Full K-FAC step (Osawa et al., section 3.2): per layer
 //   [FACTORS] A <- eps A + (1 - eps) a_bar^T a_bar / N, G likewise (SYRK on
 //             matrix cores, EMA fused into the epilogue, upper tiles mirrored;
-//             convolution rows are gathered im2col-style inside the GEMM
-//             loader, never materialised)
+//             fp32 convolution tensors are first laid out as rows, im2col of
+//             the input and a transpose of the output gradient, in one
+//             batched launch, and then take the same row-major SYRK)
 //   [INVERT]  (A + lambda I)^-1, (G + lambda I)^-1 by a blocked Cholesky
 //             factorisation, a blocked triangular inverse and Z^T Z, batched
 //             over all factors of the stack (section 4.2: damping)
@@ -10,8 +11,10 @@
 //             weight-decay / parameter write fused into the second GEMM's
 //             epilogue.
 #include <algorithm>
-#include <deque>
+#include <map>
+#include <memory>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -814,35 +817,61 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
   return reds.empty() ? KFAC_OK : launch_sym_reduce(reds, st);
 }
 
-// A second stream per device for the Cholesky look-ahead, with its events
-// (default priority; created on first use and kept for the process).
+// The library's side streams for one caller stream on one device: the
+// Cholesky chain (s) and the assembly of finished inverses (f), with their
+// events, at default priority, created at the first full step on that caller
+// stream and kept for the process.  Keying them by the caller's stream keeps
+// a step captured into a graph from pulling another stream's work into the
+// capture: the capture reaches only the side streams of the captured stream,
+// while steps on other streams (other host threads) run on their own.  A
+// whole step is enqueued under the set's lock, so that every event wait names
+// the record of the same call even when several host threads share a caller
+// stream.
 struct SideStream {
+  std::mutex mu;
   hipStream_t s = nullptr;   // Cholesky inner chain
   hipStream_t f = nullptr;   // inverse assembly of factors whose Cholesky is complete
   hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, main_done[2] = {nullptr, nullptr},
              side_done[2] = {nullptr, nullptr}, ufork = nullptr, ujoin = nullptr;
 };
 
-kfac_status_t side_stream(SideStream** out) {
+kfac_status_t side_streams_for(hipStream_t caller, SideStream** out) {
   static std::mutex mu;
-  static std::deque<SideStream> per_device;   // growing keeps the addresses of existing entries
+  static std::map<std::pair<int, uintptr_t>, std::unique_ptr<SideStream>> sets;
   int dev = 0;
   KFAC_HIP_TRY(hipGetDevice(&dev));
   std::lock_guard<std::mutex> lock(mu);
-  if (per_device.size() <= static_cast<size_t>(dev)) per_device.resize(dev + 1);
-  SideStream& S = per_device[dev];
-  if (!S.s) {
-    KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.s, hipStreamNonBlocking));
-    KFAC_HIP_TRY(hipStreamCreateWithFlags(&S.f, hipStreamNonBlocking));
-    hipEvent_t* evs[9] = {&S.fork,          &S.join,          &S.fjoin, &S.main_done[0], &S.main_done[1],
-                          &S.side_done[0], &S.side_done[1], &S.ufork, &S.ujoin};
-    for (hipEvent_t* e : evs) KFAC_HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming));
+  std::unique_ptr<SideStream>& slot = sets[{dev, reinterpret_cast<uintptr_t>(caller)}];
+  if (!slot) {
+    // streams and events are not created inside an open capture: the first
+    // full step on a stream has to run outside one
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      sets.erase({dev, reinterpret_cast<uintptr_t>(caller)});
+      return KFAC_ERR_UNSUPPORTED;
+    }
+    auto S = std::make_unique<SideStream>();
+    bool ok = hipStreamCreateWithFlags(&S->s, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&S->f, hipStreamNonBlocking) == hipSuccess;
+    hipEvent_t* evs[9] = {&S->fork,          &S->join,          &S->fjoin, &S->main_done[0], &S->main_done[1],
+                          &S->side_done[0], &S->side_done[1], &S->ufork, &S->ujoin};
+    for (hipEvent_t* e : evs) ok = ok && hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      for (hipEvent_t* e : evs)
+        if (*e) (void)hipEventDestroy(*e);
+      if (S->s) (void)hipStreamDestroy(S->s);
+      if (S->f) (void)hipStreamDestroy(S->f);
+      sets.erase({dev, reinterpret_cast<uintptr_t>(caller)});
+      return KFAC_ERR_HIP;
+    }
+    slot = std::move(S);
   }
-  *out = &S;
+  *out = slot.get();
   return KFAC_OK;
 }
 
-kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st) {
+kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st,
+                           SideStream* side) {
   const std::vector<Mat>& mats = P.mats;
   int nblk_max = 0, d_max = 0;
   for (const Mat& m : mats) {
@@ -887,9 +916,6 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   // direction so that each wait names the right step; the second stream forks
   // from and joins the caller's stream, which keeps the whole step
   // capturable in a graph.
-  SideStream* side = nullptr;
-  r = side_stream(&side);
-  if (r != KFAC_OK) return r;
   hipStream_t ss = side->s;
   auto diag_step = [&](int k, hipStream_t ds) -> kfac_status_t {
     DiagTab D{};
@@ -1109,9 +1135,14 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   }
   hipStream_t fs = side->f;
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
+  const int nouter = (nblk_max + kOuter - 1) / kOuter;
+  // everything between the fork and the join; an error inside still reaches
+  // the join below, so the caller's stream never runs ahead of work already
+  // enqueued on the side streams (and an open capture stays joined)
+  auto chain = [&]() -> kfac_status_t {
   KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
   KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->fork, 0));
-  const int nouter = (nblk_max + kOuter - 1) / kOuter;
+  kfac_status_t r;
   for (int K = 0; K < nouter; ++K) {
     const int k0 = K * kOuter, k1 = k0 + kOuter;   // blocks of outer panel K
     // second stream: F_next(K - 1) after F_rest(K - 2), then the inner steps
@@ -1178,16 +1209,18 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
     }
   }
-  // join: everything on the second stream before anything after it here
-  KFAC_HIP_TRY(hipEventRecord(side->join, ss));
-  KFAC_HIP_TRY(hipStreamWaitEvent(st, side->join, 0));
-  KFAC_HIP_TRY(hipEventRecord(side->fjoin, fs));
-  KFAC_HIP_TRY(hipStreamWaitEvent(st, side->fjoin, 0));
   return KFAC_OK;
+  };
+  r = chain();
+  // join: everything on the side streams before anything after it here
+  const bool joined = hipEventRecord(side->join, ss) == hipSuccess && hipStreamWaitEvent(st, side->join, 0) == hipSuccess &&
+                      hipEventRecord(side->fjoin, fs) == hipSuccess && hipStreamWaitEvent(st, side->fjoin, 0) == hipSuccess;
+  if (r != KFAC_OK) return r;
+  return joined ? KFAC_OK : KFAC_ERR_HIP;
 }
 
 kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
-                           uint32_t* flags, hipStream_t st) {
+                           uint32_t* flags, hipStream_t st, SideStream* side) {
   std::vector<GemmProb> g1, g2;
   std::vector<BcProb> b0, b1;
   auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
@@ -1264,25 +1297,20 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
   // The bias-column products (HBM-bound) run on the side stream beside the
   // two GEMMs (MFMA-bound): they read what the GEMMs read and write only t,
   // b and mom_b, which the GEMMs do not touch.
-  kfac_status_t r;
-  SideStream* side = nullptr;
-  if (!b0.empty()) {
-    r = side_stream(&side);
-    if (r != KFAC_OK) return r;
-    KFAC_HIP_TRY(hipEventRecord(side->ufork, st));
-    KFAC_HIP_TRY(hipStreamWaitEvent(side->s, side->ufork, 0));
-    r = launch_bias_col(b0, 0, hp, flags, side->s);
-    if (r != KFAC_OK) return r;
-    r = launch_bias_col(b1, 1, hp, flags, side->s);
-    if (r != KFAC_OK) return r;
-    KFAC_HIP_TRY(hipEventRecord(side->ujoin, side->s));
+  const bool fork = !b0.empty();
+  if (fork) KFAC_HIP_TRY(hipEventRecord(side->ufork, st));
+  kfac_status_t r = KFAC_OK;
+  if (fork) {
+    if (hipStreamWaitEvent(side->s, side->ufork, 0) != hipSuccess) r = KFAC_ERR_HIP;
+    if (r == KFAC_OK) r = launch_bias_col(b0, 0, hp, flags, side->s);
+    if (r == KFAC_OK) r = launch_bias_col(b1, 1, hp, flags, side->s);
   }
-  r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
-  if (r != KFAC_OK) return r;
-  r = launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
-  if (r != KFAC_OK) return r;
-  if (side) KFAC_HIP_TRY(hipStreamWaitEvent(st, side->ujoin, 0));
-  return KFAC_OK;
+  if (r == KFAC_OK) r = launch_gemm(g1, OP_K, OP_MN, EPI_STORE, sc, st);
+  if (r == KFAC_OK) r = launch_gemm(g2, OP_MN, OP_MN, EPI_UPDATE, sc, st);
+  // the join is enqueued after an error too (see invert_phase)
+  if (fork && (hipEventRecord(side->ujoin, side->s) != hipSuccess || hipStreamWaitEvent(st, side->ujoin, 0) != hipSuccess))
+    return r != KFAC_OK ? r : KFAC_ERR_HIP;
+  return r;
 }
 
 }  // namespace
@@ -1295,33 +1323,21 @@ kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
                            hipStream_t st, int phases) {
   FullPlan P = plan_full(layers, n, ws, phases, hp.refresh != 0);
   if (P.ws_bytes > ws_bytes) return KFAC_ERR_WORKSPACE;
-  // The side streams and their events are shared by every call on a device:
-  // a whole step is enqueued under the device's lock, so that each of its
-  // event waits names this call's own record (the streams then keep calls
-  // from different host threads in order).
-  static std::deque<std::mutex> dev_mu;   // growing keeps existing mutexes in place
-  static std::mutex table_mu;
-  int dev = 0;
-  KFAC_HIP_TRY(hipGetDevice(&dev));
-  std::mutex* mu;
-  {
-    std::lock_guard<std::mutex> t(table_mu);
-    while (dev_mu.size() <= static_cast<size_t>(dev)) dev_mu.emplace_back();
-    mu = &dev_mu[dev];
-  }
-  std::lock_guard<std::mutex> lock(*mu);
+  SideStream* side = nullptr;
+  kfac_status_t r = side_streams_for(st, &side);
+  if (r != KFAC_OK) return r;
+  std::lock_guard<std::mutex> lock(side->mu);
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
-  kfac_status_t r;
   if (phases & KFAC_PHASE_FACTORS) {
     r = factors_phase(layers, n, hp, P, st);
     if (r != KFAC_OK) return r;
   }
   if ((phases & KFAC_PHASE_INVERT) && hp.refresh) {
-    r = invert_phase(hp, P, flags, st);
+    r = invert_phase(hp, P, flags, st, side);
     if (r != KFAC_OK) return r;
   }
   if (phases & KFAC_PHASE_UPDATE) {
-    r = update_phase(layers, n, hp, P, flags, st);
+    r = update_phase(layers, n, hp, P, flags, st, side);
     if (r != KFAC_OK) return r;
   }
   return KFAC_OK;

@@ -175,3 +175,15 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(FileNotFoundError):
         K.load()
+
+
+def test_row_count_limits(lib):
+    """fp32 factors of the full method count rows in 32 bits: more rows than
+    INT32_MAX is rejected (not truncated); bf16 factors run in row chunks and
+    the diagonal method counts rows in 64 bits, so both accept such a layer."""
+    big = (1 << 31) + 5
+    assert _ws_status([_linear(rows=big)], K.MODE_FULL)[0] == K.KFAC_ERR_UNSUPPORTED
+    assert _ws_status([_linear(rows=big, act_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_ERR_UNSUPPORTED
+    assert _ws_status([_linear(rows=big, act_dtype=K.BF16, grad_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_OK
+    assert _ws_status([_linear(rows=(1 << 31) - 1)], K.MODE_FULL)[0] == K.KFAC_OK
+    assert _ws_status([_linear(rows=big)], K.MODE_DIAG)[0] == K.KFAC_OK

@@ -294,10 +294,12 @@ def test_graph_replays_match_eager(gpu_lib):
 
     eager, graphed = make(), make()
     warm = make()
-    warm.step(H)              # the library's side streams and events exist before the capture
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        warm.step(H)          # the capture stream's side streams and events exist before the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=cs):
         graphed.step(H)
     torch.cuda.synchronize()
     for rep in range(3):
