@@ -113,64 +113,81 @@ def test_diag_nonfinite_flag(gpu_lib):
     assert st.flags() == 0
 
 
-def test_diag_resnet18_full_size_sampled(gpu_lib):
+def test_diag_resnet18_full_size_trajectory(gpu_lib):
     """ResNet-18 at batch 128, 224x224 (11,679,912 weights), in the launch
-    configuration the benchmark times; one step from the synthetic state,
-    checked on sampled dA / dG entries and sampled parameters per layer."""
+    configuration the benchmark times: 100 free-running steps over two
+    pre-drawn input batches (odd steps the first, even steps the second).
+    Per layer, sampled output rows o and input columns j (the bias column
+    included): dA[j] and dG[o] of both batches from the oracle's own columns,
+    and the oracle's diagonal step run for 100 steps on those entries alone
+    (the entries of a diagonal step do not interact), compared with the
+    library's F, V and W after step 1 and step 100, and its dA, dG."""
     import torch
     from second_order_optimizer_amd.stack import KfacStack
     cfg = synth.full_config("resnet18_diag")
     hp = synth.hparams(cfg)
-    st = KfacStack(cfg.layers, "diag")
-    inputs = []
+    st = KfacStack(cfg.layers, "diag", pool=2)
+    inputs = [[], []]
     for li in range(len(cfg.layers)):
         st.set_state(li, synth.initial_state(cfg, li))
-        inp = synth.step_inputs(cfg, 1, li)
-        st.set_inputs(li, inp)
-        inputs.append(inp)
-    say("resnet18 full-size inputs loaded")
-    st.step(st.hparams(hp))
-    torch.cuda.synchronize()
-    assert st.flags() == 0
+    for slot in range(2):
+        for li in range(len(cfg.layers)):
+            inp = synth.step_inputs(cfg, slot + 1, li)
+            st.set_inputs(li, inp, slot=slot)
+            inputs[slot].append(inp)
+        say(f"resnet18 full-size input batch {slot + 1} resident")
     rng = np.random.default_rng(123)
-    worst = {}
+    samples = []
     for li, L in enumerate(cfg.layers):
-        got = st.get_state(li)
-        init = synth.initial_state(cfg, li)
         js = np.unique(np.concatenate([[0, L.d_a - 1], rng.integers(0, L.d_a, 6)]))
         os_ = np.unique(np.concatenate([[0, L.d_out - 1], rng.integers(0, L.d_out, 6)]))
-        dA = {j: np.mean(oracle.activation_column(L, inputs[li]["a"], j) ** 2) for j in js}
-        dG = {o: np.mean(oracle.gradient_column(L, inputs[li]["g"], o) ** 2) for o in os_}
-        e = max(abs(got["dA"][j] - dA[j]) / max(abs(v) for v in dA.values()) for j in js)
-        worst["dA"] = max(worst.get("dA", 0), e)
-        e = max(abs(got["dG"][o] - dG[o]) / max(abs(v) for v in dG.values()) for o in os_)
-        worst["dG"] = max(worst.get("dG", 0), e)
-        # sampled parameters: the oracle's step restricted to (o, j)
-        ref = {"F": [], "V": [], "W": []}
-        gotv = {"F": [], "V": [], "W": []}
-        for o in os_:
-            for j in js:
-                if j < L.d_in:
-                    g_, w0, f0 = inputs[li]["grad_w"][o, j], init["w"][o, j], init["F_w"][o, j]
-                    key = ("F_w", "mom_w", "w")
-                    idx = (o, j)
-                else:
-                    g_, w0, f0 = inputs[li]["grad_b"][o], init["b"][o], init["F_b"][o]
-                    key = ("F_b", "mom_b", "b")
-                    idx = (o,)
-                one = synth.linear("entry", 1, 1, 1, bias=False)
-                out, _ = oracle.step_diag(
-                    one, {"w": np.array([[w0]]), "mom_w": np.zeros((1, 1)), "F_w": np.array([[f0]])},
-                    {"a": np.array([[np.sqrt(dA[j])]]), "g": np.array([[np.sqrt(dG[o])]]),
-                     "grad_w": np.array([[g_]])}, hp)
-                ref["F"].append(out["F_w"][0, 0]); ref["V"].append(out["mom_w"][0, 0]); ref["W"].append(out["w"][0, 0])
-                gotv["F"].append(got[key[0]][idx]); gotv["V"].append(got[key[1]][idx]); gotv["W"].append(got[key[2]][idx])
-        for k in ref:
-            e = max_rel(gotv[k], ref[k])
-            worst[k] = max(worst.get(k, 0), e)
-    say("full-size sampled worst:", {k: f"{v:.2e}" for k, v in worst.items()})
-    for k, v in worst.items():
-        assert v <= 1e-4, (k, v)
+        dA = [np.array([np.mean(oracle.activation_column(L, inputs[b][li]["a"], j) ** 2) for j in js]) for b in (0, 1)]
+        dG = [np.array([np.mean(oracle.gradient_column(L, inputs[b][li]["g"], o) ** 2) for o in os_]) for b in (0, 1)]
+        init = synth.initial_state(cfg, li)
+        aug = lambda w, b: np.concatenate([w, b[:, None]], 1) if L.has_bias else w
+        grads = [aug(inputs[b][li]["grad_w"], inputs[b][li]["grad_b"])[np.ix_(os_, js)] for b in (0, 1)]
+        samples.append(dict(js=js, os=os_, dA=dA, dG=dG, grads=grads,
+                            state={"w": aug(init["w"], init.get("b"))[np.ix_(os_, js)].astype(np.float64),
+                                   "mom_w": np.zeros((len(os_), len(js))),
+                                   "F_w": aug(init["F_w"], init.get("F_b"))[np.ix_(os_, js)].astype(np.float64)}))
+    say("oracle entries of both batches ready")
+
+    def oracle_step(smp, b):
+        # the sampled entries as one bias-free linear layer with one row:
+        # a = sqrt(dA), g = sqrt(dG) give the oracle's dG dA outer product
+        one = synth.linear("entries", len(smp["js"]), len(smp["os"]), 1, bias=False)
+        out, flags = oracle.step_diag(one, smp["state"], {"a": np.sqrt(smp["dA"][b])[None, :],
+                                                          "g": np.sqrt(smp["dG"][b])[None, :],
+                                                          "grad_w": smp["grads"][b]}, hp)
+        assert flags == 0
+        smp["state"] = {k: out[k] for k in ("w", "mom_w", "F_w")}
+
+    def compare(step, b):
+        worst = {}
+        for li, (L, smp) in enumerate(zip(cfg.layers, samples)):
+            got = st.get_state(li)
+            aug = lambda w, bb: np.concatenate([w, bb[:, None]], 1) if L.has_bias else w
+            sel = np.ix_(smp["os"], smp["js"])
+            pairs = (("dA", got["dA"][smp["js"]], smp["dA"][b]), ("dG", got["dG"][smp["os"]], smp["dG"][b]),
+                     ("F", aug(got["F_w"], got.get("F_b"))[sel], smp["state"]["F_w"]),
+                     ("V", aug(got["mom_w"], got.get("mom_b"))[sel], smp["state"]["mom_w"]),
+                     ("W", aug(got["w"], got.get("b"))[sel], smp["state"]["w"]))
+            for k, x, y in pairs:
+                e = max_rel(x, y)
+                worst[k] = max(worst.get(k, 0.0), e)
+                assert e <= 1e-4, (step, L.name, k, e)
+        say(f"step {step}: " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
+
+    H = st.hparams(hp)
+    for t in range(1, 101):
+        st.use_inputs((t - 1) % 2)
+        st.step(H)
+        for smp in samples:
+            oracle_step(smp, (t - 1) % 2)
+        if t in (1, 100):
+            torch.cuda.synchronize()
+            assert st.flags() == 0
+            compare(t, (t - 1) % 2)
 
 
 @pytest.mark.parametrize("beta", [0.0, 1.0])

@@ -154,92 +154,6 @@ def test_full_deterministic(gpu_lib):
             assert np.array_equal(a[k], b[k]), k
 
 
-def _full_size_step(name):
-    import torch
-    from second_order_optimizer_amd.stack import KfacStack
-    cfg = synth.full_config(name)
-    hp = synth.hparams(cfg)
-    st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype)
-    inputs, init = [], []
-    for li in range(len(cfg.layers)):
-        s0 = synth.initial_state(cfg, li)
-        inp = synth.step_inputs(cfg, 1, li)
-        st.set_state(li, s0)
-        st.set_inputs(li, inp)
-        inputs.append(inp)
-        init.append(s0)
-    say(f"{name}: full-size inputs resident")
-    st.step(st.hparams(hp, refresh=True))
-    torch.cuda.synchronize()
-    assert st.flags() == 0
-    say(f"{name}: step done")
-    return cfg, hp, st, inputs, init
-
-
-@pytest.mark.parametrize("name", ["resnet50_kfac", "mlp24_bf16", "pair16k_bf16"])
-def test_full_size_sampled(gpu_lib, name):
-    """The workload at its stated size, in the launch configuration the
-    benchmark times (one refresh step from the synthetic state):
-      * factor entries (i, j) on sampled pairs vs the oracle's column products
-        (EMA from the identity), tolerance 1e-4 (fp32 inputs) / 2e-2 (bf16);
-      * inverse: on sampled columns, the exact float64 solve with the factor
-        the library produced agrees with the library's inverse to 1e-3;
-      * update: V1 - wd W0 = P satisfies (G + lam I) P (A + lam I) = grad on
-        sampled rows, relative to the gradient row."""
-    import scipy.linalg
-    cfg, hp, st, inputs, init = _full_size_step(name)
-    eps, lam = hp["ema_decay"], hp["damping"]
-    tol_f = 2e-2 if cfg.act_dtype == "bf16" else 1e-4
-    rng = np.random.default_rng(7)
-    layer_ids = range(len(cfg.layers))
-    if len(cfg.layers) > 12:
-        layer_ids = sorted(set([0, 1, len(cfg.layers) - 1] + list(rng.choice(len(cfg.layers), 6, replace=False))))
-    worst = {"A": 0.0, "G": 0.0, "inv": 0.0, "upd": 0.0}
-    for li in layer_ids:
-        L = cfg.layers[li]
-        got = st.get_state(li)
-        a, g = inputs[li]["a"], inputs[li]["g"]
-        # factors on sampled pairs
-        for key, d, col in (("A", L.d_a, lambda j: oracle.activation_column(L, a, j)),
-                            ("G", L.d_out, lambda j: oracle.gradient_column(L, g, j))):
-            idx = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, 4)]))
-            cols = {j: col(j) for j in idx}
-            ref = np.array([[eps * (i == j) + (1 - eps) * cols[i] @ cols[j] / L.rows for j in idx] for i in idx])
-            e = max_rel(got[key][np.ix_(idx, idx)], ref)
-            worst[key] = max(worst[key], e)
-            assert e <= tol_f, (L.name, key, e)
-        # inverse: exact float64 solve with the library's own factor, sampled columns
-        for key, ikey in (("A", "A_inv"), ("G", "G_inv")):
-            F = got[key].astype(np.float64)
-            d = F.shape[0]
-            F[np.diag_indices(d)] += lam
-            cf = scipy.linalg.cho_factor(F, lower=True)
-            js = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, 4)]))
-            E = np.zeros((d, len(js)))
-            E[js, np.arange(len(js))] = 1.0
-            X = scipy.linalg.cho_solve(cf, E)
-            e = max_rel(got[ikey][:, js], X)
-            worst["inv"] = max(worst["inv"], e)
-            assert e <= 1e-3, (L.name, ikey, e)
-        # update: P = V1 - wd W0 (V0 = 0); (G + lam I) P (A + lam I) = grad on sampled rows
-        W0 = np.concatenate([init[li]["w"], init[li]["b"][:, None]], 1) if L.has_bias else init[li]["w"]
-        V1 = np.concatenate([got["mom_w"], got["mom_b"][:, None]], 1) if L.has_bias else got["mom_w"]
-        W1 = np.concatenate([got["w"], got["b"][:, None]], 1) if L.has_bias else got["w"]
-        gr = inputs[li]["grad_w"].astype(np.float64)
-        if L.has_bias:
-            gr = np.concatenate([gr, inputs[li]["grad_b"][:, None]], 1)
-        P = V1.astype(np.float64) - hp["weight_decay"] * W0.astype(np.float64)
-        Ad = got["A"].astype(np.float64) + lam * np.eye(L.d_a)
-        Gd = got["G"].astype(np.float64) + lam * np.eye(L.d_out)
-        rows = np.unique(np.concatenate([[0, L.d_out - 1], rng.integers(0, L.d_out, 4)]))
-        lhs = (Gd[rows] @ P) @ Ad
-        e = max_rel(lhs, gr[rows])
-        worst["upd"] = max(worst["upd"], e)
-        assert e <= (2e-3 if cfg.act_dtype == "bf16" else 1e-3), (L.name, "update residual", e)
-        assert max_rel(W1, W0 - hp["lr"] * V1) <= 1e-6
-    say(f"{name} full-size worst:", {k: f"{v:.2e}" for k, v in worst.items()})
-
-
 def test_bf16_factor_row_chunks(gpu_lib):
     """A bf16 factor whose input spans more than 2 GiB (140,000 rows x 8,192
     columns) exceeds the 32-bit range of the direct-to-LDS loads: the SYRK
@@ -383,3 +297,151 @@ def test_full_steps_from_two_threads(gpu_lib):
             a, b = a_st.get_state(li), b_st.get_state(li)
             for k in a:
                 assert np.array_equal(a[k], b[k]), (cfg.layers[li].name, k)
+
+
+def test_big_tile_gemms_lockstep(gpu_lib):
+    """Nine biased fp32 layers 2048 -> 2048 at 64 rows: each preconditioning
+    GEMM launch holds 9 x 64 = 576 tiles of 256 x 256, so it runs the
+    256 x 256-tile kernels the large workloads time (the store epilogue, then
+    the fused update), checked element by element against the oracle over
+    three steps (inverse on steps 1 and 3)."""
+    L = [synth.linear(f"wide{i}", 2048, 2048, 64, bias=True) for i in range(9)]
+    cfg = with_layers(synth.full_config("fc64"), L, steps=3, act_std=1.0, grad_std=1e-2, refresh_every=2)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
+def test_full_nonfinite_flag(gpu_lib):
+    """A NaN in the weight gradient of a layer whose update runs in the GEMM
+    epilogue, and separately in the bias gradient of a layer whose bias
+    column runs as matrix-vector products, each raise KFAC_FLAG_NONFINITE;
+    reading with clear resets the flag word."""
+    import torch
+    from second_order_optimizer_amd import FLAG_NONFINITE
+    from second_order_optimizer_amd.stack import KfacStack
+    L = [synth.linear("gemm", 100, 40, 16, bias=True), synth.linear("bias_split", 128, 40, 16, bias=True)]
+    cfg = with_layers(synth.full_config("fc64"), L, steps=1)
+    for li, key, where in ((0, "grad_w", (3, 7)), (1, "grad_b", (5,))):
+        st = KfacStack(cfg.layers, "full")
+        for lj in range(2):
+            st.set_state(lj, synth.initial_state(cfg, lj))
+            inp = synth.step_inputs(cfg, 1, lj)
+            if lj == li:
+                inp[key] = inp[key].copy()
+                inp[key][where] = np.nan
+            st.set_inputs(lj, inp)
+        st.step(st.hparams(synth.hparams(cfg), refresh=True))
+        torch.cuda.synchronize()
+        assert st.flags(clear=True) == FLAG_NONFINITE, key
+        assert st.flags() == 0
+
+
+@pytest.mark.parametrize("variant", ["full", "diag"])
+def test_resume_from_copied_state(gpu_lib, variant):
+    """Checkpoint / resume: after two steps the whole state (W, V and the
+    factors and inverses, or F) is copied to the host and into a new stack
+    with its own workspace; two more steps there equal two more steps of the
+    uninterrupted stack, bit for bit."""
+    import torch
+    from second_order_optimizer_amd.stack import KfacStack
+    cfg = synth.small_config("resnet50_kfac" if variant == "full" else "resnet18_diag")
+    hp = synth.hparams(cfg)
+    n = len(cfg.layers)
+
+    def steps(st, ts):
+        for t in ts:
+            for li in range(n):
+                st.set_inputs(li, synth.step_inputs(cfg, t, li))
+            refresh = synth.refresh_at(cfg, t) if variant == "full" else True
+            st.step(st.hparams(hp, refresh=refresh))
+        torch.cuda.synchronize()
+
+    a = KfacStack(cfg.layers, variant)
+    for li in range(n):
+        a.set_state(li, synth.initial_state(cfg, li))
+    steps(a, (1, 2))
+    ckpt = [a.get_state(li) for li in range(n)]
+    b = KfacStack(cfg.layers, variant)
+    for li in range(n):
+        b.set_state(li, ckpt[li])
+    steps(a, (3, 4))
+    steps(b, (3, 4))
+    assert a.flags() == 0 and b.flags() == 0
+    for li in range(n):
+        x, y = a.get_state(li), b.get_state(li)
+        for k in x:
+            assert np.array_equal(x[k], y[k]), (cfg.layers[li].name, k)
+
+
+def test_capture_beside_steps_on_other_streams(gpu_lib):
+    """Thread A captures a full step (with the Cholesky side streams) into a
+    graph on its stream; while the capture is open, thread B runs three full
+    steps on another stream.  B's results equal the same steps run alone, and
+    three replays of A's graph equal three eager steps, bit for bit."""
+    import threading
+    import torch
+    from second_order_optimizer_amd.stack import KfacStack
+    base = synth.small_config("resnet50_kfac")
+    cfg = with_layers(base, list(base.layers) + [synth.linear("fc_split", 256, 96, 32, bias=True)])
+    H = KfacStack.hparams(synth.hparams(cfg), refresh=True)
+
+    def make(t):
+        st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype)
+        for li in range(len(cfg.layers)):
+            st.set_state(li, synth.initial_state(cfg, li))
+            st.set_inputs(li, synth.step_inputs(cfg, t, li))
+        return st
+
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    warm = make(1)
+    for s in (sa, sb):
+        with torch.cuda.stream(s):
+            warm.step(H, stream=s)     # side streams of both streams exist before the capture
+    torch.cuda.synchronize()
+    ref_b = make(2)
+    with torch.cuda.stream(sb):
+        for _ in range(3):
+            ref_b.step(H, stream=sb)
+    eager_a, graphed, par_b = make(1), make(1), make(2)
+    torch.cuda.synchronize()
+    captured, b_done, errors = threading.Event(), threading.Event(), []
+
+    def thread_a():
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=sa, capture_error_mode="thread_local"):
+                graphed.step(H)
+                captured.set()
+                if not b_done.wait(timeout=60):
+                    raise RuntimeError("thread B did not finish")
+            thread_a.graph = g
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+            captured.set()
+
+    def thread_b():
+        try:
+            captured.wait(timeout=60)
+            for _ in range(3):
+                par_b.step(H, stream=sb)
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+        finally:
+            b_done.set()
+
+    ta, tb = threading.Thread(target=thread_a), threading.Thread(target=thread_b)
+    ta.start(); tb.start(); ta.join(); tb.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for li in range(len(cfg.layers)):
+        x, y = ref_b.get_state(li), par_b.get_state(li)
+        for k in x:
+            assert np.array_equal(x[k], y[k]), ("B", cfg.layers[li].name, k)
+    for rep in range(3):
+        eager_a.step(H)
+        thread_a.graph.replay()
+        torch.cuda.synchronize()
+        for li in range(len(cfg.layers)):
+            x, y = eager_a.get_state(li), graphed.get_state(li)
+            for k in x:
+                assert np.array_equal(x[k], y[k]), ("A", rep, cfg.layers[li].name, k)
+    assert eager_a.flags() == 0 and graphed.flags() == 0 and par_b.flags() == 0
