@@ -191,8 +191,27 @@ kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const
 kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* kfac_step_diag for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step with the same kernels, but no workspace argument.  The
+ * reduction's intermediate sums live in a device array of the library that
+ * holds at most 32 MiB (KFAC_NOALLOC_SCRATCH_BYTES); each GPU the library
+ * runs on holds one until the process ends.  A stack whose
+ * kfac_workspace_size(..., KFAC_MODE_DIAG, ...) exceeds that gets
+ * KFAC_ERR_WORKSPACE before anything is enqueued (ResNet-18 at 224x224 needs
+ * 17.8 MiB, at any batch).  `flags` is a caller-owned device word, zeroed by
+ * the caller once, that receives the sticky flags (kfac_read_flags accepts
+ * its address in place of a workspace).  The call allocates no memory on the
+ * device and calls no allocating routine.  Every call on one GPU shares that
+ * GPU's array: calls that can overlap on one GPU (different streams, host
+ * threads) race and must be ordered by the caller. */
+#define KFAC_NOALLOC_SCRATCH_BYTES (32u << 20)
+kfac_status_t kfac_step_diag_noalloc(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
+                                     uint32_t* flags, void* stream);
+
 /* Copy the workspace's sticky flag word to *flags (waits for `stream`), and
- * clear it on the device afterwards when `clear` is nonzero. */
+ * clear it on the device afterwards when `clear` is nonzero.  `workspace` may
+ * also be the flag word given to kfac_step_diag_noalloc. */
 kfac_status_t kfac_read_flags(void* workspace, void* stream, uint32_t* flags, int32_t clear);
 
 /* Static description of a status code. */

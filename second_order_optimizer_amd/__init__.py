@@ -22,8 +22,9 @@ MODE_FULL, MODE_DIAG = 0, 1
 PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE, PHASE_ALL = 1, 2, 4, 7
 FLAG_NOT_PD, FLAG_NONFINITE = 1, 2
 
-EXPORTS = ("kfac_workspace_size", "kfac_step_full", "kfac_step_diag", "kfac_read_flags",
+EXPORTS = ("kfac_workspace_size", "kfac_step_full", "kfac_step_diag", "kfac_step_diag_noalloc", "kfac_read_flags",
            "kfac_status_string", "kfac_abi_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Layer(ctypes.Structure):
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     for fn in (lib.kfac_step_full, lib.kfac_step_diag):
         fn.argtypes = [ctypes.POINTER(Layer), i32, ctypes.POINTER(HParams), vp, sz, vp]
         fn.restype = i32
+    lib.kfac_step_diag_noalloc.argtypes = [ctypes.POINTER(Layer), i32, ctypes.POINTER(HParams), vp, vp]
+    lib.kfac_step_diag_noalloc.restype = i32
     lib.kfac_read_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32), i32]
     lib.kfac_read_flags.restype = i32
     lib.kfac_status_string.argtypes = [i32]
@@ -136,6 +139,14 @@ def step_diag(layers, hp: HParams, workspace: int, ws_bytes: int, stream=None) -
     st = load().kfac_step_diag(layers, len(layers), ctypes.byref(hp), workspace, ws_bytes, _stream_handle(stream))
     if st != KFAC_OK:
         raise KfacError(st, "kfac_step_diag")
+
+
+def step_diag_noalloc(layers, hp: HParams, flags: int, stream=None) -> None:
+    """kfac_step_diag_noalloc: `flags` is the device address of a zeroed
+    uint32 flag word (no workspace; the library's own scratch array is used)."""
+    st = load().kfac_step_diag_noalloc(layers, len(layers), ctypes.byref(hp), flags, _stream_handle(stream))
+    if st != KFAC_OK:
+        raise KfacError(st, "kfac_step_diag_noalloc")
 
 
 def read_flags(workspace: int, clear: bool = False, stream=None) -> int:

@@ -106,17 +106,26 @@ kfac_status_t check_all(const kfac_layer_t* layers, int32_t n, int mode) {
   return KFAC_OK;
 }
 
-kfac_status_t run(const kfac_layer_t* layers, int32_t n, const kfac_hparams_t* hp, void* workspace,
-                  size_t ws_bytes, void* stream, int mode) {
+// Descriptor, scalar and pointer checks shared by the step entry points;
+// *phases receives the phases the call runs.
+kfac_status_t validate(const kfac_layer_t* layers, int32_t n, const kfac_hparams_t* hp, int mode, int* phases) {
   kfac_status_t s = check_all(layers, n, mode);
   if (s != KFAC_OK) return s;
   if (!hp || hp->reserved != 0) return KFAC_ERR_ARG;
   if (hp->phase_mask < 0 || hp->phase_mask > KFAC_PHASE_ALL) return KFAC_ERR_ARG;
-  const int phases = hp->phase_mask == 0 ? KFAC_PHASE_ALL : hp->phase_mask;
+  *phases = hp->phase_mask == 0 ? KFAC_PHASE_ALL : hp->phase_mask;
   for (int i = 0; i < n; ++i) {
-    s = check_layer_ptrs(layers[i], mode, phases, hp->refresh != 0);
+    s = check_layer_ptrs(layers[i], mode, *phases, hp->refresh != 0);
     if (s != KFAC_OK) return s;
   }
+  return KFAC_OK;
+}
+
+kfac_status_t run(const kfac_layer_t* layers, int32_t n, const kfac_hparams_t* hp, void* workspace,
+                  size_t ws_bytes, void* stream, int mode) {
+  int phases = 0;
+  kfac_status_t s = validate(layers, n, hp, mode, &phases);
+  if (s != KFAC_OK) return s;
   if (!workspace) return KFAC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return KFAC_ERR_ALIGN;
   const size_t need = mode == KFAC_MODE_FULL ? full_workspace_bytes(layers, n) : diag_workspace_bytes(layers, n);
@@ -150,6 +159,16 @@ kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const
 kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                              void* workspace, size_t ws_bytes, void* stream) {
   return kfac::run(layers, n_layers, hp, workspace, ws_bytes, stream, KFAC_MODE_DIAG);
+}
+
+kfac_status_t kfac_step_diag_noalloc(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
+                                     uint32_t* flags, void* stream) {
+  int phases = 0;
+  kfac_status_t s = kfac::validate(layers, n_layers, hp, KFAC_MODE_DIAG, &phases);
+  if (s != KFAC_OK) return s;
+  if (!flags) return KFAC_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(flags) & 3u) != 0) return KFAC_ERR_ALIGN;
+  return kfac::diag_enqueue_noalloc(layers, n_layers, *hp, flags, static_cast<hipStream_t>(stream), phases);
 }
 
 kfac_status_t kfac_read_flags(void* workspace, void* stream, uint32_t* flags, int32_t clear) {

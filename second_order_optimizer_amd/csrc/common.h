@@ -53,6 +53,12 @@ LayerGeom geom_of(const kfac_layer_t& L);
 size_t diag_workspace_bytes(const kfac_layer_t* layers, int n);
 kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
                            size_t ws_bytes, hipStream_t stream, int phases);
+// The diagonal step with its scratch in a device array of the library (at most
+// kNoAllocScratchBytes; larger stacks get KFAC_ERR_WORKSPACE) and the flag
+// word at `flags`; allocates no device memory.
+constexpr size_t kNoAllocScratchBytes = KFAC_NOALLOC_SCRATCH_BYTES;
+kfac_status_t diag_enqueue_noalloc(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, uint32_t* flags,
+                                   hipStream_t stream, int phases);
 
 // full method (full.hip)
 size_t full_workspace_bytes(const kfac_layer_t* layers, int n);

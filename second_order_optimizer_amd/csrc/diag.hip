@@ -25,6 +25,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 namespace kfac {
@@ -563,8 +564,12 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
 
 size_t diag_workspace_bytes(const kfac_layer_t* layers, int n) { return plan_diag(layers, n, nullptr).ws_bytes; }
 
-kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
-                           size_t ws_bytes, hipStream_t stream, int phases) {
+namespace {
+
+// The step's launches with the reduction's intermediate sums carved from `ws`
+// (its first kFlagBytes are not used for them) and the flag word at `flags`.
+kfac_status_t enqueue_steps(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                            size_t ws_bytes, uint32_t* flags, hipStream_t stream, int phases) {
   DiagPlan P = plan_diag(layers, n, ws);
   if (P.ws_bytes > ws_bytes) return KFAC_ERR_WORKSPACE;
   if (phases & KFAC_PHASE_FACTORS) {
@@ -615,12 +620,61 @@ kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
       S.weight_decay = hp.weight_decay;
       S.momentum = hp.momentum;
       S.lr = hp.lr;
-      S.flags = reinterpret_cast<uint32_t*>(ws);
+      S.flags = flags;
       hipLaunchKernelGGL(diag_update_kernel, dim3(blocks), dim3(kUpdThreads), 0, stream, S);
       KFAC_HIP_TRY(hipGetLastError());
     }
   }
   return KFAC_OK;
+}
+
+}  // namespace
+
+kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                           size_t ws_bytes, hipStream_t stream, int phases) {
+  return enqueue_steps(layers, n, hp, ws, ws_bytes, reinterpret_cast<uint32_t*>(ws), stream, phases);
+}
+
+// ---------------------------------------------------------------------------
+// The same step for callers that cannot allocate device memory: the
+// reduction's intermediate sums (the only scratch the step's kernels use) live
+// in `scratch`, a file-scope device array of kNoAllocScratchBytes that every
+// GPU the library runs on holds until the process ends.  Its device address
+// on each GPU is looked up once, with that GPU current, and kept; host code
+// never passes the array's own name to a kernel.  Every call on one GPU uses
+// the same array, so calls that can overlap on one GPU race; the sums are
+// written by each FACTORS phase before they are read, so nothing in the
+// array has to start at zero.
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+kfac_status_t scratch_address(char** out) {
+  static std::mutex mu;
+  static std::vector<char*> per_device;
+  int dev = 0;
+  KFAC_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device.size() <= static_cast<size_t>(dev)) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KFAC_ERR_HIP;
+    per_device[dev] = static_cast<char*>(p);
+  }
+  *out = per_device[dev];
+  return KFAC_OK;
+}
+
+}  // namespace
+
+kfac_status_t diag_enqueue_noalloc(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, uint32_t* flags,
+                                   hipStream_t stream, int phases) {
+  if (diag_workspace_bytes(layers, n) > kNoAllocScratchBytes) return KFAC_ERR_WORKSPACE;
+  char* base = nullptr;
+  kfac_status_t r = scratch_address(&base);
+  if (r != KFAC_OK) return r;
+  return enqueue_steps(layers, n, hp, base, kNoAllocScratchBytes, flags, stream, phases);
 }
 
 }  // namespace kfac
