@@ -3,19 +3,23 @@
 
 A step is one call of the library's step entry point over the whole layer
 stack of a synthetic workload, inputs already resident in HBM.  The default
-workload is the diagonal (AdaFisher-style) step over a ResNet-18 parameter
-set, batch 128 at 224x224; ``--config`` selects the other workloads.
+run measures all five workloads in one process and prints ONE JSON line:
+`value` is the diagonal (AdaFisher-style) step over the ResNet-18 parameter
+set, batch 128 at 224x224; `configs` holds every workload's steps/s, per-phase
+times, TFLOP/s against the MFMA peak of its dtype (full K-FAC) or GB/s
+against HBM (diagonal), and the float64 CPU oracle timed on the host.
+`--config NAME` measures one workload alone.
 
-Prints one JSON line (rank 0) with steps/s, the roofline position of the
-dominant kernel (timed live with HIP events on the stream it runs on) and the
-float64 CPU oracle timed on a bounded sample of the same workload.
+Phases are timed live with HIP events on the stream the library launches on
+(single-phase calls through the C ABI).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -27,7 +31,9 @@ FP32_MFMA_TFLOPS = 157.3       # dense fp32 MFMA
 BF16_MFMA_TFLOPS = 2500.0      # dense bf16 MFMA
 
 METRIC = "K-FAC steps/s per layer stack; factor+precond TFLOP/s (%MFMA); diag-step GB/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "diag_colsq_resnet18_b128_traffic.md")
+HEADLINE = "resnet18_diag"
+ORDER = ("resnet18_diag", "fc64", "resnet50_kfac", "mlp24_bf16", "pair16k_bf16")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "diag_resnet18_b128_traffic.md")
 DIAG_SRC = os.path.join(ROOT, "second_order_optimizer_amd", "csrc", "diag.hip")
 COPY_BYTES = 1 << 30     # the --traffic-probe calibration copy reads and writes 1 GiB
 
@@ -37,26 +43,25 @@ def log(*a):
 
 
 def workload_desc(cfg) -> dict:
-    import synth
     d = {"workload": cfg.name, "variant": cfg.variant, "layers": len(cfg.layers), "params": cfg.n_params,
          "act_dtype": cfg.act_dtype, "grad_dtype": cfg.grad_dtype}
-    if cfg.name == "resnet18_diag":
-        d["desc"] = "ResNet-18 shapes (20 conv + FC 512->1000), batch 128 @ 224x224, diagonal step"
-    elif cfg.name == "resnet50_kfac":
-        d["desc"] = "ResNet-50 shapes (53 conv + FC 2048->1000), batch 32 @ 224x224, full K-FAC, invert every step"
-    elif cfg.name == "mlp24_bf16":
-        d["desc"] = "24 x (1024->4096, 4096->1024) linears with bias, 8192 tokens, bf16 a/g, invert every 10"
-    elif cfg.name == "pair16k_bf16":
-        d["desc"] = "4096->16384 and 16384->4096 linears with bias, 16384 tokens, bf16 a/g, invert every 20"
-    elif cfg.name == "fc64":
-        d["desc"] = "one FC 64(+1)->32, batch 128, full K-FAC, invert every step"
+    d["desc"] = {
+        "resnet18_diag": "ResNet-18 shapes (20 conv + FC 512->1000), batch 128 @ 224x224, diagonal step",
+        "resnet50_kfac": "ResNet-50 shapes (53 conv + FC 2048->1000), batch 32 @ 224x224, full K-FAC, invert every step",
+        "mlp24_bf16": "24 x (1024->4096, 4096->1024) linears with bias, 8192 tokens, bf16 a/g, invert every 10",
+        "pair16k_bf16": "4096->16384 and 16384->4096 linears with bias, 16384 tokens, bf16 a/g, invert every 20",
+        "fc64": "one FC 64(+1)->32, batch 128, full K-FAC, invert every step",
+    }[cfg.name]
     d["refresh_every"] = cfg.refresh_every if cfg.variant == "full" else None
     return d
 
 
+# ---------------------------------------------------------------------------
+# algorithmic work
+
 def diag_factor_bytes(cfg) -> int:
-    """Algorithmic bytes of the diagonal FACTORS launch: every element of a and
-    g read once (4 B), dA and dG written once."""
+    """Algorithmic bytes of the diagonal FACTORS phase (a7): every element of a
+    and g read once (4 B), dA and dG written once."""
     import numpy as np
     n = 0
     for L in cfg.layers:
@@ -66,37 +71,9 @@ def diag_factor_bytes(cfg) -> int:
 
 
 def diag_update_bytes(cfg) -> int:
-    """Algorithmic bytes of the diagonal parameter pass: grad, W, V, F read and
-    W, V, F written, 4 B each (28 B per parameter)."""
+    """Algorithmic bytes of the diagonal parameter pass (a8): grad, W, V, F read
+    and W, V, F written, 4 B each (28 B per parameter)."""
     return 28 * cfg.n_params
-
-
-def cpu_baseline_diag(cfg_full, seconds_target=15.0):
-    """The oracle's diagonal step over every layer of the workload at a reduced
-    batch; the oracle's cost is linear in the batch, so the full-batch step
-    time is the sample time scaled by batch / sample batch."""
-    import numpy as np
-    import oracle
-    import synth
-    full_batch = cfg_full.layers[0].batch
-    sb = 16
-    layers = synth.resnet18_layers(batch=sb)
-    cfg = synth.Config(cfg_full.cfg_id, cfg_full.name, "diag", tuple(layers), 1, cfg_full.lr, cfg_full.momentum,
-                       cfg_full.weight_decay, cfg_full.ema_decay, cfg_full.damping, act_std=cfg_full.act_std,
-                       grad_std=cfg_full.grad_std, relu=cfg_full.relu)
-    hp = synth.hparams(cfg)
-    data = [(synth.initial_state(cfg, li), synth.step_inputs(cfg, 1, li)) for li in range(len(layers))]
-    t0, c0 = time.perf_counter(), time.process_time()
-    for li, L in enumerate(layers):
-        oracle.step_diag(L, data[li][0], data[li][1], hp)
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    step_s = wall * full_batch / sb
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": max(1, int(round(cpu / max(wall, 1e-9)))),
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle, diagonal step over all {len(layers)} layers at batch {sb} "
-                      f"(full workload batch {full_batch}); measured {wall:.2f} s, scaled x{full_batch // sb} "
-                      f"(cost linear in batch)"}
 
 
 def full_flops(layers):
@@ -110,8 +87,58 @@ def full_flops(layers):
     return syrk, pre, inv
 
 
-def cpu_sample_layers(cfg):
-    """(layer indices, row divisor) of the CPU-baseline sample."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host
+
+def host_info():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def _timed(fn):
+    """Runs fn() with the BLAS pool at all host cores; (wall s, cpu s, cores)."""
+    from threadpoolctl import threadpool_limits
+    cores, _ = host_info()
+    with threadpool_limits(limits=cores, user_api="blas"):
+        c0, t0 = time.process_time(), time.perf_counter()
+        fn()
+        wall, cpu = time.perf_counter() - t0, time.process_time() - c0
+    return wall, cpu, cores
+
+
+def cpu_baseline_diag(cfg):
+    """The oracle's whole diagonal step over every layer at the workload's full
+    size (one step)."""
+    import oracle
+    import synth
+    hp = synth.hparams(cfg)
+    data = [(synth.initial_state(cfg, li), synth.step_inputs(cfg, 1, li)) for li in range(len(cfg.layers))]
+
+    def run():
+        for li, L in enumerate(cfg.layers):
+            oracle.step_diag(L, data[li][0], data[li][1], hp)
+    wall, cpu, cores = _timed(run)
+    _, model = host_info()
+    return {"value": 1.0 / wall, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"float64 numpy oracle, one whole diagonal step over all {len(cfg.layers)} layers at full size "
+                      f"(batch {cfg.layers[0].batch}): {wall:.2f} s wall, {cpu:.1f} s CPU; BLAS pool of {cores} "
+                      f"threads on {model}"}
+
+
+def cpu_sample(cfg):
+    """(layer indices, row divisor) of the full method's CPU sample; the FC 64
+    workload runs whole."""
     n = len(cfg.layers)
     if cfg.name == "mlp24_bf16":
         return [0, 1], 1                   # one of 24 identical blocks
@@ -123,56 +150,137 @@ def cpu_sample_layers(cfg):
 
 
 def cpu_baseline_full(cfg):
-    """The oracle's full step timed on a subset of the stack's layers, once as a
-    refresh step and once as a stale step; the amortised sample time is scaled
-    to the whole stack by the ratio of algorithmic flops."""
+    """The oracle's full step: the FC 64 workload's ten steps whole; the larger
+    stacks on a sample of their layers, once as a refresh step and once as a
+    stale step, the amortised time scaled to the whole stack by the ratio of
+    algorithmic flops (labelled as a sample)."""
     import dataclasses
+    import numpy as np
     import oracle
     import synth
-    idx, div = cpu_sample_layers(cfg)
+    hp = synth.hparams(cfg)
+    _, model = host_info()
+    if cfg.name == "fc64":
+        L = cfg.layers[0]
+        st0 = {k: v.astype(np.float64) for k, v in synth.initial_state(cfg, 0).items()}
+        inputs = [synth.step_inputs(cfg, t, 0) for t in range(1, cfg.steps + 1)]
+
+        def run():
+            st = st0
+            for t, inp in enumerate(inputs, 1):
+                out, _ = oracle.step_full(L, st, inp, hp, synth.refresh_at(cfg, t))
+                st = {k: out[k] for k in st0}
+        wall, cpu, cores = _timed(run)
+        return {"value": cfg.steps / wall, "unit": "steps/s", "cores": cores, "kind": "oracle",
+                "sample": f"float64 numpy oracle, all {cfg.steps} steps of the workload: {wall * 1e3:.1f} ms wall; "
+                          f"BLAS pool of {cores} threads on {model}"}
+    idx, div = cpu_sample(cfg)
     sub = [cfg.layers[i] if div == 1 else dataclasses.replace(cfg.layers[i], rows=cfg.layers[i].rows // div)
            for i in idx]
     scfg = dataclasses.replace(cfg, layers=tuple(sub))
-    hp = synth.hparams(cfg)
     data = [(synth.initial_state(scfg, j), synth.step_inputs(scfg, 1, j)) for j in range(len(sub))]
     times = {}
-    c0 = time.process_time()
-    w0 = time.perf_counter()
+    cpu_total = 0.0
     for refresh in (True, False):
-        t0 = time.perf_counter()
-        for (st, inp), L in zip(data, sub):
-            oracle.step_full(L, st, inp, hp, refresh)
-        times[refresh] = time.perf_counter() - t0
-    wall = time.perf_counter() - w0
-    cpu = time.process_time() - c0
+        def run():
+            for (st, inp), L in zip(data, sub):
+                oracle.step_full(L, st, inp, hp, refresh)
+        times[refresh], cpu, cores = _timed(run)
+        cpu_total += cpu
     k = cfg.refresh_every
     t_sample = (times[True] + (k - 1) * times[False]) / k
     fs, fp, fi = full_flops(sub)
     ts, tp, ti = full_flops(cfg.layers)
     scale = (ts + tp + ti / k) / (fs + fp + fi / k)
-    step_s = t_sample * scale
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": max(1, int(round(cpu / max(wall, 1e-9)))),
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle, full step on layers {idx} of {len(cfg.layers)}"
-                      f"{'' if div == 1 else f' at 1/{div} of the rows'}: refresh step "
-                      f"{times[True]:.2f} s, stale step {times[False]:.2f} s, amortised over a refresh interval "
-                      f"of {k}, scaled x{scale:.2f} by algorithmic flops"}
+    return {"value": 1.0 / (t_sample * scale), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"SAMPLE: float64 numpy oracle, full step on layers {idx} of {len(cfg.layers)}"
+                      f"{'' if div == 1 else f' at 1/{div} of the rows'}: refresh step {times[True]:.2f} s, stale "
+                      f"step {times[False]:.2f} s wall ({cpu_total:.1f} s CPU), amortised over a refresh interval "
+                      f"of {k}, scaled x{scale:.2f} to the whole stack by algorithmic flops; BLAS pool of {cores} "
+                      f"threads on {model}"}
+
+
+# ---------------------------------------------------------------------------
+# GPU runs
+
+def _load(cfg, pool):
+    import synth
+    from second_order_optimizer_amd.stack import KfacStack
+    st = KfacStack(cfg.layers, cfg.variant, cfg.act_dtype, cfg.grad_dtype, pool=pool)
+    for li in range(len(cfg.layers)):
+        st.set_state(li, synth.initial_state(cfg, li))
+    for slot in range(pool):
+        for li in range(len(cfg.layers)):
+            st.set_inputs(li, synth.step_inputs(cfg, slot + 1, li), slot=slot)
+        log(f"[bench] {cfg.name}: input batch {slot + 1}/{pool} resident")
+    return st
+
+
+def _time_phase(st, hp, pool, mask, n, refresh=False):
+    """Average time (ms) of `n` back-to-back calls that run only `mask`,
+    between two HIP events recorded on the stream the library launches on
+    (torch's current stream); one event pair around the whole run keeps the
+    events' own cost out of short phases."""
+    import torch
+    Hm = st.hparams(hp, refresh=refresh, phase_mask=mask)
+    stream = torch.cuda.current_stream()
+    st.step(Hm)                      # one untimed call: the phase's first launches are warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        st.use_inputs(i % pool)
+        st.step(Hm)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def run_diag(cfg, args):
+    import torch
+    import synth
+    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_UPDATE
+    pool = max(1, args.pool)
+    st = _load(cfg, pool)
+    hp = synth.hparams(cfg)
+    H = st.hparams(hp)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        st.use_inputs(i % pool)
+        st.step(H)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.use_inputs(i % pool)
+        st.step(H)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    log(f"[bench] {cfg.name}: timed {args.steps} steps: {ms:.3f} ms/step")
+    nk = max(5, args.steps)
+    t_fac = _time_phase(st, hp, pool, PHASE_FACTORS, nk)
+    t_upd = _time_phase(st, hp, pool, PHASE_UPDATE, nk)
+    assert st.flags() == 0, "device flags raised"
+    del st
+    torch.cuda.empty_cache()
+    fb, ub = diag_factor_bytes(cfg), diag_update_bytes(cfg)
+    gbs = lambda b, t: b / (t * 1e-3) / 1e9
+    return {
+        "ms_per_step": ms, "steps_per_s": 1e3 / ms, "steps": args.steps, "dtype": "f32",
+        "a7_diag_factors": {"kernels": "diag_colsq_kernel + diag_finish_kernel", "ms": t_fac, "bytes": fb,
+                            "GBps": gbs(fb, t_fac), "peak_GBps": HBM_PEAK_GBS, "frac": gbs(fb, t_fac) / HBM_PEAK_GBS},
+        "a8_diag_step": {"kernels": "diag_update_kernel", "ms": t_upd, "bytes": ub, "GBps": gbs(ub, t_upd),
+                         "peak_GBps": HBM_PEAK_GBS, "frac": gbs(ub, t_upd) / HBM_PEAK_GBS},
+        "step_GBps": gbs(fb + ub, ms),
+    }
 
 
 def run_full(cfg, args):
     import torch
     import synth
     from second_order_optimizer_amd import PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE
-    from second_order_optimizer_amd.stack import KfacStack
-
     pool = max(1, args.pool)
-    st = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype, pool=pool)
-    for li in range(len(cfg.layers)):
-        st.set_state(li, synth.initial_state(cfg, li))
-    for slot in range(pool):
-        for li in range(len(cfg.layers)):
-            st.set_inputs(li, synth.step_inputs(cfg, slot + 1, li), slot=slot)
-        log(f"[bench] input batch {slot + 1}/{pool} resident")
+    st = _load(cfg, pool)
     hp = synth.hparams(cfg)
     k = cfg.refresh_every
     steps = max(k, (args.steps + k - 1) // k * k)     # whole refresh intervals
@@ -182,7 +290,6 @@ def run_full(cfg, args):
         st.use_inputs(i % pool)
         st.step(H[i % k == 0])
     torch.cuda.synchronize()
-    log("[bench] warmup done")
     t0 = time.perf_counter()
     for i in range(steps):
         st.use_inputs(i % pool)
@@ -190,57 +297,60 @@ def run_full(cfg, args):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / steps
-    log(f"[bench] timed {steps} steps: {ms:.3f} ms/step")
-    stream = torch.cuda.current_stream()
-
-    def time_phase(mask, n, refresh=False):
-        Hm = st.hparams(hp, refresh=refresh, phase_mask=mask)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i in range(n):
-            st.use_inputs(i % pool)
-            evs[i][0].record(stream)
-            st.step(Hm)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / n
-
+    log(f"[bench] {cfg.name}: timed {steps} steps: {ms:.3f} ms/step")
     n = max(3, min(10, args.steps))
-    t_fac = time_phase(PHASE_FACTORS, n)
-    t_inv = time_phase(PHASE_INVERT, max(2, n // 3), refresh=True)
-    t_upd = time_phase(PHASE_UPDATE, n)
+    t_fac = _time_phase(st, hp, pool, PHASE_FACTORS, n)
+    t_inv = _time_phase(st, hp, pool, PHASE_INVERT, max(2, n // 3), refresh=True)
+    t_upd = _time_phase(st, hp, pool, PHASE_UPDATE, n)
     assert st.flags() == 0, "device flags raised"
+    del st
+    torch.cuda.empty_cache()
     fs, fp, fi = full_flops(cfg.layers)
     syrk_peak = BF16_MFMA_TFLOPS if cfg.act_dtype == "bf16" else FP32_MFMA_TFLOPS
     tf = lambda f, t: f / (t * 1e-3) / 1e12
-    phases = {
-        "factors": {"ms": t_fac, "tflops": tf(fs, t_fac), "peak": syrk_peak, "frac": tf(fs, t_fac) / syrk_peak,
-                    "flops": fs, "dtype": cfg.act_dtype},
-        "precond_update": {"ms": t_upd, "tflops": tf(fp, t_upd), "peak": FP32_MFMA_TFLOPS,
-                           "frac": tf(fp, t_upd) / FP32_MFMA_TFLOPS, "flops": fp, "dtype": "f32"},
-        "invert": {"ms": t_inv, "amortised_ms": t_inv / k, "tflops": tf(fi, t_inv), "peak": FP32_MFMA_TFLOPS,
-                   "frac": tf(fi, t_inv) / FP32_MFMA_TFLOPS, "flops": fi, "dtype": "f32"},
+    out = {
+        "ms_per_step": ms, "steps_per_s": 1e3 / ms, "steps": steps, "refresh_every": k, "dtype": cfg.act_dtype,
+        "factors": {"ms": t_fac, "flops": fs, "tflops": tf(fs, t_fac), "peak_tflops": syrk_peak,
+                    "frac": tf(fs, t_fac) / syrk_peak, "dtype": cfg.act_dtype},
+        "precond_update": {"ms": t_upd, "flops": fp, "tflops": tf(fp, t_upd), "peak_tflops": FP32_MFMA_TFLOPS,
+                           "frac": tf(fp, t_upd) / FP32_MFMA_TFLOPS, "dtype": "f32"},
+        "invert": {"ms": t_inv, "amortised_ms": t_inv / k, "flops": fi, "tflops": tf(fi, t_inv),
+                   "peak_tflops": FP32_MFMA_TFLOPS, "frac": tf(fi, t_inv) / FP32_MFMA_TFLOPS, "dtype": "f32"},
     }
     ideal = fs / (syrk_peak * 1e12) + fp / (FP32_MFMA_TFLOPS * 1e12)
-    phases["combined_mfma_frac"] = ideal / ((t_fac + t_upd) * 1e-3)
-    dom = max(("factors", t_fac), ("precond_update", t_upd), ("invert", t_inv / k), key=lambda x: x[1])[0]
-    names = {"factors": "factor SYRK + EMA launches (im2col, syrk_bf16_kernel / gemm_f32_kernel EPI_SYRK, split reduce)",
-             "precond_update": "preconditioning GEMMs (gemm_f32_kernel, STORE then fused UPDATE epilogue)",
-             "invert": "blocked Cholesky inverse launches"}
-    d = phases[dom]
-    roof = {"bound": "mfma", "kernel": names[dom], "achieved": d["tflops"], "peak": d["peak"], "unit": "TFLOP/s",
-            "frac": d["frac"], "traffic": None, "flops_per_launch": d["flops"], "avg_launch_ms": d["ms"]}
-    return {"value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms, "dtype": cfg.act_dtype,
-            "roofline": roof, "phases": phases, "steps": steps}
+    out["combined_mfma_frac"] = ideal / ((t_fac + t_upd) * 1e-3)
+    return out
 
 
-def source_sha256(path):
-    import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+# ---------------------------------------------------------------------------
+# counter-measured traffic of the headline workload's FACTORS phase
+
+def _function_text(src, name):
+    """Source text of the first __global__ / __device__ definition of `name`."""
+    m = re.search(r"(__global__|__device__)[^;{]*?\b" + re.escape(name) + r"\s*\(", src)
+    if not m:
+        return ""
+    i = src.index("{", m.end())
+    depth = 0
+    for j in range(i, len(src)):
+        depth += {"{": 1, "}": -1}.get(src[j], 0)
+        if depth == 0:
+            return src[m.start():j + 1]
+    return src[m.start():]
+
+
+A7_KERNELS = ("diag_colsq_kernel", "wave_sum", "tap_mask", "fin_window", "fin_window_block", "diag_finish_kernel")
+
+
+def a7_source_sha256():
+    src = open(DIAG_SRC).read()
+    return hashlib.sha256("\n".join(_function_text(src, n) for n in A7_KERNELS).encode()).hexdigest()
 
 
 def measured_traffic():
-    """HBM bytes per launch of diag_colsq_kernel from the committed counter
-    summary, or None when it is missing or the kernel source changed since."""
+    """HBM bytes per FACTORS call of the headline workload (both a7 kernels)
+    from the committed counter summary, or None when it is missing or the
+    kernels' source changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -248,10 +358,10 @@ def measured_traffic():
         if line.startswith("    ") and ":" in line:
             k, v = line.strip().split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != source_sha256(DIAG_SRC):
+    if vals.get("a7_kernels_sha256") != a7_source_sha256():
         return None
     try:
-        return int(vals["traffic_bytes_per_launch"])
+        return int(vals["a7_traffic_bytes_per_call"])
     except (KeyError, ValueError):
         return None
 
@@ -259,105 +369,36 @@ def measured_traffic():
 def traffic_probe(args):
     """What the FETCH_SIZE / WRITE_SIZE passes profile: a plain 1 GiB device
     copy (calibration of the counters), then `--steps` FACTORS-only diagonal
-    calls on ResNet-18 @ 128 (each one launch of diag_colsq_kernel) and
-    `--steps` UPDATE-only calls (diag_finish_kernel, diag_update_kernel)."""
+    calls on ResNet-18 @ 128 (diag_colsq_kernel, diag_finish_kernel) and
+    `--steps` UPDATE-only calls (diag_update_kernel)."""
     import torch
     import synth
     from second_order_optimizer_amd import PHASE_FACTORS, PHASE_UPDATE
-    from second_order_optimizer_amd.stack import KfacStack
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    cfg = synth.full_config("resnet18_diag")
-    st = KfacStack(cfg.layers, "diag")
-    for li in range(len(cfg.layers)):
-        st.set_state(li, synth.initial_state(cfg, li))
-        st.set_inputs(li, synth.step_inputs(cfg, 1, li))
-    H = st.hparams(synth.hparams(cfg), phase_mask=PHASE_FACTORS)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        st.step(H)
-    torch.cuda.synchronize()
-    Hu = st.hparams(synth.hparams(cfg), phase_mask=PHASE_UPDATE)
-    for _ in range(args.steps):
-        st.step(Hu)
-    torch.cuda.synchronize()
-    print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES, "factor_calls": args.steps,
-                      "update_calls": args.steps, "diag_src_sha256": source_sha256(DIAG_SRC)}), flush=True)
-
-
-def run_diag(cfg, args):
-    import torch
-    import synth
-    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_UPDATE
-    from second_order_optimizer_amd.stack import KfacStack
-
-    pool = max(1, args.pool)
-    st = KfacStack(cfg.layers, "diag", pool=pool)
-    for li in range(len(cfg.layers)):
-        st.set_state(li, synth.initial_state(cfg, li))
-    for slot in range(pool):
-        for li in range(len(cfg.layers)):
-            st.set_inputs(li, synth.step_inputs(cfg, slot + 1, li), slot=slot)
-        log(f"[bench] input batch {slot + 1}/{pool} resident")
-    hp = synth.hparams(cfg)
-    H_all = st.hparams(hp)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        st.use_inputs(i % pool)
-        st.step(H_all)
-    torch.cuda.synchronize()
-    log("[bench] warmup done")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        st.use_inputs(i % pool)
-        st.step(H_all)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    log(f"[bench] timed {args.steps} steps: {dt * 1e3 / args.steps:.3f} ms/step")
-
-    # live per-kernel timing with HIP events on the stream the library uses
-    stream = torch.cuda.current_stream()
-
-    def time_phase(mask, n):
-        H = st.hparams(hp, phase_mask=mask)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i in range(n):
-            st.use_inputs(i % pool)
-            evs[i][0].record(stream)
-            st.step(H)
-            evs[i][1].record(stream)
+    cfg = synth.full_config(HEADLINE)
+    st = _load(cfg, 1)
+    for mask in (PHASE_FACTORS, PHASE_UPDATE):
+        H = st.hparams(synth.hparams(cfg), phase_mask=mask)
         torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in evs) / n   # ms
+        for _ in range(args.steps):
+            st.step(H)
+        torch.cuda.synchronize()
+    print(json.dumps({"probe": "traffic", "copy_bytes": COPY_BYTES, "factor_calls": args.steps,
+                      "update_calls": args.steps, "a7_kernels_sha256": a7_source_sha256()}), flush=True)
 
-    nk = max(5, args.steps)
-    t_fac = time_phase(PHASE_FACTORS, nk)
-    t_upd = time_phase(PHASE_UPDATE, nk)
-    assert st.flags() == 0, "device flags raised"
-    fb = diag_factor_bytes(cfg)
-    ub = diag_update_bytes(cfg)
-    ms = dt * 1e3 / args.steps
-    achieved = fb / (t_fac * 1e-3) / 1e9
-    out = {
-        "value": 1e3 / ms, "unit": "steps/s", "ms_per_step": ms, "dtype": "f32",
-        "roofline": {"bound": "hbm", "kernel": "diag_colsq_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "bytes_per_launch": fb, "avg_launch_ms": t_fac},
-        "phases": {"factors_ms": t_fac, "update_ms": t_upd,
-                   "update_GBps": ub / (t_upd * 1e-3) / 1e9,
-                   "step_GBps": (fb + ub) / (ms * 1e-3) / 1e9},
-    }
-    return out
 
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="resnet18_diag")
+    ap.add_argument("--config", default="all", help="all (default) or one of " + ", ".join(ORDER))
     ap.add_argument("--pool", type=int, default=2, help="pre-loaded input batches cycled by the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -376,28 +417,44 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.config not in synth.CONFIG_NAMES:
-        print(f"unknown config {args.config}; choose from {synth.CONFIG_NAMES}", file=sys.stderr)
+    names = ORDER if args.config == "all" else (args.config,)
+    if any(n not in synth.CONFIG_NAMES for n in names):
+        print(f"unknown config {args.config}; choose all or one of {synth.CONFIG_NAMES}", file=sys.stderr)
         sys.exit(2)
     if args.traffic_probe:
         traffic_probe(args)
         return
-    cfg = synth.full_config(args.config)
-    log(f"[bench] {cfg.name}: {len(cfg.layers)} layers, {cfg.n_params} params")
-    if cfg.variant == "diag":
-        res = run_diag(cfg, args)
-    else:
-        res = run_full(cfg, args)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline_diag(cfg) if cfg.variant == "diag" else cpu_baseline_full(cfg)
-    line = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
-            "steps": res.get("steps", args.steps),
-            "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": workload_desc(cfg),
-            "roofline": res["roofline"], "cpu_baseline": cpu, "phases": res.get("phases")}
+    results = {}
+    for name in names:
+        cfg = synth.full_config(name)
+        log(f"[bench] {cfg.name}: {len(cfg.layers)} layers, {cfg.n_params} params")
+        res = run_diag(cfg, args) if cfg.variant == "diag" else run_full(cfg, args)
+        res["config"] = workload_desc(cfg)
+        if not args.no_cpu_baseline:
+            log(f"[bench] {cfg.name}: timing the CPU oracle")
+            res["cpu_baseline"] = cpu_baseline_diag(cfg) if cfg.variant == "diag" else cpu_baseline_full(cfg)
+        results[name] = res
+
+    head = HEADLINE if HEADLINE in results else names[0]
+    h = results[head]
+    if "a7_diag_factors" in h:
+        d = h["a7_diag_factors"]
+        roof = {"bound": "hbm", "kernel": "a7 diagonal factors: " + d["kernels"], "achieved": d["GBps"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
+                "traffic": measured_traffic() if head == HEADLINE else None,
+                "bytes_per_launch": d["bytes"], "avg_launch_ms": d["ms"]}
+    else:
+        phases = {p: h[p] for p in ("factors", "precond_update", "invert")}
+        dom = max(phases, key=lambda p: phases[p]["ms"] / (h["refresh_every"] if p == "invert" else 1))
+        d = phases[dom]
+        roof = {"bound": "mfma", "kernel": dom, "achieved": d["tflops"], "peak": d["peak_tflops"], "unit": "TFLOP/s",
+                "frac": d["frac"], "traffic": None, "flops_per_launch": d["flops"], "avg_launch_ms": d["ms"]}
+    line = {"metric": METRIC, "value": h["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": h["steps"],
+            "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": h["dtype"], "data": "synthetic", "config": h["config"],
+            "roofline": roof, "cpu_baseline": h.get("cpu_baseline"),
+            "configs": {n: {k: v for k, v in r.items() if k != "config"} for n, r in results.items()}}
     print(json.dumps(line), flush=True)
 
 
