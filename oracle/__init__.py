@@ -24,6 +24,12 @@ from .kfac import (  # noqa: F401
     diag_factors,
     step_full,
     step_diag,
+    step_bn,
+    bn_fisher,
+    rescale_weights,
+    schedule,
+    pack_upper,
+    unpack_upper,
     aug_weight,
     split_weight,
 )

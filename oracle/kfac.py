@@ -35,7 +35,21 @@ where it is used):
   R7  weight decay is added after preconditioning: D = P + wd * W;
   R8  heavy-ball momentum without dampening: V = mu V + D, W = W - lr V;
   R9  diagonal variant: EMA of the per-parameter product dG[o] * dA[j],
-      preconditioner 1 / (F + lambda), no square root, no bias correction.
+      preconditioner 1 / (F + lambda), no square root, no bias correction;
+  R17 batch normalisation [KFAC sections 1 and 5.4: its Fisher approximated
+      as diagonal]: the diagonal of the Fisher of gamma and beta from
+      per-sample gradients, mean over samples of (sum_hw g x_hat)^2 and of
+      (sum_hw g)^2, with the same EMA / damping / momentum tail (damping
+      scaled for batch-norm layers, section 4.2);
+  R18 weight rescaling [KFAC section 4.4]: after the update the layer's
+      weight (bias excluded) is scaled to Frobenius norm sqrt(2 d_out), the
+      norm of a He-initialised d_out x d_in weight; epsilon in the divisor;
+  R19 warm-up damping [KFAC section 4.2]: from gamma(0) to gamma_target over
+      t_warmup steps, linearly (or geometrically), then constant;
+  R20 refresh schedule [KFAC sections 1 and 5.4]: both inverses every step
+      for the first steps, then A and G on their own intervals;
+  R21 packed factor storage [KFAC section 3.4]: the upper triangle, row by
+      row, d (d + 1) / 2 entries.
 """
 from __future__ import annotations
 
@@ -198,24 +212,86 @@ def split_weight(wa: np.ndarray, has_bias: bool):
     return wa, None
 
 
+def bn_fisher(xhat: np.ndarray, g: np.ndarray):
+    """Diagonal Fisher of a batch-norm layer's affine parameters [KFAC
+    sections 1 and 5.4, R17].  With y = gamma x_hat + beta per channel, sample
+    b's gradients are dgamma_b[c] = sum_hw g[b, c] x_hat[b, c] and
+    dbeta_b[c] = sum_hw g[b, c]; the Fisher diagonal is their mean square over
+    the samples.  xhat, g: [B, C, H, W].  Returns (f_gamma [C], f_beta [C])."""
+    xhat = widen(xhat)
+    g = widen(g)
+    dgamma = (g * xhat).sum(axis=(2, 3))      # [B, C]
+    dbeta = g.sum(axis=(2, 3))
+    return (dgamma * dgamma).mean(axis=0), (dbeta * dbeta).mean(axis=0)
+
+
+def rescale_weights(w: np.ndarray, d_out: int, eps: float) -> np.ndarray:
+    """Weight rescaling after the update [KFAC section 4.4, R18]:
+    W sqrt(2 d_out) / (||W||_F + eps)."""
+    w = np.asarray(w, np.float64)
+    return w * (np.sqrt(2.0 * d_out) / (np.linalg.norm(w) + eps))
+
+
+def schedule(sched: dict, t: int):
+    """Per-step damping and refresh choice [KFAC section 4.2 (R19), sections 1
+    and 5.4 (R20)] for step t >= 1.  ``sched`` keys: damping_init,
+    damping_target, warmup_steps, warmup_shape ("linear" | "geometric"),
+    bn_damping_scale, dense_steps, refresh_every_a, refresh_every_g.
+    Returns (damping, damping_bn, refresh_A, refresh_G)."""
+    g0, gt, tw = sched["damping_init"], sched["damping_target"], sched["warmup_steps"]
+    u = 1.0 if tw == 0 else min(t - 1, tw) / tw
+    if sched["warmup_shape"] == "linear":
+        lam = g0 + (gt - g0) * u
+    else:
+        lam = g0 * (gt / g0) ** u
+    D = max(sched["dense_steps"], 1)
+    ra = t <= D or (t - D) % sched["refresh_every_a"] == 0
+    rg = t <= D or (t - D) % sched["refresh_every_g"] == 0
+    return lam, sched["bn_damping_scale"] * lam, ra, rg
+
+
+def pack_upper(M: np.ndarray) -> np.ndarray:
+    """Packed storage of a symmetric factor [KFAC section 3.4, R21]: the upper
+    triangle, row after row (row i contributes M[i, i:])."""
+    M = np.asarray(M)
+    return np.concatenate([M[i, i:] for i in range(M.shape[0])])
+
+
+def unpack_upper(p: np.ndarray, d: int) -> np.ndarray:
+    """The symmetric d x d matrix whose packed upper triangle is p."""
+    p = np.asarray(p)
+    M = np.zeros((d, d), p.dtype)
+    k = 0
+    for i in range(d):
+        M[i, i:] = p[k:k + d - i]
+        k += d - i
+    return M + np.triu(M, 1).T
+
+
 # ---------------------------------------------------------------------------
 # whole steps
 
-def step_full(layer, state: dict, inputs: dict, hp: dict, refresh: bool):
+def step_full(layer, state: dict, inputs: dict, hp: dict, refresh):
     """One full K-FAC step for one layer, in the order the pages give
     [KFAC section 3.2; CAFIN Kernel Fusion Strategy]:
 
       1. rows a_bar, g of this batch (R1-R3);
       2. A <- ema(A, a_bar^T a_bar / N), G <- ema(G, g^T g / N);
       3. on a refresh step: A_inv = (A + lambda I)^-1, G_inv = (G + lambda I)^-1
-         (R5, R6); a factor that is not positive definite keeps its previous
-         inverse and raises FLAG_NOT_PD;
+         (R5, R6); ``refresh`` is a bool (both) or a pair (A, G) (R20); a
+         factor that is not positive definite keeps its previous inverse and
+         raises FLAG_NOT_PD;
       4. P = G_inv . grad_W_aug . A_inv;
-      5. D = P + wd W_aug; V <- mu V + D; W_aug <- W_aug - lr V (R7, R8).
+      5. D = P + wd W_aug; V <- mu V + D; W_aug <- W_aug - lr V (R7, R8);
+      6. with hp["rescale"], W <- rescale_weights(W) (R18).
 
-    ``state`` holds w, mom_w, A, G, A_inv, G_inv (+ b, mom_b with a bias);
-    ``inputs`` holds a, g, grad_w (+ grad_b).  Returns (new_state, flags),
-    new arrays in float64."""
+    A batch-norm layer (kind "bn") takes the diagonal step of step_bn instead
+    (R17).  ``state`` holds w, mom_w, A, G, A_inv, G_inv (+ b, mom_b with a
+    bias); ``inputs`` holds a, g, grad_w (+ grad_b).  Returns (new_state,
+    flags), new arrays in float64."""
+    if layer.kind == "bn":
+        return step_bn(layer, state, inputs, hp)
+    ref_a, ref_g = (refresh, refresh) if isinstance(refresh, (bool, np.bool_, int)) else refresh
     eps, lam = hp["ema_decay"], hp["damping"]
     abar, grows = layer_rows(layer, inputs["a"], inputs["g"])
     A = ema(state["A"], kronecker_factor(abar), eps)
@@ -223,11 +299,12 @@ def step_full(layer, state: dict, inputs: dict, hp: dict, refresh: bool):
     A_inv = np.asarray(state["A_inv"], np.float64)
     G_inv = np.asarray(state["G_inv"], np.float64)
     flags = 0
-    if refresh:
+    if ref_a:
         try:
             A_inv = damped_inverse(A, lam)
         except np.linalg.LinAlgError:
             flags |= FLAG_NOT_PD
+    if ref_g:
         try:
             G_inv = damped_inverse(G, lam)
         except np.linalg.LinAlgError:
@@ -242,6 +319,8 @@ def step_full(layer, state: dict, inputs: dict, hp: dict, refresh: bool):
         flags |= FLAG_NONFINITE
     w, b = split_weight(W, has_bias)
     mw, mb = split_weight(V, has_bias)
+    if hp.get("rescale"):
+        w = rescale_weights(w, np.shape(state["w"])[0], hp["rescale_eps"])
     out = {"A": A, "G": G, "A_inv": A_inv, "G_inv": G_inv, "P": P,
            "w": w.reshape(np.shape(state["w"])), "mom_w": mw.reshape(np.shape(state["w"]))}
     if has_bias:
@@ -249,22 +328,15 @@ def step_full(layer, state: dict, inputs: dict, hp: dict, refresh: bool):
     return out, flags
 
 
-def step_diag(layer, state: dict, inputs: dict, hp: dict):
-    """One AdaFisher-style diagonal step for one layer [CAFIN Introduction and
-    Kernel Fusion Strategy, R9]:
-
-      1. dA, dG from this batch;
-      2. F <- beta F + (1 - beta) dG[o] dA[j]   (per parameter, [W | b] layout);
-      3. P = grad_W_aug / (F + lambda);
-      4. D = P + wd W_aug; V <- mu V + D; W_aug <- W_aug - lr V.
-
-    ``state`` holds w, mom_w, F_w (+ b, mom_b, F_b).  Returns
-    (new_state, flags) with dA, dG included."""
-    beta, lam = hp["ema_decay"], hp["damping"]
-    dA, dG = diag_factors(layer, inputs["a"], inputs["g"])
+def _diagonal_tail(layer, state: dict, inputs: dict, hp: dict, target: np.ndarray, lam: float):
+    """The elementwise part of a diagonal step [CAFIN Kernel Fusion Strategy,
+    R7-R9]: F <- beta F + (1 - beta) target (per parameter, [W | b] layout);
+    P = grad_W_aug / (F + lambda); D = P + wd W_aug; V <- mu V + D;
+    W_aug <- W_aug - lr V.  Returns (out, flags) with w, mom_w, F_w (+ b,
+    mom_b, F_b)."""
     has_bias = layer.has_bias
     F = aug_weight(state["F_w"], state.get("F_b") if has_bias else None)
-    F = ema(F, np.outer(dG, dA), beta)
+    F = ema(F, target, hp["ema_decay"])
     grad = aug_weight(inputs["grad_w"], inputs.get("grad_b") if has_bias else None)
     W = aug_weight(state["w"], state.get("b") if has_bias else None)
     V = aug_weight(state["mom_w"], state.get("mom_b") if has_bias else None)
@@ -275,8 +347,43 @@ def step_diag(layer, state: dict, inputs: dict, hp: dict):
     w, b = split_weight(W, has_bias)
     mw, mb = split_weight(V, has_bias)
     fw, fb = split_weight(F, has_bias)
-    out = {"dA": dA, "dG": dG, "P": P, "w": w.reshape(shape), "mom_w": mw.reshape(shape),
-           "F_w": fw.reshape(shape)}
+    out = {"P": P, "w": w.reshape(shape), "mom_w": mw.reshape(shape), "F_w": fw.reshape(shape)}
     if has_bias:
         out["b"], out["mom_b"], out["F_b"] = b, mb, fb
+    return out, flags
+
+
+def step_diag(layer, state: dict, inputs: dict, hp: dict):
+    """One AdaFisher-style diagonal step for one layer [CAFIN Introduction and
+    Kernel Fusion Strategy, R9]:
+
+      1. dA, dG from this batch;
+      2. F <- beta F + (1 - beta) dG[o] dA[j]   (per parameter, [W | b] layout);
+      3. P = grad_W_aug / (F + lambda);
+      4. D = P + wd W_aug; V <- mu V + D; W_aug <- W_aug - lr V;
+      5. with hp["rescale"], W <- rescale_weights(W) (R18).
+
+    A batch-norm layer (kind "bn") takes step_bn.  ``state`` holds w, mom_w,
+    F_w (+ b, mom_b, F_b).  Returns (new_state, flags) with dA, dG included."""
+    if layer.kind == "bn":
+        return step_bn(layer, state, inputs, hp)
+    dA, dG = diag_factors(layer, inputs["a"], inputs["g"])
+    out, flags = _diagonal_tail(layer, state, inputs, hp, np.outer(dG, dA), hp["damping"])
+    if hp.get("rescale"):
+        out["w"] = rescale_weights(out["w"], np.shape(state["w"])[0], hp["rescale_eps"])
+    out["dA"], out["dG"] = dA, dG
+    return out, flags
+
+
+def step_bn(layer, state: dict, inputs: dict, hp: dict):
+    """One step of a batch-norm layer's affine parameters, the diagonal way
+    [KFAC sections 1 and 5.4, R17] in both methods: the Fisher diagonal of
+    gamma (weight, [C, 1]) and beta (bias, [C]) from bn_fisher, its EMA, the
+    division by (F + damping_bn) (section 4.2: the batch-norm damping) and
+    the momentum update; no rescaling.  Returns (new_state, flags) with
+    dA = the gamma diagonal and dG = the beta diagonal."""
+    f_gamma, f_beta = bn_fisher(inputs["a"], inputs["g"])
+    target = np.stack([f_gamma, f_beta], axis=1)[:, :2 if layer.has_bias else 1]
+    out, flags = _diagonal_tail(layer, state, inputs, hp, target, hp["damping_bn"])
+    out["dA"], out["dG"] = f_gamma, f_beta
     return out, flags

@@ -558,9 +558,146 @@ def pin_full_step_exact_rational(O) -> bool:
     return bool(ok)
 
 
+# ---------------------------------------------------------------------------
+# batch normalisation (diagonal Fisher), weight rescaling, schedule, packing
+
+def pin_bn_fisher_autograd(O, seed=16) -> bool:
+    """The batch-norm Fisher diagonal equals the mean over samples of the
+    squared per-sample gradients of gamma and beta, each computed by torch
+    autograd (float64, CPU) through y = gamma x_hat + beta with the sample's
+    loss sum(g_b * y_b); a constant x_hat = 1, g = c gives (H W c)^2 exactly."""
+    rng = np.random.default_rng(seed)
+    B, C, H, W = 3, 2, 2, 3
+    xhat = rng.standard_normal((B, C, H, W))
+    g = rng.standard_normal((B, C, H, W))
+    gamma = torch.tensor(rng.standard_normal(C), requires_grad=True)
+    beta = torch.tensor(rng.standard_normal(C), requires_grad=True)
+    sq_g, sq_b = np.zeros(C), np.zeros(C)
+    for b in range(B):
+        y = gamma[:, None, None] * torch.from_numpy(xhat[b]) + beta[:, None, None]
+        dg, db = torch.autograd.grad((torch.from_numpy(g[b]) * y).sum(), (gamma, beta))
+        sq_g += dg.numpy() ** 2
+        sq_b += db.numpy() ** 2
+    fg, fb = O.bn_fisher(xhat.astype(np.float32), g.astype(np.float32))
+    fg32, fb32 = O.bn_fisher(xhat, g)
+    ones = np.ones((2, 3, 4, 5))
+    cg, cb = O.bn_fisher(ones, 0.5 * ones)
+    return (np.allclose(fg32, sq_g / B, rtol=1e-12) and np.allclose(fb32, sq_b / B, rtol=1e-12)
+            and fg.shape == (C,) and np.allclose(fg, fg32, rtol=1e-5)
+            and np.array_equal(cg, np.full(3, 100.0)) and np.array_equal(cb, np.full(3, 100.0)))
+
+
+def pin_bn_step_closed_form(O, seed=17) -> bool:
+    """A batch-norm step at EMA decay 0: F becomes the Fisher diagonal
+    (gamma in the weight column, beta in the bias column), the gradient is
+    divided by F + damping_bn (not the layer damping), then the momentum
+    update, element by element; dA / dG carry the two diagonals."""
+    rng = np.random.default_rng(seed)
+    B, C, H, W = 4, 3, 2, 2
+    xhat = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    g = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    x64, g64 = xhat.astype(np.float64), g.astype(np.float64)
+    fg = np.array([np.mean([np.sum(g64[b, c] * x64[b, c]) ** 2 for b in range(B)]) for c in range(C)])
+    fb = np.array([np.mean([np.sum(g64[b, c]) ** 2 for b in range(B)]) for c in range(C)])
+    geo = Geo("bn", True)
+    st = {"w": rng.standard_normal((C, 1)), "b": rng.standard_normal(C), "mom_w": rng.standard_normal((C, 1)),
+          "mom_b": rng.standard_normal(C), "F_w": np.full((C, 1), 5.0), "F_b": np.full(C, 5.0)}
+    inp = {"a": xhat, "g": g, "grad_w": rng.standard_normal((C, 1)), "grad_b": rng.standard_normal(C)}
+    hp = {"lr": 0.1, "momentum": 0.9, "weight_decay": 1e-2, "ema_decay": 0.0, "damping": 7.0, "damping_bn": 0.05}
+    out, flags = O.step_bn(geo, st, inp, hp)
+    ok = flags == 0 and np.allclose(out["dA"], fg, rtol=1e-12) and np.allclose(out["dG"], fb, rtol=1e-12)
+    for c in range(C):
+        for key, wk, vk, fk, f in (("grad_w", "w", "mom_w", "F_w", fg[c]), ("grad_b", "b", "mom_b", "F_b", fb[c])):
+            gr = np.ravel(inp[key])[c]
+            w0, v0 = np.ravel(st[wk])[c], np.ravel(st[vk])[c]
+            v1 = 0.9 * v0 + gr / (f + 0.05) + 1e-2 * w0
+            ok &= np.isclose(np.ravel(out[fk])[c], f, rtol=1e-12)
+            ok &= np.isclose(np.ravel(out[vk])[c], v1, rtol=1e-12) and np.isclose(np.ravel(out[wk])[c], w0 - 0.1 * v1,
+                                                                                  rtol=1e-12)
+    return bool(ok)
+
+
+def pin_rescale_norm(O, seed=18) -> bool:
+    """Rescaled weights point the same way with Frobenius norm
+    sqrt(2 d_out) ||W|| / (||W|| + eps) (np.linalg.norm); a He-initialised
+    d_out x d_in weight (std sqrt(2 / d_in)) is left almost unchanged, which
+    fixes d_out (not d_in) in the target; in a full step only the weight is
+    rescaled, the bias is not."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((30, 7))
+    ok = True
+    for eps in (0.0, 1e-9, 0.5):
+        R = O.rescale_weights(W, 30, eps)
+        n = np.linalg.norm(W)
+        ok &= np.isclose(np.linalg.norm(R), np.sqrt(60.0) * n / (n + eps), rtol=1e-13)
+        ok &= np.isclose(np.sum(R * W) / (np.linalg.norm(R) * n), 1.0, rtol=1e-13)
+    He = rng.standard_normal((400, 50)) * np.sqrt(2.0 / 50)
+    ratio = np.linalg.norm(O.rescale_weights(He, 400, 1e-9)) / np.linalg.norm(He)
+    ok &= abs(ratio - 1.0) < 0.02
+    geo = Geo("linear", True)
+    st = {"w": rng.standard_normal((3, 4)), "b": rng.standard_normal(3), "mom_w": np.zeros((3, 4)), "mom_b": np.zeros(3),
+          "A": np.eye(5), "G": np.eye(3), "A_inv": np.eye(5), "G_inv": np.eye(3)}
+    inp = {"a": rng.standard_normal((6, 4)), "g": rng.standard_normal((6, 3)), "grad_w": rng.standard_normal((3, 4)),
+           "grad_b": rng.standard_normal(3)}
+    hp = {"lr": 0.1, "momentum": 0.9, "weight_decay": 0.0, "ema_decay": 0.5, "damping": 0.1, "rescale_eps": 1e-9}
+    plain, _ = O.step_full(geo, st, inp, hp, False)
+    resc, _ = O.step_full(geo, st, inp, dict(hp, rescale=True), False)
+    ok &= np.isclose(np.linalg.norm(resc["w"]), np.sqrt(6.0), rtol=1e-9)
+    ok &= np.array_equal(resc["b"], plain["b"]) and np.allclose(resc["w"] / np.linalg.norm(resc["w"]),
+                                                                  plain["w"] / np.linalg.norm(plain["w"]), rtol=1e-12)
+    return bool(ok)
+
+
+def pin_schedule(O) -> bool:
+    """Warm-up damping: step 1 uses gamma(0), steps after t_warmup the target;
+    the mid-warm-up step takes the arithmetic (linear) or geometric
+    (geometric) mean; the damping never increases; batch norm scales it by
+    rho_BN.  Refresh: step 1 and the dense steps refresh both; over steps
+    1..T the number of A refreshes is D + floor((T - D) / k_A) (and G's with
+    k_G), with refreshes exactly k apart after the dense steps."""
+    ok = True
+    for shape in ("linear", "geometric"):
+        s = {"damping_init": 0.04, "damping_target": 0.0025, "warmup_steps": 10, "warmup_shape": shape,
+             "bn_damping_scale": 16.0, "dense_steps": 7, "refresh_every_a": 5, "refresh_every_g": 3}
+        lam = [O.schedule(s, t)[0] for t in range(1, 30)]
+        mid = O.schedule(s, 6)[0]
+        ok &= lam[0] == 0.04 and all(abs(x - 0.0025) < 1e-15 for x in lam[10:])
+        ok &= all(b <= a + 1e-18 for a, b in zip(lam, lam[1:]))
+        ok &= np.isclose(mid, (0.04 + 0.0025) / 2 if shape == "linear" else np.sqrt(0.04 * 0.0025), rtol=1e-12)
+        ok &= np.isclose(O.schedule(s, 3)[1], 16.0 * O.schedule(s, 3)[0], rtol=1e-15)
+        T = 40
+        ra = [t for t in range(1, T + 1) if O.schedule(s, t)[2]]
+        rg = [t for t in range(1, T + 1) if O.schedule(s, t)[3]]
+        ok &= len(ra) == 7 + (T - 7) // 5 and len(rg) == 7 + (T - 7) // 3
+        ok &= ra[:7] == list(range(1, 8)) and all(b - a == 5 for a, b in zip(ra[6:], ra[7:]))
+        ok &= all(b - a == 3 for a, b in zip(rg[6:], rg[7:]))
+    s0 = {"damping_init": 1.0, "damping_target": 0.5, "warmup_steps": 0, "warmup_shape": "linear",
+          "bn_damping_scale": 1.0, "dense_steps": 0, "refresh_every_a": 4, "refresh_every_g": 4}
+    ok &= O.schedule(s0, 1)[0] == 0.5 and O.schedule(s0, 1)[2] and O.schedule(s0, 1)[3]
+    ok &= [t for t in range(1, 12) if O.schedule(s0, t)[2]] == [1, 5, 9]
+    return bool(ok)
+
+
+def pin_pack_upper(O, seed=19) -> bool:
+    """Packed storage lists the upper triangle row by row: enumerating the
+    pairs i <= j in row-major order gives the same sequence; d (d + 1) / 2
+    entries; unpacking restores a symmetric matrix."""
+    rng = np.random.default_rng(seed)
+    ok = True
+    for d in (1, 2, 5, 8):
+        M = rng.standard_normal((d, d))
+        M = M + M.T
+        p = O.pack_upper(M)
+        ref = [M[i, j] for i in range(d) for j in range(d) if i <= j]
+        ok &= p.shape == (d * (d + 1) // 2,) and np.array_equal(p, np.array(ref))
+        ok &= np.array_equal(O.unpack_upper(p, d), M)
+    return bool(ok)
+
+
 ALL_PINS = [pin_full_step_exact_rational, pin_unfold_direct_conv, pin_unfold_library, pin_factor_outer_products, pin_factor_hadamard,
             pin_bias_column, pin_conv_rows, pin_unfold_column_library, pin_layer_columns, pin_bf16_widen, pin_ema_closed_form,
             pin_inverse_sherman_morrison, pin_inverse_diagonal_and_residual, pin_inverse_not_pd_raises,
             pin_kronecker_identity, pin_full_step_hadamard, pin_sgd_reduction,
             pin_momentum_constant_direction, pin_diag_is_factor_diagonal, pin_diag_conv_window_sums,
-            pin_diag_step_closed_form, pin_refresh_keeps_inverses]
+            pin_diag_step_closed_form, pin_refresh_keeps_inverses, pin_bn_fisher_autograd,
+            pin_bn_step_closed_form, pin_rescale_norm, pin_schedule, pin_pack_upper]

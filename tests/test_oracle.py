@@ -144,11 +144,38 @@ def _mut_activation_column_bias(M):
     M.activation_column = activation_column
 
 
+def _mut_bn_fisher_per_element(M):
+    def bn_fisher(xhat, g):
+        x, gg = M.widen(xhat), M.widen(g)
+        return ((gg * x) ** 2).sum(axis=(2, 3)).mean(axis=0), (gg ** 2).sum(axis=(2, 3)).mean(axis=0)
+    M.bn_fisher = bn_fisher
+
+
+def _mut_bn_layer_damping(M):
+    orig = M.step_bn
+    M.step_bn = lambda layer, state, inputs, hp: orig(layer, state, inputs, dict(hp, damping_bn=hp["damping"]))
+
+
+def _mut_rescale_d_in(M):
+    M.rescale_weights = lambda w, d_out, eps: (np.asarray(w, np.float64) * np.sqrt(2.0 * np.shape(w)[1]) /
+                                                (np.linalg.norm(w) + eps))
+
+
+def _mut_schedule_off_by_one(M):
+    orig = M.schedule
+    M.schedule = lambda s, t: orig(s, t + 1)
+
+
+def _mut_pack_by_columns(M):
+    M.pack_upper = lambda A: np.concatenate([np.asarray(A)[:j + 1, j] for j in range(np.shape(A)[0])])
+
+
 MUTANTS = [_mut_unfold_order, _mut_unfold_no_pad_shift, _mut_factor_norm, _mut_factor_transpose,
            _mut_ema_swap, _mut_inverse_no_damping, _mut_inverse_wrong_product, _mut_precond_drop_A,
            _mut_precond_squared, _mut_wd_sign, _mut_dampening, _mut_nesterov, _mut_bias_first,
            _mut_diag_abs, _mut_widen_low_half, _mut_unfold_column_kh_kw,
-           _mut_gradient_column_order, _mut_activation_column_bias]
+           _mut_gradient_column_order, _mut_activation_column_bias, _mut_bn_fisher_per_element,
+           _mut_bn_layer_damping, _mut_rescale_d_in, _mut_schedule_off_by_one, _mut_pack_by_columns]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
