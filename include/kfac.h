@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KFAC_ABI_VERSION 1
+#define KFAC_ABI_VERSION 2
 
 typedef int32_t kfac_status_t;
 enum {
@@ -84,7 +84,9 @@ enum {
 };
 
 /* layer kinds */
-enum { KFAC_LINEAR = 0, KFAC_CONV2D = 1 };
+enum { KFAC_LINEAR = 0, KFAC_CONV2D = 1, KFAC_BATCHNORM = 2 };
+/* kfac_layer_t.factor_layout: storage of A and G (full method) */
+enum { KFAC_FACTORS_FULL = 0, KFAC_FACTORS_PACKED = 1 };
 /* element types of a / g (every other tensor is float32) */
 enum { KFAC_F32 = 0, KFAC_BF16 = 1 };
 /* kfac_workspace_size modes */
@@ -98,6 +100,11 @@ enum { KFAC_MODE_FULL = 0, KFAC_MODE_DIAG = 1 };
  *         dA / dG from those buffers (so an UPDATE-only call uses whatever
  *         they hold, e.g. the last FACTORS call's result). */
 enum { KFAC_PHASE_FACTORS = 1, KFAC_PHASE_INVERT = 2, KFAC_PHASE_UPDATE = 4, KFAC_PHASE_ALL = 7 };
+/* kfac_hparams_t.refresh bits (full method): which damped inverses this step
+ * recomputes */
+enum { KFAC_REFRESH_A = 1, KFAC_REFRESH_G = 2, KFAC_REFRESH_BOTH = 3 };
+/* kfac_hparams_t.options bits */
+enum { KFAC_OPT_RESCALE = 1 };
 /* sticky device flags */
 enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
 
@@ -110,17 +117,35 @@ enum { KFAC_FLAG_NOT_PD = 1u, KFAC_FLAG_NONFINITE = 2u };
  *            width), rows = batch * h_out * w_out; dilation 1, groups 1.
  *   d_a = d_in + (has_bias ? 1 : 0)   (the bias acts as a constant-1 input,
  *                                      appended as the last column)
+ *   batchnorm: the affine parameters gamma, beta of a batch-norm layer over
+ *            C channels (Osawa et al. section 1, "Curvature approximation",
+ *            and section 5.4: a diagonal Fisher for batch normalisation).
+ *            a = the normalised input x_hat [batch, C, height, width], g = the
+ *            per-sample output gradient [batch, C, height, width] (float32);
+ *            d_out = c_in = C, d_in = 1, rows = batch, kh = kw = stride = 1,
+ *            pad = 0; w = gamma, b = beta (has_bias), grad_w / grad_b their
+ *            gradients, all [C].  Both methods treat it the diagonal way:
+ *            dA[c] = mean_b (sum_hw g x_hat)^2 and dG[c] = mean_b (sum_hw g)^2
+ *            (the Fisher diagonal of gamma and of beta from per-sample
+ *            gradients), F_w / F_b their EMA, damping_bn in place of damping.
  *   Full method: a layer with float32 a or g, and every conv2d layer, has at
  *   most INT32_MAX rows (KFAC_ERR_UNSUPPORTED otherwise).
  *   grad_w, w, mom_w, F_w : [d_out, d_in] float32
  *   grad_b, b, mom_b, F_b : [d_out] float32, NULL iff has_bias == 0
  * Full method:  A, A_inv : [d_a, d_a]; G, G_inv : [d_out, d_out]  (float32,
- *               symmetric; the library reads the upper triangle of A and G and
- *               writes both triangles).  A, G are updated in place every step;
- *               A_inv, G_inv are written on refresh steps and read every step;
- *               the UPDATE phase reads them as symmetric matrices (either
- *               triangle, rows in place of columns), so inverses a caller
- *               supplies must be symmetric too.
+ *               symmetric; the library reads the upper triangle of A and G).
+ *               With factor_layout KFAC_FACTORS_FULL, A and G are stored
+ *               whole and the library writes both triangles; with
+ *               KFAC_FACTORS_PACKED only the upper triangle is stored, row
+ *               after row: element (i, j), i <= j, at i d - i (i - 1) / 2 +
+ *               (j - i), d (d + 1) / 2 floats (section 3.4: a symmetric factor
+ *               is carried as its N (N + 1) / 2 upper entries).  A, G are
+ *               updated in place every step; A_inv, G_inv (always whole) are
+ *               written on refresh steps and read every step; the UPDATE phase
+ *               reads them as symmetric matrices (either triangle, rows in
+ *               place of columns), so inverses a caller supplies must be
+ *               symmetric too.  Batch-norm layers use F_w, F_b, dA, dG [C]
+ *               instead (no factors).
  * Diag method:  F_w, F_b updated in place; dA [d_a], dG [d_out] are written by
  *               the FACTORS phase and read by the UPDATE phase.
  * Pointers a method does not use may be NULL.  w, mom_w, b, mom_b are updated
@@ -134,7 +159,9 @@ typedef struct kfac_layer {
   int64_t rows;        /* N */
   int32_t d_in;
   int32_t d_out;
-  int32_t batch, c_in, height, width, kh, kw, stride, pad;   /* conv2d only */
+  int32_t batch, c_in, height, width, kh, kw, stride, pad;   /* conv2d and batchnorm */
+  int32_t factor_layout;   /* KFAC_FACTORS_FULL | KFAC_FACTORS_PACKED (full method) */
+  int32_t reserved;        /* must be 0 */
   const void* a;
   const void* g;
   const float* grad_w;
@@ -154,17 +181,27 @@ typedef struct kfac_layer {
 } kfac_layer_t;
 
 /* Per-call scalars.  Schedules (warm-up damping, learning-rate decay, the
- * inverse-refresh policy) live with the caller: it passes this step's values. */
+ * inverse-refresh policy) live with the caller: it passes this step's values
+ * (kfac_schedule_hparams below computes the damping and refresh ones). */
 typedef struct kfac_hparams {
   float lr;
   float momentum;
   float weight_decay;
-  float ema_decay;     /* full: factor EMA decay; diag: F EMA decay */
-  float damping;       /* lambda */
-  int32_t refresh;     /* full: nonzero = recompute the damped inverses this step */
+  float ema_decay;     /* full: factor EMA decay; diag and batch-norm layers: F EMA decay */
+  float damping;       /* lambda of the conv / linear layers */
+  float damping_bn;    /* lambda of the batch-norm layers */
+  float rescale_eps;   /* epsilon of the weight rescaling (KFAC_OPT_RESCALE) */
+  int32_t refresh;     /* full: KFAC_REFRESH_* bits, the damped inverses recomputed this step */
   int32_t phase_mask;  /* KFAC_PHASE_* bits, 0 = all */
+  int32_t options;     /* KFAC_OPT_* bits */
   int32_t reserved;    /* must be 0 */
 } kfac_hparams_t;
+/* KFAC_OPT_RESCALE (Osawa et al. section 4.4, weights rescaling): after the
+ * update, the weight W (bias excluded) of every conv2d and linear layer is
+ * scaled in place to Frobenius norm sqrt(2 d_out):
+ *     W <- W sqrt(2 d_out) / (||W||_F + rescale_eps)
+ * d_out = the layer's output width (channels of a conv2d).  Batch-norm
+ * parameters are not rescaled.  Runs as part of the UPDATE phase. */
 
 /* Bytes of workspace the given stack needs in `mode` (host only, no GPU
  * call).  Returns KFAC_ERR_ARG / _DTYPE / _UNSUPPORTED for descriptors the
@@ -174,11 +211,15 @@ kfac_status_t kfac_workspace_size(const kfac_layer_t* layers, int32_t n_layers, 
 
 /* Enqueue one full K-FAC step for all layers on `stream`:
  *   [FACTORS] A <- ema_decay A + (1 - ema_decay) a_bar^T a_bar / N, same for G
- *   [INVERT]  if refresh: A_inv = (A + damping I)^-1, G_inv = (G + damping I)^-1
- *             by Cholesky; a factor that is not positive definite keeps its
+ *             (batch-norm layers: their dA, dG)
+ *   [INVERT]  A_inv = (A + damping I)^-1 when refresh has KFAC_REFRESH_A,
+ *             G_inv = (G + damping I)^-1 when it has KFAC_REFRESH_G, by
+ *             Cholesky; a factor that is not positive definite keeps its
  *             previous inverse and sets KFAC_FLAG_NOT_PD
  *   [UPDATE]  P = G_inv [grad_w | grad_b] A_inv; D = P + wd W; V = mu V + D;
- *             W = W - lr V  (w, b, mom_w, mom_b in place)
+ *             W = W - lr V  (w, b, mom_w, mom_b in place); batch-norm layers
+ *             take the diagonal step of kfac_step_diag with damping_bn; then
+ *             the weight rescaling when options has KFAC_OPT_RESCALE
  * Layers are processed in order; phases are ordered as listed. */
 kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                              void* workspace, size_t ws_bytes, void* stream);
@@ -186,8 +227,11 @@ kfac_status_t kfac_step_full(const kfac_layer_t* layers, int32_t n_layers, const
 /* Enqueue one diagonal step for all layers on `stream`:
  *   [FACTORS] dA[j] = mean_n a_bar[n, j]^2 (conv: over the unfolded rows,
  *             which are never materialised), dG[o] = mean_n g[n, o]^2
- *   [UPDATE]  in one pass F = beta F + (1 - beta) dG[o] dA[j];
- *             P = grad / (F + damping); D = P + wd W; V = mu V + D; W = W - lr V */
+ *             (batch-norm layers: the per-channel Fisher diagonals above)
+ *   [UPDATE]  in one pass F = beta F + (1 - beta) dG[o] dA[j] (batch norm:
+ *             dA[c] for gamma, dG[c] for beta);
+ *             P = grad / (F + damping); D = P + wd W; V = mu V + D; W = W - lr V;
+ *             then the weight rescaling when options has KFAC_OPT_RESCALE */
 kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                              void* workspace, size_t ws_bytes, void* stream);
 
@@ -208,6 +252,37 @@ kfac_status_t kfac_step_diag(const kfac_layer_t* layers, int32_t n_layers, const
 #define KFAC_NOALLOC_SCRATCH_BYTES (32u << 20)
 kfac_status_t kfac_step_diag_noalloc(const kfac_layer_t* layers, int32_t n_layers, const kfac_hparams_t* hp,
                                      uint32_t* flags, void* stream);
+
+/* Host-side schedule of the per-step scalars (no GPU call).
+ *   Warm-up damping (Osawa et al. section 4.2): the damping starts at
+ *   damping_init and decreases to damping_target over warmup_steps steps,
+ *   then stays there.  Step t (1-based) uses u = min(t - 1, warmup_steps) /
+ *   warmup_steps (u = 1 when warmup_steps is 0) and
+ *       LINEAR:    damping = init + (target - init) u
+ *       GEOMETRIC: damping = init (target / init)^u
+ *   Batch-norm layers use bn_damping_scale (rho_BN > 1 on the page) times it.
+ *   Inverse refresh (sections 1 and 5.4: the Fisher changes fast early on, so
+ *   refreshes are reduced only after the first few hundred steps, and A
+ *   changes less than G): steps 1 .. max(dense_steps, 1) refresh both
+ *   inverses; after that, with D = max(dense_steps, 1), A is refreshed at the
+ *   steps t with (t - D) a multiple of refresh_every_a, G likewise with
+ *   refresh_every_g.
+ * kfac_schedule_hparams writes damping, damping_bn and refresh of *hp for
+ * step `step` (>= 1) and leaves the other fields alone; KFAC_ERR_ARG for a
+ * step below 1, a negative warmup, intervals below 1, a non-positive damping
+ * (geometric shape) or an unknown shape. */
+enum { KFAC_WARMUP_LINEAR = 0, KFAC_WARMUP_GEOMETRIC = 1 };
+typedef struct kfac_schedule {
+  float damping_init;       /* gamma(0) */
+  float damping_target;     /* gamma_target */
+  int32_t warmup_steps;     /* t_warmup */
+  int32_t warmup_shape;     /* KFAC_WARMUP_LINEAR | KFAC_WARMUP_GEOMETRIC */
+  float bn_damping_scale;   /* rho_BN */
+  int32_t dense_steps;      /* steps that refresh both inverses every step */
+  int32_t refresh_every_a;  /* then: A inverse every this many steps */
+  int32_t refresh_every_g;  /* and G inverse every this many steps */
+} kfac_schedule_t;
+kfac_status_t kfac_schedule_hparams(const kfac_schedule_t* schedule, int64_t step, kfac_hparams_t* hp);
 
 /* Copy the workspace's sticky flag word to *flags (waits for `stream`), and
  * clear it on the device afterwards when `clear` is nonzero.  `workspace` may

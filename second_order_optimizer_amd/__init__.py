@@ -16,14 +16,18 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkfac.so")
 
 KFAC_OK, KFAC_ERR_ARG, KFAC_ERR_DTYPE, KFAC_ERR_ALIGN, KFAC_ERR_WORKSPACE, KFAC_ERR_UNSUPPORTED, KFAC_ERR_HIP = range(7)
-LINEAR, CONV2D = 0, 1
+LINEAR, CONV2D, BATCHNORM = 0, 1, 2
+FACTORS_FULL, FACTORS_PACKED = 0, 1
+REFRESH_A, REFRESH_G, REFRESH_BOTH = 1, 2, 3
+OPT_RESCALE = 1
+WARMUP_LINEAR, WARMUP_GEOMETRIC = 0, 1
 F32, BF16 = 0, 1
 MODE_FULL, MODE_DIAG = 0, 1
 PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE, PHASE_ALL = 1, 2, 4, 7
 FLAG_NOT_PD, FLAG_NONFINITE = 1, 2
 
 EXPORTS = ("kfac_workspace_size", "kfac_step_full", "kfac_step_diag", "kfac_step_diag_noalloc", "kfac_read_flags",
-           "kfac_status_string", "kfac_abi_version")
+           "kfac_schedule_hparams", "kfac_status_string", "kfac_abi_version")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -36,6 +40,7 @@ class Layer(ctypes.Structure):
         ("batch", ctypes.c_int32), ("c_in", ctypes.c_int32), ("height", ctypes.c_int32),
         ("width", ctypes.c_int32), ("kh", ctypes.c_int32), ("kw", ctypes.c_int32),
         ("stride", ctypes.c_int32), ("pad", ctypes.c_int32),
+        ("factor_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("a", ctypes.c_void_p), ("g", ctypes.c_void_p),
         ("grad_w", ctypes.c_void_p), ("grad_b", ctypes.c_void_p),
         ("w", ctypes.c_void_p), ("b", ctypes.c_void_p),
@@ -51,8 +56,18 @@ class HParams(ctypes.Structure):
     """Mirror of kfac_hparams_t."""
     _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float),
                 ("weight_decay", ctypes.c_float), ("ema_decay", ctypes.c_float),
-                ("damping", ctypes.c_float), ("refresh", ctypes.c_int32),
-                ("phase_mask", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("damping", ctypes.c_float), ("damping_bn", ctypes.c_float),
+                ("rescale_eps", ctypes.c_float), ("refresh", ctypes.c_int32),
+                ("phase_mask", ctypes.c_int32), ("options", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Schedule(ctypes.Structure):
+    """Mirror of kfac_schedule_t."""
+    _fields_ = [("damping_init", ctypes.c_float), ("damping_target", ctypes.c_float),
+                ("warmup_steps", ctypes.c_int32), ("warmup_shape", ctypes.c_int32),
+                ("bn_damping_scale", ctypes.c_float), ("dense_steps", ctypes.c_int32),
+                ("refresh_every_a", ctypes.c_int32), ("refresh_every_g", ctypes.c_int32)]
 
 
 class KfacError(RuntimeError):
@@ -83,6 +98,8 @@ def load() -> ctypes.CDLL:
     lib.kfac_step_diag_noalloc.restype = i32
     lib.kfac_read_flags.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32), i32]
     lib.kfac_read_flags.restype = i32
+    lib.kfac_schedule_hparams.argtypes = [ctypes.POINTER(Schedule), ctypes.c_int64, ctypes.POINTER(HParams)]
+    lib.kfac_schedule_hparams.restype = i32
     lib.kfac_status_string.argtypes = [i32]
     lib.kfac_status_string.restype = ctypes.c_char_p
     lib.kfac_abi_version.argtypes = []
@@ -123,8 +140,22 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def hparams(lr, momentum, weight_decay, ema_decay, damping, refresh=True, phase_mask=0) -> HParams:
-    return HParams(lr, momentum, weight_decay, ema_decay, damping, int(bool(refresh)), phase_mask, 0)
+def hparams(lr, momentum, weight_decay, ema_decay, damping, refresh=True, phase_mask=0, damping_bn=None,
+            rescale_eps=1e-9, options=0) -> HParams:
+    """refresh: True (both inverses), False, or KFAC_REFRESH_* bits;
+    damping_bn defaults to damping."""
+    bits = REFRESH_BOTH if refresh is True else (0 if refresh is False else int(refresh))
+    return HParams(lr, momentum, weight_decay, ema_decay, damping, damping if damping_bn is None else damping_bn,
+                   rescale_eps, bits, phase_mask, options, 0)
+
+
+def schedule_hparams(sched: Schedule, step: int, hp: HParams) -> HParams:
+    """kfac_schedule_hparams: fills damping, damping_bn and refresh of hp for
+    `step` (host only)."""
+    st = load().kfac_schedule_hparams(ctypes.byref(sched), step, ctypes.byref(hp))
+    if st != KFAC_OK:
+        raise KfacError(st, "kfac_schedule_hparams")
+    return hp
 
 
 def step_full(layers, hp: HParams, workspace: int, ws_bytes: int, stream=None) -> None:
@@ -167,7 +198,8 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_layer(kind: int, d_in: int, d_out: int, rows: int, has_bias: bool, *, act_dtype=F32, grad_dtype=F32,
-               batch=0, c_in=0, height=0, width=0, k=0, stride=0, pad=0, **tensors) -> Layer:
+               batch=0, c_in=0, height=0, width=0, k=0, stride=0, pad=0, factor_layout=FACTORS_FULL,
+               **tensors) -> Layer:
     """Builds one descriptor; keyword tensors (torch, on the GPU) are taken by
     pointer: a, g, grad_w, grad_b, w, b, mom_w, mom_b, A, G, A_inv, G_inv,
     F_w, F_b, dA, dG.  The caller keeps the tensors alive."""
@@ -177,6 +209,7 @@ def make_layer(kind: int, d_in: int, d_out: int, rows: int, has_bias: bool, *, a
     L.batch, L.c_in, L.height, L.width = batch, c_in, height, width
     L.kh = L.kw = k
     L.stride, L.pad = stride, pad
+    L.factor_layout = factor_layout
     for name, t in tensors.items():
         if not hasattr(L, name):
             raise KeyError(name)

@@ -2,6 +2,8 @@
 // workspace sizing and dispatch to the diagonal and full launchers.
 #include "common.h"
 
+#include <algorithm>
+#include <cmath>
 #include <cstring>
 
 namespace kfac {
@@ -14,7 +16,9 @@ LayerGeom geom_of(const kfac_layer_t& L) {
   g.bias = L.has_bias != 0;
   g.d_a = L.d_in + (g.bias ? 1 : 0);
   g.conv = L.kind == KFAC_CONV2D;
-  if (g.conv) {
+  g.bn = L.kind == KFAC_BATCHNORM;
+  g.packed = L.factor_layout == KFAC_FACTORS_PACKED;
+  if (g.conv || g.bn) {
     g.batch = L.batch;
     g.c_in = L.c_in;
     g.h = L.height;
@@ -35,13 +39,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shape / dtype checks that do not look at pointers.
 kfac_status_t check_shape(const kfac_layer_t& L, int mode) {
-  if (L.kind != KFAC_LINEAR && L.kind != KFAC_CONV2D) return KFAC_ERR_ARG;
+  if (L.kind != KFAC_LINEAR && L.kind != KFAC_CONV2D && L.kind != KFAC_BATCHNORM) return KFAC_ERR_ARG;
   if (L.has_bias != 0 && L.has_bias != 1) return KFAC_ERR_ARG;
+  if (L.reserved != 0) return KFAC_ERR_ARG;
+  if (L.factor_layout != KFAC_FACTORS_FULL && L.factor_layout != KFAC_FACTORS_PACKED) return KFAC_ERR_ARG;
   if (L.act_dtype != KFAC_F32 && L.act_dtype != KFAC_BF16) return KFAC_ERR_DTYPE;
   if (L.grad_dtype != KFAC_F32 && L.grad_dtype != KFAC_BF16) return KFAC_ERR_DTYPE;
   if (L.d_in <= 0 || L.d_out <= 0 || L.rows <= 0) return KFAC_ERR_ARG;
   // int32 element indexing of parameter matrices and of per-sample planes
   if (static_cast<int64_t>(L.d_out) * (L.d_in + 1) >= (int64_t(1) << 31)) return KFAC_ERR_UNSUPPORTED;
+  if (L.kind == KFAC_BATCHNORM) {
+    // gamma, beta over C planes of height x width per sample
+    if (L.batch <= 0 || L.c_in <= 0 || L.height <= 0 || L.width <= 0) return KFAC_ERR_ARG;
+    if (L.d_in != 1 || L.d_out != L.c_in || L.rows != L.batch) return KFAC_ERR_ARG;
+    if (L.kh != 1 || L.kw != 1 || L.stride != 1 || L.pad != 0) return KFAC_ERR_ARG;
+    if (L.act_dtype != KFAC_F32 || L.grad_dtype != KFAC_F32) return KFAC_ERR_DTYPE;
+    if (static_cast<int64_t>(L.c_in) * L.height * L.width >= (int64_t(1) << 31)) return KFAC_ERR_UNSUPPORTED;
+    return KFAC_OK;
+  }
   if (L.kind == KFAC_CONV2D) {
     if (L.batch <= 0 || L.c_in <= 0 || L.height <= 0 || L.width <= 0 || L.kh <= 0 || L.kw <= 0 || L.stride <= 0 ||
         L.pad < 0)
@@ -75,18 +90,18 @@ kfac_status_t check_ptr(const void* p, bool required) {
   return aligned16(p) ? KFAC_OK : KFAC_ERR_ALIGN;
 }
 
-kfac_status_t check_layer_ptrs(const kfac_layer_t& L, int mode, int phases, bool refresh) {
+kfac_status_t check_layer_ptrs(const kfac_layer_t& L, int mode, int phases, int refresh) {
   const bool bias = L.has_bias != 0;
   kfac_status_t s;
   auto req = [&](const void* p, bool r) { return (s = check_ptr(p, r)) != KFAC_OK; };
   const bool fac = phases & KFAC_PHASE_FACTORS;
   const bool upd = phases & KFAC_PHASE_UPDATE;
-  const bool inv = (phases & KFAC_PHASE_INVERT) && refresh;
+  const bool inv = (phases & KFAC_PHASE_INVERT) && refresh != 0;
   if (req(L.a, fac) || req(L.g, fac)) return s;
   if (req(L.grad_w, upd) || req(L.w, upd) || req(L.mom_w, upd)) return s;
   if (bias && (req(L.grad_b, upd) || req(L.b, upd) || req(L.mom_b, upd))) return s;
   if (!bias && (L.grad_b || L.b || L.mom_b || L.F_b)) return KFAC_ERR_ARG;
-  if (mode == KFAC_MODE_FULL) {
+  if (mode == KFAC_MODE_FULL && L.kind != KFAC_BATCHNORM) {
     if (req(L.A, fac || inv) || req(L.G, fac || inv)) return s;
     if (req(L.A_inv, inv || upd) || req(L.G_inv, inv || upd)) return s;
   } else {
@@ -113,9 +128,11 @@ kfac_status_t validate(const kfac_layer_t* layers, int32_t n, const kfac_hparams
   if (s != KFAC_OK) return s;
   if (!hp || hp->reserved != 0) return KFAC_ERR_ARG;
   if (hp->phase_mask < 0 || hp->phase_mask > KFAC_PHASE_ALL) return KFAC_ERR_ARG;
+  if (hp->refresh < 0 || hp->refresh > KFAC_REFRESH_BOTH) return KFAC_ERR_ARG;
+  if ((hp->options & ~KFAC_OPT_RESCALE) != 0) return KFAC_ERR_ARG;
   *phases = hp->phase_mask == 0 ? KFAC_PHASE_ALL : hp->phase_mask;
   for (int i = 0; i < n; ++i) {
-    s = check_layer_ptrs(layers[i], mode, *phases, hp->refresh != 0);
+    s = check_layer_ptrs(layers[i], mode, *phases, hp->refresh);
     if (s != KFAC_OK) return s;
   }
   return KFAC_OK;
@@ -182,6 +199,28 @@ kfac_status_t kfac_read_flags(void* workspace, void* stream, uint32_t* flags, in
     if (hipMemsetAsync(workspace, 0, sizeof(uint32_t), st) != hipSuccess) return KFAC_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return KFAC_ERR_HIP;
   }
+  return KFAC_OK;
+}
+
+kfac_status_t kfac_schedule_hparams(const kfac_schedule_t* sc, int64_t step, kfac_hparams_t* hp) {
+  if (!sc || !hp || step < 1) return KFAC_ERR_ARG;
+  if (sc->warmup_steps < 0 || sc->dense_steps < 0 || sc->refresh_every_a < 1 || sc->refresh_every_g < 1)
+    return KFAC_ERR_ARG;
+  if (sc->warmup_shape != KFAC_WARMUP_LINEAR && sc->warmup_shape != KFAC_WARMUP_GEOMETRIC) return KFAC_ERR_ARG;
+  const double g0 = sc->damping_init, gt = sc->damping_target;
+  if (sc->warmup_shape == KFAC_WARMUP_GEOMETRIC && !(g0 > 0.0 && gt > 0.0)) return KFAC_ERR_ARG;
+  // warm-up damping: fraction u of the way from the initial to the target value
+  const double u = sc->warmup_steps == 0
+                       ? 1.0
+                       : static_cast<double>(std::min<int64_t>(step - 1, sc->warmup_steps)) / sc->warmup_steps;
+  const double lam = sc->warmup_shape == KFAC_WARMUP_LINEAR ? g0 + (gt - g0) * u : g0 * std::pow(gt / g0, u);
+  hp->damping = static_cast<float>(lam);
+  hp->damping_bn = static_cast<float>(static_cast<double>(sc->bn_damping_scale) * lam);
+  // refresh: every step up to D, then each factor on its own interval
+  const int64_t D = std::max<int64_t>(sc->dense_steps, 1);
+  const bool ra = step <= D || (step - D) % sc->refresh_every_a == 0;
+  const bool rg = step <= D || (step - D) % sc->refresh_every_g == 0;
+  hp->refresh = (ra ? KFAC_REFRESH_A : 0) | (rg ? KFAC_REFRESH_G : 0);
   return KFAC_OK;
 }
 

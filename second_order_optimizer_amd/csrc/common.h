@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <vector>
+
 #include "../../include/kfac.h"
 
 namespace kfac {
@@ -27,6 +29,13 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Sets `bits` in the workspace flag word.  Called by one lane.
 __device__ inline void raise_flag(uint32_t* flags, uint32_t bits) { atomicOr(flags, bits); }
 
+// Packed upper-triangle storage of a symmetric d x d factor: element (i, j),
+// i <= j, at i d - i (i - 1) / 2 + (j - i) (rows of the upper triangle one
+// after the other).
+__host__ __device__ inline int64_t packed_index(int64_t i, int64_t j, int64_t d) {
+  return i * (2 * d - i + 1) / 2 + (j - i);
+}
+
 __device__ inline float bf16_bits_to_float(unsigned short u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
@@ -43,11 +52,22 @@ __device__ inline float bf16_bits_to_float(unsigned short u) {
 struct LayerGeom {
   int64_t rows;
   int d_in, d_out, d_a;
-  bool conv, bias;
+  bool conv, bias, bn, packed;
   int batch, c_in, h, w, kh, kw, stride, pad, h_out, w_out;
 };
 
 LayerGeom geom_of(const kfac_layer_t& L);
+
+// weight rescaling (rescale.hip): W <- W sqrt(2 d_out) / (||W||_F + eps) for
+// every listed weight; `part` holds rescale_blocks(n) floats of workspace.
+struct RescaleSeg {
+  float* w;
+  float* part;
+  int64_t n;
+  int32_t d_out;
+};
+int64_t rescale_blocks(int64_t n);
+kfac_status_t launch_rescale(const std::vector<RescaleSeg>& segs, float eps, hipStream_t st);
 
 // diag method (diag.hip)
 size_t diag_workspace_bytes(const kfac_layer_t* layers, int n);
@@ -59,6 +79,11 @@ kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
 constexpr size_t kNoAllocScratchBytes = KFAC_NOALLOC_SCRATCH_BYTES;
 kfac_status_t diag_enqueue_noalloc(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, uint32_t* flags,
                                    hipStream_t stream, int phases);
+// The diagonal step with its workspace regions carved from `ws` (the first
+// kFlagBytes of it unused) and the flag word at `flags` (the full method runs
+// its batch-norm layers through this).
+kfac_status_t diag_enqueue_into(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                                size_t ws_bytes, uint32_t* flags, hipStream_t stream, int phases);
 
 // full method (full.hip)
 size_t full_workspace_bytes(const kfac_layer_t* layers, int n);

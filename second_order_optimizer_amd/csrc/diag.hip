@@ -22,6 +22,10 @@
 //                       chunk partials in chunk order; bias entries dA[d_in] = 1.
 //   diag_update_kernel  one float4-vectorised pass over every parameter
 //                       segment: 4 loads + 3 stores of float32 per parameter.
+// Batch-norm layers (Osawa et al. sections 1 and 5.4: a diagonal Fisher for
+// batch normalisation) take one more FACTORS launch, diag_bn_kernel, which
+// forms their gamma / beta Fisher diagonals directly; their parameters join
+// the same parameter pass with their own damping.
 #include "common.h"
 
 #include <algorithm>
@@ -93,19 +97,43 @@ struct Seg {
   float* w;
   float* mom;
   float* F;
-  const float* dA;    // nullptr for a bias segment (its dA entry is exactly 1)
+  const float* dA;    // nullptr: the target of element e is dG[e] (a bias segment, whose dA entry is
+                      // exactly 1, or a batch-norm parameter with its own Fisher diagonal in dG)
   const float* dG;
   int32_t n;
   int32_t cols;       // d_in for a weight segment
   int32_t blk_begin;
-  int32_t pad_;
+  float damping;      // lambda of this segment's layer
 };
 struct Segs {
   Seg s[kMaxSegs];
   int32_t n;
-  float beta, one_minus_beta, damping, weight_decay, momentum, lr;
+  float beta, one_minus_beta, weight_decay, momentum, lr;
   uint32_t* flags;
 };
+static_assert(sizeof(Segs) <= 4096, "kernel arguments");
+
+// Batch-norm Fisher diagonals: one workgroup per channel c of a layer; its 4
+// wavefronts take the samples b = w, w + 4, ...; per sample the per-sample
+// gradients s1 = sum_hw g x_hat (gamma) and s2 = sum_hw g (beta) by a
+// wavefront reduction, squared and summed; the 4 wavefront sums in order.
+constexpr int kBnThreads = 256;
+constexpr int kBnWaves = kBnThreads / kWave;
+constexpr int kMaxBnTasks = 64;
+struct BnTask {
+  const float* x;     // x_hat [B, C, HW]
+  const float* g;     // output gradient [B, C, HW]
+  float* fg;          // [C] gamma Fisher diagonal
+  float* fb;          // [C] beta Fisher diagonal
+  int32_t C, B, HW, blk_begin;
+  float scale;        // 1 / B
+  int32_t pad_;
+};
+struct BnTasks {
+  BnTask t[kMaxBnTasks];
+  int32_t n;
+};
+static_assert(sizeof(BnTasks) <= 4096, "kernel arguments");
 
 template <typename T, int N>
 __device__ inline int find_task(const T (&t)[N], int n, int blk) {
@@ -186,6 +214,72 @@ __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
+}
+
+__global__ void __launch_bounds__(kBnThreads) diag_bn_kernel(BnTasks tasks) {
+  __shared__ float red[kBnWaves][2];
+  const BnTask& T = tasks.t[find_task(tasks.t, tasks.n, blockIdx.x)];
+  const int c = blockIdx.x - T.blk_begin;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  float q1 = 0.f, q2 = 0.f;
+  for (int b = wid; b < T.B; b += kBnWaves) {
+    const int64_t off = (static_cast<int64_t>(b) * T.C + c) * T.HW;
+    const float* xp = T.x + off;
+    const float* gp = T.g + off;
+    float s1 = 0.f, s2 = 0.f;
+    if ((T.HW & 3) == 0) {
+      // 16-byte loads, four of each tensor in flight per lane
+      constexpr int kStep = 4 * kWave;
+      int e = 4 * lane;
+      for (; e + 3 * kStep < T.HW; e += 4 * kStep) {
+        f32x4 xv[4], gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          xv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp + e + u * kStep));
+          gv[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gp + e + u * kStep));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            s1 = fmaf(gv[u][q], xv[u][q], s1);
+            s2 += gv[u][q];
+          }
+      }
+      for (; e < T.HW; e += kStep) {
+        const f32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xp + e));
+        const f32x4 gv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gp + e));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s1 = fmaf(gv[q], xv[q], s1);
+          s2 += gv[q];
+        }
+      }
+    } else {
+      for (int e = lane; e < T.HW; e += kWave) {
+        s1 = fmaf(gp[e], xp[e], s1);
+        s2 += gp[e];
+      }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    q1 = fmaf(s1, s1, q1);
+    q2 = fmaf(s2, s2, q2);
+  }
+  if (lane == 0) {
+    red[wid][0] = q1;
+    red[wid][1] = q2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a1 = 0.f, a2 = 0.f;
+    for (int w = 0; w < kBnWaves; ++w) {
+      a1 += red[w][0];
+      a2 += red[w][1];
+    }
+    T.fg[c] = a1 * T.scale;
+    T.fb[c] = a2 * T.scale;
+  }
 }
 
 // Bit t of the result is set when input row (or column) x is reached by
@@ -352,10 +446,10 @@ struct UpdOut {
   float w, v, f;
 };
 
-__device__ inline UpdOut upd_one(float g, float w, float v, float f, float target, const Segs& P) {
+__device__ inline UpdOut upd_one(float g, float w, float v, float f, float target, float damping, const Segs& P) {
   UpdOut o;
   o.f = P.beta * f + P.one_minus_beta * target;
-  const float p = g / (o.f + P.damping);
+  const float p = g / (o.f + damping);
   const float d = fmaf(P.weight_decay, w, p);
   o.v = fmaf(P.momentum, v, d);
   o.w = fmaf(-P.lr, o.v, w);
@@ -409,7 +503,7 @@ __global__ void __launch_bounds__(kUpdThreads) diag_update_kernel(Segs segs) {
       f32x4 wn, vn, fn;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        UpdOut r = upd_one(g[u][q], w[u][q], v[u][q], f[u][q], tgt[q], segs);
+        UpdOut r = upd_one(g[u][q], w[u][q], v[u][q], f[u][q], tgt[q], S.damping, segs);
         wn[q] = r.w; vn[q] = r.v; fn[q] = r.f;
         bad |= !(isfinite(r.w) && isfinite(r.v));
       }
@@ -428,7 +522,7 @@ __global__ void __launch_bounds__(kUpdThreads) diag_update_kernel(Segs segs) {
       } else {
         tgt = S.dG[e];
       }
-      UpdOut r = upd_one(S.grad[e], S.w[e], S.mom[e], S.F[e], tgt, segs);
+      UpdOut r = upd_one(S.grad[e], S.w[e], S.mom[e], S.F[e], tgt, S.damping, segs);
       S.F[e] = r.f; S.mom[e] = r.v; S.w[e] = r.w;
       bad |= !(isfinite(r.w) && isfinite(r.v));
     }
@@ -442,7 +536,10 @@ __global__ void __launch_bounds__(kUpdThreads) diag_update_kernel(Segs segs) {
 struct DiagPlan {
   std::vector<ColTask> col;
   std::vector<FinTask> fin;
+  std::vector<BnTask> bn;
   std::vector<Seg> seg;
+  std::vector<char> seg_bn;          // per segment: a batch-norm parameter (damping_bn)
+  std::vector<RescaleSeg> rescale;   // conv / linear weights
   size_t ws_bytes = kFlagBytes;
 };
 
@@ -497,10 +594,51 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
     fin_blk += blocks;
     P.fin.push_back(t);
   };
+  int bn_blk = 0;
   for (int li = 0; li < n; ++li) {
     const kfac_layer_t& L = layers[li];
     const LayerGeom g = geom_of(L);
     const float invN = 1.0f / static_cast<float>(g.rows);
+    if (g.bn) {
+      // gamma / beta Fisher diagonals straight into dA / dG, then one
+      // segment per parameter vector whose target is that diagonal
+      BnTask t{};
+      t.x = static_cast<const float*>(L.a);
+      t.g = static_cast<const float*>(L.g);
+      t.fg = L.dA;
+      t.fb = L.dG;
+      t.C = g.c_in;
+      t.B = g.batch;
+      t.HW = g.h * g.w;
+      t.scale = 1.0f / static_cast<float>(g.batch);
+      t.blk_begin = bn_blk;
+      bn_blk += t.C;
+      P.bn.push_back(t);
+      for (int which = 0; which < (g.bias ? 2 : 1); ++which) {
+        Seg sg{};
+        sg.grad = which == 0 ? L.grad_w : L.grad_b;
+        sg.w = which == 0 ? L.w : L.b;
+        sg.mom = which == 0 ? L.mom_w : L.mom_b;
+        sg.F = which == 0 ? L.F_w : L.F_b;
+        sg.dA = nullptr;
+        sg.dG = which == 0 ? L.dA : L.dG;
+        sg.n = g.d_out;
+        sg.cols = 1;
+        sg.blk_begin = upd_blk;
+        upd_blk += (sg.n + kUpdPerBlock - 1) / kUpdPerBlock;
+        P.seg.push_back(sg);
+        P.seg_bn.push_back(1);
+      }
+      continue;
+    }
+    {
+      RescaleSeg r{};
+      r.w = L.w;
+      r.n = static_cast<int64_t>(g.d_out) * g.d_in;
+      r.d_out = g.d_out;
+      r.part = carve(static_cast<size_t>(rescale_blocks(r.n)));
+      P.rescale.push_back(r);
+    }
     if (g.conv) {
       // input: S_x[c*H*W + p] = sum_b x^2 ; then strided window sums
       const int Kx = g.c_in * g.h * g.w;
@@ -547,12 +685,14 @@ DiagPlan plan_diag(const kfac_layer_t* layers, int n, char* ws) {
       s.n = g.d_out * g.d_in; s.cols = g.d_in; s.blk_begin = upd_blk;
       upd_blk += (s.n + kUpdPerBlock - 1) / kUpdPerBlock;
       P.seg.push_back(s);
+      P.seg_bn.push_back(0);
       if (g.bias) {
         Seg sb{};
         sb.grad = L.grad_b; sb.w = L.b; sb.mom = L.mom_b; sb.F = L.F_b; sb.dA = nullptr; sb.dG = L.dG;
         sb.n = g.d_out; sb.cols = 1; sb.blk_begin = upd_blk;
         upd_blk += (sb.n + kUpdPerBlock - 1) / kUpdPerBlock;
         P.seg.push_back(sb);
+        P.seg_bn.push_back(0);
       }
     }
   }
@@ -587,6 +727,19 @@ kfac_status_t enqueue_steps(const kfac_layer_t* layers, int n, const kfac_hparam
       hipLaunchKernelGGL(diag_colsq_kernel, dim3(blocks), dim3(kColThreads), 0, stream, T);
       KFAC_HIP_TRY(hipGetLastError());
     }
+    for (size_t g0 = 0; g0 < P.bn.size(); g0 += kMaxBnTasks) {
+      const size_t g1 = std::min(P.bn.size(), g0 + kMaxBnTasks);
+      BnTasks T{};
+      const int base = P.bn[g0].blk_begin;
+      for (size_t i = g0; i < g1; ++i) {
+        T.t[i - g0] = P.bn[i];
+        T.t[i - g0].blk_begin -= base;
+      }
+      const int blocks = P.bn[g1 - 1].blk_begin - base + P.bn[g1 - 1].C;
+      T.n = static_cast<int>(g1 - g0);
+      hipLaunchKernelGGL(diag_bn_kernel, dim3(blocks), dim3(kBnThreads), 0, stream, T);
+      KFAC_HIP_TRY(hipGetLastError());
+    }
     for (size_t g0 = 0; g0 < P.fin.size(); g0 += kMaxFinTasks) {
       const size_t g1 = std::min(P.fin.size(), g0 + kMaxFinTasks);
       FinTasks T{};
@@ -610,13 +763,13 @@ kfac_status_t enqueue_steps(const kfac_layer_t* layers, int n, const kfac_hparam
       for (size_t i = g0; i < g1; ++i) {
         S.s[i - g0] = P.seg[i];
         S.s[i - g0].blk_begin -= base;
+        S.s[i - g0].damping = P.seg_bn[i] ? hp.damping_bn : hp.damping;
       }
       const Seg& last = P.seg[g1 - 1];
       const int blocks = last.blk_begin - base + (last.n + kUpdPerBlock - 1) / kUpdPerBlock;
       S.n = static_cast<int>(g1 - g0);
       S.beta = hp.ema_decay;
       S.one_minus_beta = 1.0f - hp.ema_decay;
-      S.damping = hp.damping;
       S.weight_decay = hp.weight_decay;
       S.momentum = hp.momentum;
       S.lr = hp.lr;
@@ -624,11 +777,20 @@ kfac_status_t enqueue_steps(const kfac_layer_t* layers, int n, const kfac_hparam
       hipLaunchKernelGGL(diag_update_kernel, dim3(blocks), dim3(kUpdThreads), 0, stream, S);
       KFAC_HIP_TRY(hipGetLastError());
     }
+    if ((hp.options & KFAC_OPT_RESCALE) && !P.rescale.empty()) {
+      kfac_status_t r = launch_rescale(P.rescale, hp.rescale_eps, stream);
+      if (r != KFAC_OK) return r;
+    }
   }
   return KFAC_OK;
 }
 
 }  // namespace
+
+kfac_status_t diag_enqueue_into(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
+                                size_t ws_bytes, uint32_t* flags, hipStream_t stream, int phases) {
+  return enqueue_steps(layers, n, hp, ws, ws_bytes, flags, stream, phases);
+}
 
 kfac_status_t diag_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws,
                            size_t ws_bytes, hipStream_t stream, int phases) {

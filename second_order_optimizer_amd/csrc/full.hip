@@ -38,7 +38,7 @@ struct SymRedItem {
   const float* part;
   float* F;
   const int32_t* fail;   // when set and nonzero, F is left as it is
-  int32_t d, nsplit, blk_begin, pad_;
+  int32_t d, nsplit, blk_begin, packed;   // packed: F is the packed upper triangle (no mirror)
   float alpha, beta;
 };
 struct SymRedTab {
@@ -64,15 +64,18 @@ __global__ void __launch_bounds__(256) sym_reduce_kernel(SymRedTab tab) {
   for (int r = ty; r < 32; r += 8) {
     const int i = I * 32 + r, j = J * 32 + tx;
     float o = 0.f;
-    if (i < R.d && j < R.d) {
+    const bool upper = I != J || i <= j;
+    if (i < R.d && j < R.d && (upper || !R.packed)) {
       const int64_t e = static_cast<int64_t>(i) * R.d + j;
+      const int64_t f = R.packed ? packed_index(i, j, R.d) : e;
       float sum = 0.f;
       for (int k = 0; k < R.nsplit; ++k) sum += R.part[k * dd + e];
-      o = R.beta != 0.f ? R.beta * R.F[e] + R.alpha * sum : R.alpha * sum;
-      if (I != J || i <= j) R.F[e] = o;
+      o = R.beta != 0.f ? R.beta * R.F[f] + R.alpha * sum : R.alpha * sum;
+      if (upper) R.F[f] = o;
     }
     t[r][tx] = o;
   }
+  if (R.packed) return;   // a packed factor holds only the upper triangle
   __syncthreads();
   for (int r = ty; r < 32; r += 8) {
     const int i = J * 32 + r, j = I * 32 + tx;   // lower tile (J, I) = transpose of (I, J)
@@ -203,7 +206,7 @@ struct Mat {
   float* Dinv;        // inverses of the diagonal blocks, [nblk][128][128]
   int32_t* fail;
   int32_t d;
-  int32_t pad_;
+  int32_t packed;     // F is stored as its packed upper triangle
 };
 struct MatTab {
   Mat m[kMaxMats];
@@ -247,7 +250,10 @@ __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
     __syncthreads();
     for (int r = ty; r < 32; r += 8) {
       const int i = sr + r, j = sc + tx;
-      t[r][tx] = (i < d && j < d) ? M.F[static_cast<int64_t>(i) * d + j] : 0.f;
+      // only upper entries are used (a diagonal tile mirrors its upper part)
+      float v = 0.f;
+      if (i < d && j < d && i <= j) v = M.F[M.packed ? packed_index(i, j, d) : static_cast<int64_t>(i) * d + j];
+      t[r][tx] = v;
     }
     __syncthreads();
     for (int r = ty; r < 32; r += 8) {
@@ -588,6 +594,7 @@ kfac_status_t launch_bias_col(std::vector<BcProb>& probs, int stage, const kfac_
 
 struct FullPlan {
   size_t ws_bytes = kFlagBytes;
+  std::vector<RescaleSeg> rescale;   // per layer: its weight (KFAC_OPT_RESCALE)
   std::vector<float*> part;      // per layer and factor (2 li + which): split-K partials, or null
   std::vector<int> nsplit;       // per layer and factor
   std::vector<float*> T;         // per layer, d_out x d_a
@@ -642,6 +649,15 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   }
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
+    RescaleSeg rs{};
+    rs.w = layers[li].w;
+    rs.n = static_cast<int64_t>(g.d_out) * g.d_in;
+    rs.d_out = g.d_out;
+    rs.part = reinterpret_cast<float*>(carve(static_cast<size_t>(rescale_blocks(rs.n)) * 4));
+    P.rescale.push_back(rs);
+  }
+  for (int li = 0; li < n; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
     P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * g.d_a * 4)));
     P.tb.push_back(bias_column_split(g) ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * 4)) : nullptr);
   }
@@ -667,6 +683,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
       m.F = which == 0 ? layers[li].A : layers[li].G;
       m.Finv = which == 0 ? layers[li].A_inv : layers[li].G_inv;
       m.d = which == 0 ? g.d_a : g.d_out;
+      m.packed = g.packed ? 1 : 0;
       order[2 * li + which] = 2 * li + which;
     }
   }
@@ -742,6 +759,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         q.bias = special >= 0;
         q.alpha = alpha;
         q.beta = eps;
+        q.packed = g.packed ? 1 : 0;
         bf16.push_back(q);
         continue;
       }
@@ -783,6 +801,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         p.C = F;
         p.alpha = alpha;
         p.beta = eps;
+        p.c_packed = g.packed ? 1 : 0;
         probs.push_back(p);
       } else {
         p.C = P.part[2 * li + which];
@@ -796,6 +815,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
         r.nsplit = s;
         r.alpha = alpha;
         r.beta = eps;
+        r.packed = g.packed ? 1 : 0;
         reds.push_back(r);
       }
     }
@@ -873,20 +893,44 @@ kfac_status_t side_streams_for(hipStream_t caller, SideStream** out) {
 kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t* flags, hipStream_t st,
                            SideStream* side) {
   const std::vector<Mat>& mats = P.mats;
+  // the factors this step inverts: A (even entries) and / or G (odd entries)
+  std::vector<char> on(mats.size());
+  for (size_t mi = 0; mi < mats.size(); ++mi)
+    on[mi] = (hp.refresh & (mi % 2 == 0 ? KFAC_REFRESH_A : KFAC_REFRESH_G)) != 0;
   int nblk_max = 0, d_max = 0;
-  for (const Mat& m : mats) {
-    nblk_max = std::max<int>(nblk_max, static_cast<int>(nblk_of(m.d)));
-    d_max = std::max(d_max, m.d);
+  for (size_t mi = 0; mi < mats.size(); ++mi) {
+    if (!on[mi]) continue;
+    nblk_max = std::max<int>(nblk_max, static_cast<int>(nblk_of(mats[mi].d)));
+    d_max = std::max(d_max, mats[mi].d);
+  }
+  if (nblk_max == 0) return KFAC_OK;
+  // runs of equal-size factors of this step whose work areas lie at a
+  // constant stride (a plan group with some members left out splits into runs)
+  std::vector<FullPlan::Group> groups;
+  for (const FullPlan::Group& g : P.groups) {
+    FullPlan::Group run{-1, 0, g.stride, {}};
+    for (int mi : g.members) {
+      if (on[mi]) {
+        if (run.count == 0) run.first = mi;
+        run.members.push_back(mi);
+        ++run.count;
+      } else if (run.count > 0) {
+        groups.push_back(run);
+        run = FullPlan::Group{-1, 0, g.stride, {}};
+      }
+    }
+    if (run.count > 0) groups.push_back(run);
   }
   GemmScalars sc{};
-  // runs `fn` on the matrices selected by `pred`, kMaxMats at a time
+  // runs `fn` on the matrices of this step selected by `pred`, kMaxMats at a time
   auto tables = [&](auto pred, int k, auto fn) -> kfac_status_t {
     MatTab T{};
     T.damping = hp.damping;
     T.flags = flags;
     T.k = k;
-    for (const Mat& m : mats) {
-      if (!pred(m)) continue;
+    for (size_t mi = 0; mi < mats.size(); ++mi) {
+      const Mat& m = mats[mi];
+      if (!on[mi] || !pred(m)) continue;
       T.m[T.n++] = m;
       if (T.n == kMaxMats) {
         kfac_status_t r = fn(T);
@@ -931,7 +975,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
         if (mi == mats.size()) break;
       }
       const Mat& m = mats[mi];
-      if (static_cast<int>(nblk_of(m.d)) <= k) continue;
+      if (!on[mi] || static_cast<int>(nblk_of(m.d)) <= k) continue;
       D.m[D.n++] = DMat{m.L, m.Z, m.Dinv, m.fail, m.d, 0};
     }
     return KFAC_OK;
@@ -993,7 +1037,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   // panel k (side stream) for every matrix with a block below k
   auto panel_step = [&](int k) -> kfac_status_t {
     std::vector<GemmProb> v;
-    for (const FullPlan::Group& g : P.groups)
+    for (const FullPlan::Group& g : groups)
       if (static_cast<int>(nblk_of(mats[g.first].d)) > k + 1) v.push_back(batched(panel_of(mats[g.first], k), g));
     return v.empty() ? KFAC_OK : launch_gemm(v, OP_K, OP_K, EPI_STORE, sc, ss);
   };
@@ -1130,7 +1174,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     r = diag_step(0, st);
     if (r != KFAC_OK) return r;
     std::vector<const FullPlan::Group*> all;
-    for (const FullPlan::Group& g : P.groups) all.push_back(&g);
+    for (const FullPlan::Group& g : groups) all.push_back(&g);
     return finish(all, st);
   }
   hipStream_t fs = side->f;
@@ -1149,7 +1193,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     if (K > 0) {
       if (K > 1) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[K & 1], 0));
       std::vector<GemmProb> fn;
-      for (const FullPlan::Group& g : P.groups) {
+      for (const FullPlan::Group& g : groups) {
         const Mat& m = mats[g.first];
         if (static_cast<int>(nblk_of(m.d)) > k0) {
           const int r0 = k0 * kNb;
@@ -1169,7 +1213,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
       if (k + 1 < k1) {
         std::vector<GemmProb> ui;
-        for (const FullPlan::Group& g : P.groups) {
+        for (const FullPlan::Group& g : groups) {
           const Mat& m = mats[g.first];
           if (static_cast<int>(nblk_of(m.d)) > k + 1) {
             const int r0 = (k + 1) * kNb;
@@ -1185,7 +1229,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     KFAC_HIP_TRY(hipEventRecord(side->side_done[K & 1], ss));
     // caller's stream: F_rest(K), after the last panel of outer panel K
     std::vector<GemmProb> fr;
-    for (const FullPlan::Group& g : P.groups) {
+    for (const FullPlan::Group& g : groups) {
       const Mat& m = mats[g.first];
       if (static_cast<int>(nblk_of(m.d)) > k1 + kOuter) {
         const int r0 = (k1 + kOuter) * kNb;
@@ -1201,7 +1245,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     // factors whose last block is in outer panel K are complete: their
     // inverse is assembled on a third stream beside the remaining steps
     std::vector<const FullPlan::Group*> done;
-    for (const FullPlan::Group& g : P.groups)
+    for (const FullPlan::Group& g : groups)
       if ((static_cast<int>(nblk_of(mats[g.first].d)) - 1) / kOuter == K) done.push_back(&g);
     if (!done.empty()) {
       KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->side_done[K & 1], 0));
@@ -1315,32 +1359,66 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
 
 }  // namespace
 
+namespace {
+
+// conv / linear layers take the Kronecker-factored path; batch-norm layers
+// (a diagonal Fisher, Osawa et al. sections 1 and 5.4) the diagonal one
+void split_layers(const kfac_layer_t* layers, int n, std::vector<kfac_layer_t>& kf, std::vector<kfac_layer_t>& bn) {
+  for (int i = 0; i < n; ++i) (layers[i].kind == KFAC_BATCHNORM ? bn : kf).push_back(layers[i]);
+}
+
+// the batch-norm layers' diagonal workspace follows the Kronecker-factored plan
+size_t bn_region_bytes(const std::vector<kfac_layer_t>& bn) {
+  return bn.empty() ? 0 : diag_workspace_bytes(bn.data(), static_cast<int>(bn.size())) - kFlagBytes;
+}
+
+}  // namespace
+
 size_t full_workspace_bytes(const kfac_layer_t* layers, int n) {
-  return plan_full(layers, n, nullptr, KFAC_PHASE_ALL, true).ws_bytes;
+  std::vector<kfac_layer_t> kf, bn;
+  split_layers(layers, n, kf, bn);
+  return plan_full(kf.data(), static_cast<int>(kf.size()), nullptr, KFAC_PHASE_ALL, true).ws_bytes +
+         bn_region_bytes(bn);
 }
 
 kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, char* ws, size_t ws_bytes,
                            hipStream_t st, int phases) {
-  FullPlan P = plan_full(layers, n, ws, phases, hp.refresh != 0);
-  if (P.ws_bytes > ws_bytes) return KFAC_ERR_WORKSPACE;
-  SideStream* side = nullptr;
-  kfac_status_t r = side_streams_for(st, &side);
-  if (r != KFAC_OK) return r;
-  std::lock_guard<std::mutex> lock(side->mu);
+  std::vector<kfac_layer_t> kf, bn;
+  split_layers(layers, n, kf, bn);
+  const int nk = static_cast<int>(kf.size());
+  FullPlan P = plan_full(kf.data(), nk, ws, phases, hp.refresh != 0);
+  if (P.ws_bytes + bn_region_bytes(bn) > ws_bytes) return KFAC_ERR_WORKSPACE;
   uint32_t* flags = reinterpret_cast<uint32_t*>(ws);
-  if (phases & KFAC_PHASE_FACTORS) {
-    r = factors_phase(layers, n, hp, P, st);
+  kfac_status_t r = KFAC_OK;
+  if (nk > 0) {
+    SideStream* side = nullptr;
+    r = side_streams_for(st, &side);
     if (r != KFAC_OK) return r;
+    std::lock_guard<std::mutex> lock(side->mu);
+    if (phases & KFAC_PHASE_FACTORS) {
+      r = factors_phase(kf.data(), nk, hp, P, st);
+      if (r != KFAC_OK) return r;
+    }
+    if ((phases & KFAC_PHASE_INVERT) && hp.refresh) {
+      r = invert_phase(hp, P, flags, st, side);
+      if (r != KFAC_OK) return r;
+    }
+    if (phases & KFAC_PHASE_UPDATE) {
+      r = update_phase(kf.data(), nk, hp, P, flags, st, side);
+      if (r != KFAC_OK) return r;
+      if (hp.options & KFAC_OPT_RESCALE) {
+        r = launch_rescale(P.rescale, hp.rescale_eps, st);
+        if (r != KFAC_OK) return r;
+      }
+    }
   }
-  if ((phases & KFAC_PHASE_INVERT) && hp.refresh) {
-    r = invert_phase(hp, P, flags, st, side);
-    if (r != KFAC_OK) return r;
+  if (!bn.empty() && (phases & (KFAC_PHASE_FACTORS | KFAC_PHASE_UPDATE))) {
+    // carved from kFlagBytes past its base: right after the plan's regions
+    char* base = ws + P.ws_bytes - kFlagBytes;
+    r = diag_enqueue_into(bn.data(), static_cast<int>(bn.size()), hp, base, bn_region_bytes(bn) + kFlagBytes, flags,
+                          st, phases & (KFAC_PHASE_FACTORS | KFAC_PHASE_UPDATE));
   }
-  if (phases & KFAC_PHASE_UPDATE) {
-    r = update_phase(layers, n, hp, P, flags, st, side);
-    if (r != KFAC_OK) return r;
-  }
-  return KFAC_OK;
+  return r;
 }
 
 }  // namespace kfac

@@ -22,7 +22,8 @@ enum GemmEpi : int {
   EPI_SUB = 1,        // C -= alpha * acc
   EPI_UPDATE = 2,     // P = acc; D = P + wd W; V = mu V + D; W -= lr V  (columns >= d_in go to b / mom_b)
   EPI_SYRK = 3,       // upper tiles; nsplit == 1: C = beta * C + alpha * acc (C not read when beta == 0),
-                      // mirrored to the lower triangle; else C + split * split_stride = alpha * acc
+                      // mirrored to the lower triangle (packed C: upper entries only);
+                      // else C + split * split_stride = alpha * acc
 };
 
 // Tile grids.
@@ -59,7 +60,8 @@ struct GemmProb {
   uint8_t tri;            // GemmTri
   uint8_t krange;         // GemmKRange
   uint8_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
-  uint8_t pad_[2];
+  uint8_t c_packed;       // EPI_SYRK with nsplit == 1: C is a packed upper triangle of an M x M matrix
+  uint8_t pad_;
   float alpha, beta;
 };
 

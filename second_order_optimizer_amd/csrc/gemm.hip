@@ -339,9 +339,10 @@ __device__ __forceinline__ void gemm_f32_body(const GemmBatch& batch) {
           Cp[idx] = P.alpha * v;
         } else if (EPI == EPI_SYRK) {
           if (row <= col) {
-            const float o = P.beta != 0.f ? P.beta * Cp[idx] + P.alpha * v : P.alpha * v;
-            Cp[idx] = o;
-            if (row != col) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
+            const int64_t u = P.c_packed ? packed_index(row, col, P.M) : idx;
+            const float o = P.beta != 0.f ? P.beta * Cp[u] + P.alpha * v : P.alpha * v;
+            Cp[u] = o;
+            if (row != col && !P.c_packed) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
         } else if (EPI == EPI_UPDATE) {
           const bool wcol = col < P.d_in;

@@ -37,9 +37,14 @@ struct Prob {
   const uint16_t* X;
   float* F;
   int64_t rows;
-  int32_t width, bias, ldf, tiles, blk_begin, pad_;
+  int32_t width, bias, ldf, tiles, blk_begin, packed;   // packed: F is the packed upper triangle
   float alpha, beta;
 };
+
+// position of F's element (row, col), row <= col
+__device__ inline int64_t f_index(const Prob& P, int row, int col) {
+  return P.packed ? packed_index(row, col, P.ldf) : static_cast<int64_t>(row) * P.ldf + col;
+}
 struct Batch {
   Prob p[kMaxProbs];
   int32_t n;
@@ -209,10 +214,10 @@ syrk_bf16_kernel(Batch batch) {
         for (int r = 0; r < 16; ++r) {
           const int row = i0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row >= width || col >= width || row > col) continue;
-          const int64_t idx = static_cast<int64_t>(row) * ldf + col;
+          const int64_t idx = f_index(P, row, col);
           const float o = P.beta * F[idx] + P.alpha * acc[i][j][r];
           F[idx] = o;
-          if (row != col) F[static_cast<int64_t>(col) * ldf + row] = o;
+          if (row != col && !P.packed) F[static_cast<int64_t>(col) * ldf + row] = o;
         }
       }
     }
@@ -225,14 +230,14 @@ syrk_bf16_kernel(Batch batch) {
       for (int r = 0; r < 16; ++r) {
         const int m = i0 + cs0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= width) continue;
-        const int64_t idx = static_cast<int64_t>(m) * ldf + width;
+        const int64_t idx = f_index(P, m, width);
         const float o = P.beta * F[idx] + P.alpha * acc[i][0][r];
         F[idx] = o;
-        F[static_cast<int64_t>(width) * ldf + m] = o;
+        if (!P.packed) F[static_cast<int64_t>(width) * ldf + m] = o;
       }
     }
     if (ti == 0 && cs0 == 0 && lane == 0) {
-      const int64_t c = static_cast<int64_t>(width) * ldf + width;
+      const int64_t c = f_index(P, width, width);
       F[c] = P.beta * F[c] + P.alpha * static_cast<float>(rows);
     }
   }
@@ -467,7 +472,7 @@ syrk_bf16_dma_kernel(Batch batch) {
         for (int r = 0; r < 16; ++r) {
           const int row = r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const bool in = row < width && col < width && row <= col;
-          o[r] = F[in ? static_cast<int64_t>(row) * ldf + col : static_cast<int64_t>(r0) * ldf + c0];
+          o[r] = F[in ? f_index(P, row, col) : f_index(P, r0, c0)];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -475,9 +480,10 @@ syrk_bf16_dma_kernel(Batch batch) {
           const int row = r0 + rr;
           const bool in = row < width && col < width && row <= col;
           const float v = P.beta * o[r] + P.alpha * acc[i][j][r];
-          if (in) F[static_cast<int64_t>(row) * ldf + col] = v;
+          if (in) F[f_index(P, row, col)] = v;
           stg[(lane & 31) * 33 + rr] = v;
         }
+        if (P.packed) continue;   // the upper triangle is all a packed factor holds
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int cc = 2 * q + (lane >> 5), rr = lane & 31;
@@ -494,14 +500,14 @@ syrk_bf16_dma_kernel(Batch batch) {
       for (int r = 0; r < 16; ++r) {
         const int m = i0 + cs0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= width) continue;
-        const int64_t idx = static_cast<int64_t>(m) * ldf + width;
+        const int64_t idx = f_index(P, m, width);
         const float o = P.beta * F[idx] + P.alpha * acc[i][0][r];
         F[idx] = o;
-        F[static_cast<int64_t>(width) * ldf + m] = o;
+        if (!P.packed) F[static_cast<int64_t>(width) * ldf + m] = o;
       }
     }
     if (ti == 0 && cs0 == 0 && lane == 0) {
-      const int64_t c = static_cast<int64_t>(width) * ldf + width;
+      const int64_t c = f_index(P, width, width);
       F[c] = P.beta * F[c] + P.alpha * static_cast<float>(rows);
     }
   }
@@ -531,6 +537,7 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
     p.tiles = (q.width + kBT - 1) / kBT;
     p.alpha = q.alpha;
     p.beta = q.beta;
+    p.packed = q.packed;
     const bool aligned = (q.width % 8) == 0 && (reinterpret_cast<uintptr_t>(q.X) % 16) == 0;
     if (!aligned) {
       ragged.push_back({p, 0});

@@ -2,9 +2,12 @@
 descriptor array pointing at it.  Allocation and marshalling only: the step
 itself is one call into libkfac.so.
 
-A layer shape is any object with the attributes ``kind`` ("linear" | "conv"),
-``d_in``, ``d_out``, ``has_bias``, ``rows`` and, for convolutions, ``batch``,
-``c_in``, ``h``, ``w``, ``k``, ``stride``, ``pad``, ``h_out``, ``w_out``.
+A layer shape is any object with the attributes ``kind`` ("linear" | "conv" |
+"bn"), ``d_in``, ``d_out``, ``has_bias``, ``rows`` and, for convolutions and
+batch norm, ``batch``, ``c_in``, ``h``, ``w``, ``k``, ``stride``, ``pad``,
+``h_out``, ``w_out``.  With ``factor_layout="packed"`` the full method's A and
+G buffers hold the packed upper triangle (d (d + 1) / 2 floats, row after row)
+and are set and read in that form.
 """
 from __future__ import annotations
 
@@ -13,8 +16,9 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BF16, CONV2D, F32, LINEAR, MODE_DIAG, MODE_FULL, HParams, hparams, layer_array, make_layer,
-               read_flags, step_diag, step_full, workspace_size)
+from . import (BATCHNORM, BF16, CONV2D, F32, FACTORS_FULL, FACTORS_PACKED, LINEAR, MODE_DIAG, MODE_FULL, OPT_RESCALE,
+               REFRESH_A, REFRESH_G, HParams, hparams, layer_array, make_layer, read_flags, step_diag, step_full,
+               workspace_size)
 
 INPUT_NAMES = ("a", "g", "grad_w", "grad_b")
 
@@ -39,8 +43,9 @@ class KfacStack:
     """
 
     def __init__(self, shapes: Sequence, variant: str, act_dtype: str = "f32", grad_dtype: str = "f32",
-                 device="cuda", pool: int = 1):
+                 device="cuda", pool: int = 1, factor_layout: str = "full"):
         self.shapes = list(shapes)
+        self.packed = factor_layout == "packed"
         self.variant = variant
         self.mode = MODE_FULL if variant == "full" else MODE_DIAG
         self.dev = torch.device(device)
@@ -70,28 +75,34 @@ class KfacStack:
         if L.has_bias:
             st["b"] = torch.zeros(L.d_out, **f)
             st["mom_b"] = torch.zeros(L.d_out, **f)
-        if self.variant == "full":
-            st["A"] = torch.eye(d_a, **f)
-            st["G"] = torch.eye(L.d_out, **f)
+        if self.variant == "full" and L.kind != "bn":
+            if self.packed:
+                st["A"] = torch.zeros(d_a * (d_a + 1) // 2, **f)
+                st["G"] = torch.zeros(L.d_out * (L.d_out + 1) // 2, **f)
+            else:
+                st["A"] = torch.eye(d_a, **f)
+                st["G"] = torch.eye(L.d_out, **f)
             st["A_inv"] = torch.zeros(d_a, d_a, **f)
             st["G_inv"] = torch.zeros(L.d_out, L.d_out, **f)
         else:
             st["F_w"] = torch.ones(L.d_out, L.d_in, **f)
             if L.has_bias:
                 st["F_b"] = torch.ones(L.d_out, **f)
-            st["dA"] = torch.zeros(d_a, **f)
+            # a batch-norm layer's dA / dG hold the gamma / beta Fisher diagonals, one entry per channel
+            st["dA"] = torch.zeros(L.d_out if L.kind == "bn" else d_a, **f)
             st["dG"] = torch.zeros(L.d_out, **f)
         return st
 
     def _alloc_inputs(self, L) -> Dict[str, Optional[torch.Tensor]]:
-        if L.kind == "conv":
+        if L.kind in ("conv", "bn"):
             ashape = (L.batch, L.c_in, L.h, L.w)
             gshape = (L.batch, L.d_out, L.h_out, L.w_out)
         else:
             ashape = (L.rows, L.d_in)
             gshape = (L.rows, L.d_out)
-        return {"a": torch.zeros(ashape, dtype=self.adt, device=self.dev),
-                "g": torch.zeros(gshape, dtype=self.gdt, device=self.dev),
+        bn = L.kind == "bn"    # batch-norm inputs are float32
+        return {"a": torch.zeros(ashape, dtype=torch.float32 if bn else self.adt, device=self.dev),
+                "g": torch.zeros(gshape, dtype=torch.float32 if bn else self.gdt, device=self.dev),
                 "grad_w": torch.zeros(L.d_out, L.d_in, dtype=torch.float32, device=self.dev),
                 "grad_b": torch.zeros(L.d_out, dtype=torch.float32, device=self.dev) if L.has_bias else None}
 
@@ -100,13 +111,15 @@ class KfacStack:
         for li, L in enumerate(self.shapes):
             t = dict(self.state[li])
             t.update({k: v for k, v in self.inputs[self.active][li].items() if v is not None})
-            conv = L.kind == "conv"
+            conv = L.kind in ("conv", "bn")
+            kind = {"conv": CONV2D, "bn": BATCHNORM}.get(L.kind, LINEAR)
+            bn = L.kind == "bn"
             descs.append(make_layer(
-                CONV2D if conv else LINEAR, L.d_in, L.d_out, L.rows, L.has_bias,
-                act_dtype=self.act_code, grad_dtype=self.grad_code,
+                kind, L.d_in, L.d_out, L.rows, L.has_bias,
+                act_dtype=F32 if bn else self.act_code, grad_dtype=F32 if bn else self.grad_code,
                 batch=L.batch if conv else 0, c_in=L.c_in if conv else 0, height=L.h if conv else 0,
                 width=L.w if conv else 0, k=L.k if conv else 0, stride=L.stride if conv else 0,
-                pad=L.pad if conv else 0, **t))
+                pad=L.pad if conv else 0, factor_layout=FACTORS_PACKED if self.packed else FACTORS_FULL, **t))
         self.desc = layer_array(descs)
 
     # -- data movement ----------------------------------------------------
@@ -143,6 +156,11 @@ class KfacStack:
         return read_flags(self.ws_ptr, clear)
 
     @staticmethod
-    def hparams(cfg_hp: Dict[str, float], refresh: bool = True, phase_mask: int = 0) -> HParams:
+    def hparams(cfg_hp: Dict[str, float], refresh=True, phase_mask: int = 0) -> HParams:
+        """refresh: True / False, KFAC_REFRESH_* bits, or a pair (A, G) of bools."""
+        if isinstance(refresh, tuple):
+            refresh = (REFRESH_A if refresh[0] else 0) | (REFRESH_G if refresh[1] else 0)
         return hparams(cfg_hp["lr"], cfg_hp["momentum"], cfg_hp["weight_decay"], cfg_hp["ema_decay"],
-                       cfg_hp["damping"], refresh, phase_mask)
+                       cfg_hp["damping"], refresh, phase_mask, damping_bn=cfg_hp.get("damping_bn"),
+                       rescale_eps=cfg_hp.get("rescale_eps", 1e-9),
+                       options=OPT_RESCALE if cfg_hp.get("rescale") else 0)

@@ -43,9 +43,11 @@ class Layer:
     Conv2d: input x [batch, c_in, h, w] (NCHW), output gradient
     g [batch, d_out, h_out, w_out]; d_in = c_in * k * k in (c, kh, kw) order;
     rows = batch * h_out * w_out.
+    Batch norm ("bn"): normalised input x_hat and output gradient, both
+    [batch, C, h, w]; d_in = 1 (gamma), d_out = C, rows = batch.
     """
     name: str
-    kind: str              # "linear" | "conv"
+    kind: str              # "linear" | "conv" | "bn"
     d_in: int              # unfolded input width (without the bias column)
     d_out: int
     has_bias: bool
@@ -63,22 +65,26 @@ class Layer:
         return self.d_in + (1 if self.has_bias else 0)
 
     @property
+    def spatial(self) -> bool:
+        return self.kind in ("conv", "bn")
+
+    @property
     def h_out(self) -> int:
-        return (self.h + 2 * self.pad - self.k) // self.stride + 1 if self.kind == "conv" else 0
+        return (self.h + 2 * self.pad - self.k) // self.stride + 1 if self.spatial else 0
 
     @property
     def w_out(self) -> int:
-        return (self.w + 2 * self.pad - self.k) // self.stride + 1 if self.kind == "conv" else 0
+        return (self.w + 2 * self.pad - self.k) // self.stride + 1 if self.spatial else 0
 
     @property
     def act_shape(self):
-        if self.kind == "conv":
+        if self.spatial:
             return (self.batch, self.c_in, self.h, self.w)
         return (self.rows, self.d_in)
 
     @property
     def grad_out_shape(self):
-        if self.kind == "conv":
+        if self.spatial:
             return (self.batch, self.d_out, self.h_out, self.w_out)
         return (self.rows, self.d_out)
 
@@ -97,6 +103,23 @@ def conv(name, c_in, c_out, k, stride, pad, batch, h, w=None, bias=False) -> Lay
 
 def linear(name, d_in, d_out, rows, bias=True) -> Layer:
     return Layer(name, "linear", d_in, d_out, bias, rows)
+
+
+def batchnorm(name, channels, batch, h, w=None, bias=True) -> Layer:
+    """Affine parameters of a batch-norm layer over `channels` planes of h x w."""
+    w = h if w is None else w
+    return Layer(name, "bn", 1, channels, bias, batch, batch, channels, h, w, 1, 1, 0)
+
+
+def with_batchnorm(layers) -> List[Layer]:
+    """A conv stack with a batch-norm layer after every convolution (on its
+    output planes), as in the ResNet families."""
+    out = []
+    for L in layers:
+        out.append(L)
+        if L.kind == "conv":
+            out.append(batchnorm(L.name + ".bn", L.d_out, L.batch, L.h_out, L.w_out))
+    return out
 
 
 def resnet18_layers(batch=128, res=224, classes=1000) -> List[Layer]:
@@ -172,6 +195,8 @@ class Config:
     w_std: float = 0.02
     grad_w_std: float = 1e-3
     seed: int = 0
+    bn_damping_scale: float = 1.0    # damping of batch-norm layers = this x damping
+    rescale: bool = False            # weight rescaling after the update
 
     @property
     def n_params(self) -> int:
@@ -294,7 +319,7 @@ def draw_activation(cfg: Config, step: int, li: int) -> np.ndarray:
     L = cfg.layers[li]
     n = int(np.prod(L.act_shape))
     x = _normal(_key(cfg, step, li, T_ACT), n, cfg.act_std)
-    if cfg.relu:
+    if cfg.relu and L.kind != "bn":     # a batch-norm input is the normalised (unclipped) activation
         np.maximum(x, np.float32(0), out=x)
     x = x.reshape(L.act_shape)
     return to_bf16_bits(x) if cfg.act_dtype == "bf16" else x
@@ -333,7 +358,7 @@ def initial_state(cfg: Config, li: int) -> Dict[str, np.ndarray]:
     if L.has_bias:
         s["b"] = _normal(_key(cfg, 0, li, T_B), L.d_out, cfg.w_std)
         s["mom_b"] = np.zeros(L.d_out, np.float32)
-    if cfg.variant == "full":
+    if cfg.variant == "full" and L.kind != "bn":
         s["A"] = np.eye(L.d_a, dtype=np.float32)
         s["G"] = np.eye(L.d_out, dtype=np.float32)
         s["A_inv"] = np.zeros((L.d_a, L.d_a), np.float32)
@@ -352,4 +377,5 @@ def refresh_at(cfg: Config, step: int) -> bool:
 
 def hparams(cfg: Config) -> Dict[str, float]:
     return {"lr": cfg.lr, "momentum": cfg.momentum, "weight_decay": cfg.weight_decay,
-            "ema_decay": cfg.ema_decay, "damping": cfg.damping}
+            "ema_decay": cfg.ema_decay, "damping": cfg.damping, "damping_bn": cfg.damping * cfg.bn_damping_scale,
+            "rescale": cfg.rescale, "rescale_eps": 1e-9}

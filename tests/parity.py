@@ -37,36 +37,67 @@ def oracle_state(cfg, li):
     return {k: v.astype(np.float64) for k, v in synth.initial_state(cfg, li).items()}
 
 
-def lockstep(cfg, steps, tol, check_keys, stack=None, phase_mask=0):
+def _sched_struct(sched):
+    import second_order_optimizer_amd as K
+    return K.Schedule(sched["damping_init"], sched["damping_target"], sched["warmup_steps"],
+                      K.WARMUP_LINEAR if sched["warmup_shape"] == "linear" else K.WARMUP_GEOMETRIC,
+                      sched["bn_damping_scale"], sched["dense_steps"], sched["refresh_every_a"],
+                      sched["refresh_every_g"])
+
+
+def lockstep(cfg, steps, tol, check_keys, stack=None, phase_mask=0, packed=False, schedule=None):
     """Runs `steps` steps of cfg on the GPU (C ABI) and in the oracle, comparing
-    every layer's state after each step.  Returns the worst error per key."""
+    every layer's state after each step.  Returns the worst error per key.
+
+    packed: the library keeps A and G as packed upper triangles (set from and
+    read back into whole matrices with the oracle's packing).  schedule: a
+    dict of oracle.schedule; each step's damping and refresh bits come from
+    the library's kfac_schedule_hparams on the GPU side and from
+    oracle.schedule on the oracle side (the refresh bits must agree)."""
+    import second_order_optimizer_amd as K
     from second_order_optimizer_amd.stack import KfacStack
     variant = cfg.variant
     if stack is None:
-        stack = KfacStack(cfg.layers, variant, cfg.act_dtype, cfg.grad_dtype)
+        stack = KfacStack(cfg.layers, variant, cfg.act_dtype, cfg.grad_dtype,
+                          factor_layout="packed" if packed else "full")
     ostate = []
-    for li in range(len(cfg.layers)):
+    for li, L in enumerate(cfg.layers):
         st = synth.initial_state(cfg, li)
-        stack.set_state(li, st)
         ostate.append({k: v.astype(np.float64) for k, v in st.items()})
+        if packed and "A" in st:
+            st = dict(st, A=oracle.pack_upper(st["A"]), G=oracle.pack_upper(st["G"]))
+        stack.set_state(li, st)
     hp = synth.hparams(cfg)
     worst = {}
     import torch
     for t in range(1, steps + 1):
-        refresh = synth.refresh_at(cfg, t) if variant == "full" else True
+        hp_t = hp
+        if schedule is not None:
+            lam, lam_bn, ra, rg = oracle.schedule(schedule, t)
+            hp_t = dict(hp, damping=lam, damping_bn=lam_bn)
+            refresh = (bool(ra), bool(rg))
+            H = K.schedule_hparams(_sched_struct(schedule), t, stack.hparams(hp, phase_mask=phase_mask))
+            assert H.refresh == (K.REFRESH_A if ra else 0) | (K.REFRESH_G if rg else 0), (t, H.refresh, ra, rg)
+            assert abs(H.damping - lam) <= 1e-6 * lam and abs(H.damping_bn - lam_bn) <= 1e-6 * lam_bn
+        else:
+            refresh = synth.refresh_at(cfg, t) if variant == "full" else True
+            H = stack.hparams(hp, refresh=refresh, phase_mask=phase_mask)
         inputs = [synth.step_inputs(cfg, t, li) for li in range(len(cfg.layers))]
         for li in range(len(cfg.layers)):
             stack.set_inputs(li, inputs[li])
-        stack.step(stack.hparams(hp, refresh=refresh, phase_mask=phase_mask))
+        stack.step(H)
         torch.cuda.synchronize()
         assert stack.flags() == 0, f"device flags raised at step {t}"
         for li, L in enumerate(cfg.layers):
             if variant == "full":
-                ref, flags = oracle.step_full(L, ostate[li], inputs[li], hp, refresh)
+                ref, flags = oracle.step_full(L, ostate[li], inputs[li], hp_t, refresh)
             else:
-                ref, flags = oracle.step_diag(L, ostate[li], inputs[li], hp)
+                ref, flags = oracle.step_diag(L, ostate[li], inputs[li], hp_t)
             assert flags == 0
             got = stack.get_state(li)
+            if packed and "A" in got:
+                got["A"] = oracle.unpack_upper(got["A"], L.d_a)
+                got["G"] = oracle.unpack_upper(got["G"], L.d_out)
             for k in check_keys:
                 if k not in ref or k not in got:
                     continue

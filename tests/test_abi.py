@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version(lib):
-    assert K.abi_version() == 1
+    assert K.abi_version() == 2
     assert K.status_string(K.KFAC_ERR_WORKSPACE) == "workspace missing or too small"
 
 
@@ -161,6 +161,74 @@ def test_step_rejects_before_enqueue(lib, fn_name, mode):
     assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
     bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, phase_mask=8)
     assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
+
+
+@pytest.mark.parametrize("fn_name,mode", [("kfac_step_full", K.MODE_FULL), ("kfac_step_diag", K.MODE_DIAG)])
+def test_step_rejects_bad_scalars_and_fields(lib, fn_name, mode):
+    """Refresh bits beyond A | G, unknown option bits, a nonzero reserved
+    field of a layer and an unknown factor layout are argument errors,
+    returned before anything is enqueued."""
+    fn = getattr(lib, fn_name)
+    ws = 0x100000
+    good = _fake_layer()
+    need = K.workspace_size([good], mode)
+    assert _call(fn, [good], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, refresh=4), ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [good], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, refresh=-1), ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [good], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, options=2), ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [_fake_layer(reserved=1)], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3), ws, need) == K.KFAC_ERR_ARG
+    assert _call(fn, [_fake_layer(factor_layout=2)], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3), ws, need) == K.KFAC_ERR_ARG
+
+
+def _bn(**kw):
+    base = dict(d_in=1, d_out=6, rows=4, has_bias=True, batch=4, c_in=6, height=5, width=3, k=1, stride=1, pad=0)
+    base.update(kw)
+    return K.make_layer(K.BATCHNORM, base.pop("d_in"), base.pop("d_out"), base.pop("rows"), base.pop("has_bias"),
+                        **base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(), K.KFAC_OK),
+    (dict(d_in=2), K.KFAC_ERR_ARG),                 # gamma is one entry per channel
+    (dict(d_out=5), K.KFAC_ERR_ARG),                # d_out = channels
+    (dict(rows=20), K.KFAC_ERR_ARG),                # rows = samples
+    (dict(k=3), K.KFAC_ERR_ARG),
+    (dict(pad=1), K.KFAC_ERR_ARG),
+    (dict(act_dtype=K.BF16), K.KFAC_ERR_DTYPE),
+])
+def test_batchnorm_descriptor(lib, bad, code):
+    for mode in (K.MODE_FULL, K.MODE_DIAG):
+        assert _ws_status([_bn(**bad)], mode)[0] == code
+
+
+def test_schedule_matches_oracle(lib):
+    """kfac_schedule_hparams (host only) against the oracle's schedule: the
+    refresh bits exactly, the damping to float32 rounding, for both warm-up
+    shapes, with and without dense steps, over 80 steps; fields other than
+    damping, damping_bn and refresh are left alone."""
+    import numpy as np
+    import oracle
+    f32 = lambda x: float(np.float32(x))
+    for shape in ("linear", "geometric"):
+        for dense, ka, kg, tw in ((7, 5, 3, 10), (0, 4, 4, 0), (500, 20, 10, 200), (1, 1, 2, 3)):
+            sched = {"damping_init": f32(0.04), "damping_target": f32(2.5e-4), "warmup_steps": tw,
+                     "warmup_shape": shape, "bn_damping_scale": f32(16.0), "dense_steps": dense,
+                     "refresh_every_a": ka, "refresh_every_g": kg}
+            S = K.Schedule(sched["damping_init"], sched["damping_target"], tw,
+                           K.WARMUP_LINEAR if shape == "linear" else K.WARMUP_GEOMETRIC, sched["bn_damping_scale"],
+                           dense, ka, kg)
+            for t in list(range(1, 81)) + [499, 500, 501, 520, 530, 1000]:
+                H = K.schedule_hparams(S, t, K.hparams(0.1, 0.9, 5e-4, 0.95, 9.0, options=1))
+                lam, lam_bn, ra, rg = oracle.schedule(sched, t)
+                assert H.refresh == (K.REFRESH_A if ra else 0) | (K.REFRESH_G if rg else 0), (shape, dense, t)
+                assert abs(H.damping - lam) <= 1e-6 * lam and abs(H.damping_bn - lam_bn) <= 1e-6 * lam_bn
+                assert H.options == 1 and abs(H.lr - 0.1) < 1e-7
+    H = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3)
+    bad = [K.Schedule(0.1, 0.01, 5, 0, 1.0, 0, 0, 1), K.Schedule(0.1, 0.01, -1, 0, 1.0, 0, 1, 1),
+           K.Schedule(0.0, 0.01, 5, K.WARMUP_GEOMETRIC, 1.0, 0, 1, 1), K.Schedule(0.1, 0.01, 5, 7, 1.0, 0, 1, 1)]
+    for S in bad:
+        assert lib.kfac_schedule_hparams(ctypes.byref(S), 1, ctypes.byref(H)) == K.KFAC_ERR_ARG
+    assert lib.kfac_schedule_hparams(ctypes.byref(K.Schedule(0.1, 0.01, 5, 0, 1.0, 0, 1, 1)), 0,
+                                     ctypes.byref(H)) == K.KFAC_ERR_ARG
 
 
 def test_read_flags_rejects_null(lib):
