@@ -32,7 +32,7 @@ BF16_MFMA_TFLOPS = 2500.0      # dense bf16 MFMA
 
 METRIC = "K-FAC steps/s per layer stack; factor+precond TFLOP/s (%MFMA); diag-step GB/s"
 HEADLINE = "resnet18_diag"
-ORDER = ("resnet18_diag", "fc64", "resnet50_kfac", "mlp24_bf16", "pair16k_bf16")
+ORDER = ("resnet18_diag", "fc64", "resnet50_kfac", "mlp24_bf16", "pair16k_bf16", "resnet50_bn_diag")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "diag_resnet18_b128_traffic.md")
 DIAG_SRC = os.path.join(ROOT, "second_order_optimizer_amd", "csrc", "diag.hip")
 COPY_BYTES = 1 << 30     # the --traffic-probe calibration copy reads and writes 1 GiB
@@ -51,6 +51,8 @@ def workload_desc(cfg) -> dict:
         "mlp24_bf16": "24 x (1024->4096, 4096->1024) linears with bias, 8192 tokens, bf16 a/g, invert every 10",
         "pair16k_bf16": "4096->16384 and 16384->4096 linears with bias, 16384 tokens, bf16 a/g, invert every 20",
         "fc64": "one FC 64(+1)->32, batch 128, full K-FAC, invert every step",
+        "resnet50_bn_diag": "the 53 batch-norm layers of ResNet-50 at batch 32 @ 224x224 (gamma, beta per channel), "
+                            "diagonal Fisher step",
     }[cfg.name]
     d["refresh_every"] = cfg.refresh_every if cfg.variant == "full" else None
     return d
@@ -66,8 +68,14 @@ def diag_factor_bytes(cfg) -> int:
     n = 0
     for L in cfg.layers:
         n += 4 * (int(np.prod(L.act_shape)) + int(np.prod(L.grad_out_shape)))
-        n += 4 * (L.d_a + L.d_out)
+        n += 4 * (2 * L.d_out if L.kind == "bn" else L.d_a + L.d_out)
     return n
+
+
+def rescale_bytes(cfg) -> int:
+    """Algorithmic bytes of the weight rescaling: every conv / linear weight
+    read twice (norm, then scale) and written once, 12 B per weight."""
+    return 12 * sum(L.d_out * L.d_in for L in cfg.layers if L.kind != "bn")
 
 
 def diag_update_bytes(cfg) -> int:
@@ -239,7 +247,7 @@ def _time_phase(st, hp, pool, mask, n, refresh=False):
 def run_diag(cfg, args):
     import torch
     import synth
-    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_UPDATE
+    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_RESCALE, PHASE_UPDATE
     pool = max(1, args.pool)
     st = _load(cfg, pool)
     hp = synth.hparams(cfg)
@@ -260,25 +268,34 @@ def run_diag(cfg, args):
     nk = max(5, args.steps)
     t_fac = _time_phase(st, hp, pool, PHASE_FACTORS, nk)
     t_upd = _time_phase(st, hp, pool, PHASE_UPDATE, nk)
+    rb = rescale_bytes(cfg)
+    t_resc = _time_phase(st, dict(hp, rescale=True), pool, PHASE_RESCALE, nk) if rb else None
     assert st.flags() == 0, "device flags raised"
     del st
     torch.cuda.empty_cache()
     fb, ub = diag_factor_bytes(cfg), diag_update_bytes(cfg)
     gbs = lambda b, t: b / (t * 1e-3) / 1e9
-    return {
+    bn = all(L.kind == "bn" for L in cfg.layers)
+    out = {
         "ms_per_step": ms, "steps_per_s": 1e3 / ms, "steps": args.steps, "dtype": "f32",
-        "a7_diag_factors": {"kernels": "diag_colsq_kernel + diag_finish_kernel", "ms": t_fac, "bytes": fb,
-                            "GBps": gbs(fb, t_fac), "peak_GBps": HBM_PEAK_GBS, "frac": gbs(fb, t_fac) / HBM_PEAK_GBS},
+        "a7_diag_factors": {"kernels": "diag_bn_kernel" if bn else "diag_colsq_kernel + diag_finish_kernel",
+                            "ms": t_fac, "bytes": fb, "GBps": gbs(fb, t_fac), "peak_GBps": HBM_PEAK_GBS,
+                            "frac": gbs(fb, t_fac) / HBM_PEAK_GBS},
         "a8_diag_step": {"kernels": "diag_update_kernel", "ms": t_upd, "bytes": ub, "GBps": gbs(ub, t_upd),
                          "peak_GBps": HBM_PEAK_GBS, "frac": gbs(ub, t_upd) / HBM_PEAK_GBS},
         "step_GBps": gbs(fb + ub, ms),
     }
+    if rb:
+        out["rescale"] = {"kernels": "rescale_norm_kernel + rescale_apply_kernel", "ms": t_resc, "bytes": rb,
+                          "GBps": gbs(rb, t_resc), "frac": gbs(rb, t_resc) / HBM_PEAK_GBS}
+    return out
 
 
 def run_full(cfg, args):
     import torch
     import synth
-    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE
+    from second_order_optimizer_amd import PHASE_FACTORS, PHASE_INVERT, PHASE_RESCALE, PHASE_UPDATE, REFRESH_A, REFRESH_G
+    from second_order_optimizer_amd.stack import KfacStack
     pool = max(1, args.pool)
     st = _load(cfg, pool)
     hp = synth.hparams(cfg)
@@ -301,9 +318,17 @@ def run_full(cfg, args):
     n = max(3, min(10, args.steps))
     t_fac = _time_phase(st, hp, pool, PHASE_FACTORS, n)
     t_inv = _time_phase(st, hp, pool, PHASE_INVERT, max(2, n // 3), refresh=True)
+    t_inv_a = _time_phase(st, hp, pool, PHASE_INVERT, max(2, n // 3), refresh=REFRESH_A)
+    t_inv_g = _time_phase(st, hp, pool, PHASE_INVERT, max(2, n // 3), refresh=REFRESH_G)
     t_upd = _time_phase(st, hp, pool, PHASE_UPDATE, n)
+    rb = rescale_bytes(cfg)
+    t_resc = _time_phase(st, dict(hp, rescale=True), pool, PHASE_RESCALE, n)
     assert st.flags() == 0, "device flags raised"
-    del st
+    # the factor phase again with A and G stored as packed upper triangles
+    # (same input buffers; factor contents do not affect the timing)
+    pk = KfacStack(cfg.layers, "full", cfg.act_dtype, cfg.grad_dtype, factor_layout="packed", inputs_from=st)
+    t_fac_packed = _time_phase(pk, hp, pool, PHASE_FACTORS, n)
+    del pk, st
     torch.cuda.empty_cache()
     fs, fp, fi = full_flops(cfg.layers)
     syrk_peak = BF16_MFMA_TFLOPS if cfg.act_dtype == "bf16" else FP32_MFMA_TFLOPS
@@ -315,7 +340,15 @@ def run_full(cfg, args):
         "precond_update": {"ms": t_upd, "flops": fp, "tflops": tf(fp, t_upd), "peak_tflops": FP32_MFMA_TFLOPS,
                            "frac": tf(fp, t_upd) / FP32_MFMA_TFLOPS, "dtype": "f32"},
         "invert": {"ms": t_inv, "amortised_ms": t_inv / k, "flops": fi, "tflops": tf(fi, t_inv),
-                   "peak_tflops": FP32_MFMA_TFLOPS, "frac": tf(fi, t_inv) / FP32_MFMA_TFLOPS, "dtype": "f32"},
+                   "peak_tflops": FP32_MFMA_TFLOPS, "frac": tf(fi, t_inv) / FP32_MFMA_TFLOPS, "dtype": "f32",
+                   "A_only_ms": t_inv_a, "G_only_ms": t_inv_g},
+        "factors_packed": {"ms": t_fac_packed, "tflops": tf(fs, t_fac_packed),
+                           "frac": tf(fs, t_fac_packed) / syrk_peak,
+                           "ema_bytes_whole": 8 * sum(L.d_a ** 2 + L.d_out ** 2 for L in cfg.layers),
+                           "ema_bytes_packed": 4 * sum(L.d_a * (L.d_a + 1) + L.d_out * (L.d_out + 1)
+                                                       for L in cfg.layers)},
+        "rescale": {"kernels": "rescale_norm_kernel + rescale_apply_kernel", "ms": t_resc, "bytes": rb,
+                    "GBps": rb / (t_resc * 1e-3) / 1e9, "frac": rb / (t_resc * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     ideal = fs / (syrk_peak * 1e12) + fp / (FP32_MFMA_TFLOPS * 1e12)
     out["combined_mfma_frac"] = ideal / ((t_fac + t_upd) * 1e-3)

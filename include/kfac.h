@@ -91,7 +91,8 @@ enum { KFAC_FACTORS_FULL = 0, KFAC_FACTORS_PACKED = 1 };
 enum { KFAC_F32 = 0, KFAC_BF16 = 1 };
 /* kfac_workspace_size modes */
 enum { KFAC_MODE_FULL = 0, KFAC_MODE_DIAG = 1 };
-/* kfac_hparams_t.phase_mask bits; 0 means all phases.
+/* kfac_hparams_t.phase_mask bits; 0 means all phases.  RESCALE = the weight
+ * rescaling (runs only when options has KFAC_OPT_RESCALE; after UPDATE).
  *   full: FACTORS = factor construction + EMA, INVERT = damped inverses
  *         (only when refresh != 0), UPDATE = precondition + momentum/decay/write
  *   diag: FACTORS = dA, dG of this batch (a streaming reduction of a and g
@@ -99,7 +100,8 @@ enum { KFAC_MODE_FULL = 0, KFAC_MODE_DIAG = 1 };
  *         every layer kind; UPDATE = the fused elementwise step, which reads
  *         dA / dG from those buffers (so an UPDATE-only call uses whatever
  *         they hold, e.g. the last FACTORS call's result). */
-enum { KFAC_PHASE_FACTORS = 1, KFAC_PHASE_INVERT = 2, KFAC_PHASE_UPDATE = 4, KFAC_PHASE_ALL = 7 };
+enum { KFAC_PHASE_FACTORS = 1, KFAC_PHASE_INVERT = 2, KFAC_PHASE_UPDATE = 4, KFAC_PHASE_RESCALE = 8,
+       KFAC_PHASE_ALL = 15 };
 /* kfac_hparams_t.refresh bits (full method): which damped inverses this step
  * recomputes */
 enum { KFAC_REFRESH_A = 1, KFAC_REFRESH_G = 2, KFAC_REFRESH_BOTH = 3 };
@@ -201,7 +203,7 @@ typedef struct kfac_hparams {
  * scaled in place to Frobenius norm sqrt(2 d_out):
  *     W <- W sqrt(2 d_out) / (||W||_F + rescale_eps)
  * d_out = the layer's output width (channels of a conv2d).  Batch-norm
- * parameters are not rescaled.  Runs as part of the UPDATE phase. */
+ * parameters are not rescaled.  Runs as the RESCALE phase, after UPDATE. */
 
 /* Bytes of workspace the given stack needs in `mode` (host only, no GPU
  * call).  Returns KFAC_ERR_ARG / _DTYPE / _UNSUPPORTED for descriptors the

@@ -23,7 +23,7 @@ OPT_RESCALE = 1
 WARMUP_LINEAR, WARMUP_GEOMETRIC = 0, 1
 F32, BF16 = 0, 1
 MODE_FULL, MODE_DIAG = 0, 1
-PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE, PHASE_ALL = 1, 2, 4, 7
+PHASE_FACTORS, PHASE_INVERT, PHASE_UPDATE, PHASE_RESCALE, PHASE_ALL = 1, 2, 4, 8, 15
 FLAG_NOT_PD, FLAG_NONFINITE = 1, 2
 
 EXPORTS = ("kfac_workspace_size", "kfac_step_full", "kfac_step_diag", "kfac_step_diag_noalloc", "kfac_read_flags",

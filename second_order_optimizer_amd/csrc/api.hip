@@ -90,7 +90,7 @@ kfac_status_t check_ptr(const void* p, bool required) {
   return aligned16(p) ? KFAC_OK : KFAC_ERR_ALIGN;
 }
 
-kfac_status_t check_layer_ptrs(const kfac_layer_t& L, int mode, int phases, int refresh) {
+kfac_status_t check_layer_ptrs(const kfac_layer_t& L, int mode, int phases, int refresh, int options) {
   const bool bias = L.has_bias != 0;
   kfac_status_t s;
   auto req = [&](const void* p, bool r) { return (s = check_ptr(p, r)) != KFAC_OK; };
@@ -98,7 +98,9 @@ kfac_status_t check_layer_ptrs(const kfac_layer_t& L, int mode, int phases, int 
   const bool upd = phases & KFAC_PHASE_UPDATE;
   const bool inv = (phases & KFAC_PHASE_INVERT) && refresh != 0;
   if (req(L.a, fac) || req(L.g, fac)) return s;
-  if (req(L.grad_w, upd) || req(L.w, upd) || req(L.mom_w, upd)) return s;
+  // the weight rescaling writes the weight of every conv / linear layer
+  const bool resc = (phases & KFAC_PHASE_RESCALE) && (options & KFAC_OPT_RESCALE) && L.kind != KFAC_BATCHNORM;
+  if (req(L.grad_w, upd) || req(L.w, upd || resc) || req(L.mom_w, upd)) return s;
   if (bias && (req(L.grad_b, upd) || req(L.b, upd) || req(L.mom_b, upd))) return s;
   if (!bias && (L.grad_b || L.b || L.mom_b || L.F_b)) return KFAC_ERR_ARG;
   if (mode == KFAC_MODE_FULL && L.kind != KFAC_BATCHNORM) {
@@ -132,7 +134,7 @@ kfac_status_t validate(const kfac_layer_t* layers, int32_t n, const kfac_hparams
   if ((hp->options & ~KFAC_OPT_RESCALE) != 0) return KFAC_ERR_ARG;
   *phases = hp->phase_mask == 0 ? KFAC_PHASE_ALL : hp->phase_mask;
   for (int i = 0; i < n; ++i) {
-    s = check_layer_ptrs(layers[i], mode, *phases, hp->refresh);
+    s = check_layer_ptrs(layers[i], mode, *phases, hp->refresh, hp->options);
     if (s != KFAC_OK) return s;
   }
   return KFAC_OK;

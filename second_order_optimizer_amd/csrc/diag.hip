@@ -777,10 +777,10 @@ kfac_status_t enqueue_steps(const kfac_layer_t* layers, int n, const kfac_hparam
       hipLaunchKernelGGL(diag_update_kernel, dim3(blocks), dim3(kUpdThreads), 0, stream, S);
       KFAC_HIP_TRY(hipGetLastError());
     }
-    if ((hp.options & KFAC_OPT_RESCALE) && !P.rescale.empty()) {
-      kfac_status_t r = launch_rescale(P.rescale, hp.rescale_eps, stream);
-      if (r != KFAC_OK) return r;
-    }
+  }
+  if ((phases & KFAC_PHASE_RESCALE) && (hp.options & KFAC_OPT_RESCALE) && !P.rescale.empty()) {
+    kfac_status_t r = launch_rescale(P.rescale, hp.rescale_eps, stream);
+    if (r != KFAC_OK) return r;
   }
   return KFAC_OK;
 }

@@ -1406,10 +1406,10 @@ kfac_status_t full_enqueue(const kfac_layer_t* layers, int n, const kfac_hparams
     if (phases & KFAC_PHASE_UPDATE) {
       r = update_phase(kf.data(), nk, hp, P, flags, st, side);
       if (r != KFAC_OK) return r;
-      if (hp.options & KFAC_OPT_RESCALE) {
-        r = launch_rescale(P.rescale, hp.rescale_eps, st);
-        if (r != KFAC_OK) return r;
-      }
+    }
+    if ((phases & KFAC_PHASE_RESCALE) && (hp.options & KFAC_OPT_RESCALE)) {
+      r = launch_rescale(P.rescale, hp.rescale_eps, st);
+      if (r != KFAC_OK) return r;
     }
   }
   if (!bn.empty() && (phases & (KFAC_PHASE_FACTORS | KFAC_PHASE_UPDATE))) {

@@ -294,6 +294,9 @@ __device__ inline int tr_off(int cb0, int ks, int lane) {
 // s_waitcnt with only the vector-memory counter limited to n (n < 16)
 #define KFAC_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
 
+// PACKED: F holds the packed upper triangle (a separate instantiation, so
+// that the whole-storage epilogue keeps its registers).
+template <bool PACKED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 syrk_bf16_dma_kernel(Batch batch) {
   __shared__ __attribute__((aligned(16))) unsigned short ring[kNS][2][kOpElems];
@@ -468,11 +471,37 @@ syrk_bf16_dma_kernel(Batch batch) {
         // unconditional loads (an element outside the upper triangle reads the
         // block's first element, which is inside it) keep them in one batch
         float o[16];
+        if constexpr (PACKED) {
+          // packed row starts relative to this lane's first row rb: element
+          // (rb + k, col) lies at B(rb) + k (ldf - 1) - k (2 rb + k - 1) / 2 + col,
+          // with B(i) = i (ldf - 1) - i (i - 1) / 2 (one 64-bit base per lane,
+          // 32-bit offsets)
+          const int rb = r0 + 4 * (lane >> 5);
+          float* Fb = F + (static_cast<int64_t>(rb) * (ldf - 1) - static_cast<int64_t>(rb) * (rb - 1) / 2);
+          const int fb0 = static_cast<int>(packed_index(r0, c0, ldf) - (static_cast<int64_t>(rb) * (ldf - 1) -
+                                                                         static_cast<int64_t>(rb) * (rb - 1) / 2));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = 8 * (r >> 2) + (r & 3);
+            const int row = rb + k;
+            const bool in = row < width && col < width && row <= col;
+            o[r] = Fb[in ? k * (ldf - 1) - k * (2 * rb + k - 1) / 2 + col : fb0];
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int k = 8 * (r >> 2) + (r & 3);
+            const int row = rb + k;
+            const bool in = row < width && col < width && row <= col;
+            const float v = P.beta * o[r] + P.alpha * acc[i][j][r];
+            if (in) Fb[k * (ldf - 1) - k * (2 * rb + k - 1) / 2 + col] = v;
+          }
+          continue;   // the upper triangle is all a packed factor holds
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const bool in = row < width && col < width && row <= col;
-          o[r] = F[in ? f_index(P, row, col) : f_index(P, r0, c0)];
+          o[r] = F[in ? static_cast<int64_t>(row) * ldf + col : static_cast<int64_t>(r0) * ldf + c0];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -480,10 +509,9 @@ syrk_bf16_dma_kernel(Batch batch) {
           const int row = r0 + rr;
           const bool in = row < width && col < width && row <= col;
           const float v = P.beta * o[r] + P.alpha * acc[i][j][r];
-          if (in) F[f_index(P, row, col)] = v;
+          if (in) F[static_cast<int64_t>(row) * ldf + col] = v;
           stg[(lane & 31) * 33 + rr] = v;
         }
-        if (P.packed) continue;   // the upper triangle is all a packed factor holds
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int cc = 2 * q + (lane >> 5), rr = lane & 31;
@@ -500,14 +528,14 @@ syrk_bf16_dma_kernel(Batch batch) {
       for (int r = 0; r < 16; ++r) {
         const int m = i0 + cs0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= width) continue;
-        const int64_t idx = f_index(P, m, width);
+        const int64_t idx = PACKED ? packed_index(m, width, ldf) : static_cast<int64_t>(m) * ldf + width;
         const float o = P.beta * F[idx] + P.alpha * acc[i][0][r];
         F[idx] = o;
-        if (!P.packed) F[static_cast<int64_t>(width) * ldf + m] = o;
+        if (!PACKED) F[static_cast<int64_t>(width) * ldf + m] = o;
       }
     }
     if (ti == 0 && cs0 == 0 && lane == 0) {
-      const int64_t c = f_index(P, width, width);
+      const int64_t c = PACKED ? packed_index(width, width, ldf) : static_cast<int64_t>(width) * ldf + width;
       F[c] = P.beta * F[c] + P.alpha * static_cast<float>(rows);
     }
   }
@@ -525,7 +553,7 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
     Prob p;
     int pass;
   };
-  std::vector<Piece> dma, ragged;
+  std::vector<Piece> dma, dma_packed, ragged;   // one kernel instantiation per launch
   for (const SyrkBf16Prob& q : probs) {
     Prob p{};
     p.X = q.X;
@@ -551,7 +579,7 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
       c.X = q.X + r0 * q.width;
       c.rows = std::min<int64_t>(chunk, q.rows - r0);
       c.beta = pass == 0 ? q.beta : 1.0f;
-      dma.push_back({c, pass});
+      (q.packed ? dma_packed : dma).push_back({c, pass});
     }
   }
   auto launch = [&](const std::vector<Piece>& pieces, bool use_dma) -> kfac_status_t {
@@ -573,7 +601,8 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
         int max_tiles = 0;
         for (int j = 0; j < b.n; ++j) max_tiles = std::max(max_tiles, b.p[j].tiles);
         b.xcd_run = max_tiles <= kXcdRunMaxTiles ? kXcdRun : 1;
-        if (use_dma) hipLaunchKernelGGL(syrk_bf16_dma_kernel, dim3(blocks), dim3(512), 0, st, b);
+        if (use_dma && b.p[0].packed) hipLaunchKernelGGL(syrk_bf16_dma_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
+        else if (use_dma) hipLaunchKernelGGL(syrk_bf16_dma_kernel<false>, dim3(blocks), dim3(512), 0, st, b);
         else hipLaunchKernelGGL(syrk_bf16_kernel, dim3(blocks), dim3(512), 0, st, b);
         if (hipGetLastError() != hipSuccess) return KFAC_ERR_HIP;
       }
@@ -581,6 +610,7 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
     return KFAC_OK;
   };
   kfac_status_t r = launch(dma, true);
+  if (r == KFAC_OK) r = launch(dma_packed, true);
   return r != KFAC_OK ? r : launch(ragged, false);
 }
 

@@ -43,7 +43,7 @@ class KfacStack:
     """
 
     def __init__(self, shapes: Sequence, variant: str, act_dtype: str = "f32", grad_dtype: str = "f32",
-                 device="cuda", pool: int = 1, factor_layout: str = "full"):
+                 device="cuda", pool: int = 1, factor_layout: str = "full", inputs_from: "KfacStack" = None):
         self.shapes = list(shapes)
         self.packed = factor_layout == "packed"
         self.variant = variant
@@ -58,9 +58,13 @@ class KfacStack:
         for L in self.shapes:
             st = self._alloc_state(L)
             self.state.append(st)
-        for _ in range(pool):
-            self.inputs.append([self._alloc_inputs(L) for L in self.shapes])
+        if inputs_from is not None:       # read the input buffers of another stack of the same shapes
+            self.inputs = inputs_from.inputs
+        else:
+            for _ in range(pool):
+                self.inputs.append([self._alloc_inputs(L) for L in self.shapes])
         self.active = 0
+        self._descs = {}          # one descriptor array per input slot (the buffers never move)
         self._build_desc()
         self.ws_bytes = workspace_size(self.desc, self.mode)
         self._ws = torch.zeros(self.ws_bytes + 256, dtype=torch.uint8, device=self.dev)
@@ -107,6 +111,9 @@ class KfacStack:
                 "grad_b": torch.zeros(L.d_out, dtype=torch.float32, device=self.dev) if L.has_bias else None}
 
     def _build_desc(self):
+        if self.active in self._descs:
+            self.desc = self._descs[self.active]
+            return
         descs = []
         for li, L in enumerate(self.shapes):
             t = dict(self.state[li])
@@ -121,6 +128,7 @@ class KfacStack:
                 width=L.w if conv else 0, k=L.k if conv else 0, stride=L.stride if conv else 0,
                 pad=L.pad if conv else 0, factor_layout=FACTORS_PACKED if self.packed else FACTORS_FULL, **t))
         self.desc = layer_array(descs)
+        self._descs[self.active] = self.desc
 
     # -- data movement ----------------------------------------------------
     def set_inputs(self, li: int, arrays: Dict[str, np.ndarray], slot: int = 0):

@@ -235,13 +235,23 @@ def _c5(layers=None):
                   act_std=1.0, grad_std=1e-3, relu=False)
 
 
+def _bn50(layers=None):
+    """The 53 batch-norm layers of ResNet-50 at 32 x 224^2 (one after every
+    convolution, on its output planes), alone: their diagonal-Fisher step."""
+    bn = [L for L in with_batchnorm(resnet50_layers()) if L.kind == "bn"]
+    return Config(5, "resnet50_bn_diag", "diag", tuple(layers or bn),
+                  steps=10, lr=0.1, momentum=0.9, weight_decay=5e-4, ema_decay=0.95,
+                  damping=2.5e-4, act_std=1.0, grad_std=1e-3, relu=False)
+
+
 def full_config(name: str) -> Config:
-    """The five workloads at their stated sizes."""
+    """The five workloads at their stated sizes, and the batch-norm layers of
+    ResNet-50 on their own."""
     return {"fc64": _c1, "resnet18_diag": _c2, "resnet50_kfac": _c3,
-            "mlp24_bf16": _c4, "pair16k_bf16": _c5}[name]()
+            "mlp24_bf16": _c4, "pair16k_bf16": _c5, "resnet50_bn_diag": _bn50}[name]()
 
 
-CONFIG_NAMES = ("fc64", "resnet18_diag", "resnet50_kfac", "mlp24_bf16", "pair16k_bf16")
+CONFIG_NAMES = ("fc64", "resnet18_diag", "resnet50_kfac", "mlp24_bf16", "pair16k_bf16", "resnet50_bn_diag")
 
 
 def small_config(name: str) -> Config:

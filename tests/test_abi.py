@@ -159,7 +159,7 @@ def test_step_rejects_before_enqueue(lib, fn_name, mode):
     bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3)
     bad.reserved = 1
     assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
-    bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, phase_mask=8)
+    bad = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, phase_mask=16)
     assert _call(fn, [good], bad, ws, need) == K.KFAC_ERR_ARG
 
 
@@ -177,6 +177,10 @@ def test_step_rejects_bad_scalars_and_fields(lib, fn_name, mode):
     assert _call(fn, [good], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, options=2), ws, need) == K.KFAC_ERR_ARG
     assert _call(fn, [_fake_layer(reserved=1)], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3), ws, need) == K.KFAC_ERR_ARG
     assert _call(fn, [_fake_layer(factor_layout=2)], K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3), ws, need) == K.KFAC_ERR_ARG
+    # a rescaling-only call needs the weight it writes
+    resc = K.hparams(0.1, 0.9, 5e-4, 0.95, 1e-3, phase_mask=K.PHASE_RESCALE, options=K.OPT_RESCALE)
+    assert _call(fn, [_fake_layer(w=None, grad_w=None, mom_w=None, b=None, grad_b=None, mom_b=None, F_b=None,
+                                  has_bias=0)], resc, ws, need) == K.KFAC_ERR_ARG
 
 
 def _bn(**kw):
