@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkfac.so")
+# KFAC_LIBRARY names another build of the same library (the host-sanitized
+# one the sanitizer test loads); there is no fallback when it is missing.
+LIB_PATH = os.environ.get("KFAC_LIBRARY") or os.path.join(_PKG, "libkfac.so")
 
 KFAC_OK, KFAC_ERR_ARG, KFAC_ERR_DTYPE, KFAC_ERR_ALIGN, KFAC_ERR_WORKSPACE, KFAC_ERR_UNSUPPORTED, KFAC_ERR_HIP = range(7)
 LINEAR, CONV2D, BATCHNORM = 0, 1, 2

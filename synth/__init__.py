@@ -276,6 +276,9 @@ def small_config(name: str) -> Config:
         return dataclasses.replace(_c4(mlp_layers(2, 200, 513, 700)), steps=3, refresh_every=2)
     if name == "pair16k_bf16":
         return dataclasses.replace(_c5(mlp_layers(1, 256, 1023, 900)), steps=3, refresh_every=2)
+    if name == "resnet50_bn_diag":
+        bn = [L for L in with_batchnorm(resnet50_layers(batch=2, res=64)) if L.kind == "bn"]
+        return dataclasses.replace(_bn50(bn), steps=3)
     raise KeyError(name)
 
 

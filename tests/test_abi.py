@@ -259,3 +259,46 @@ def test_row_count_limits(lib):
     assert _ws_status([_linear(rows=big, act_dtype=K.BF16, grad_dtype=K.BF16)], K.MODE_FULL)[0] == K.KFAC_OK
     assert _ws_status([_linear(rows=(1 << 31) - 1)], K.MODE_FULL)[0] == K.KFAC_OK
     assert _ws_status([_linear(rows=big)], K.MODE_DIAG)[0] == K.KFAC_OK
+
+
+def _descs(cfg, packed):
+    out = []
+    for L in cfg.layers:
+        conv = L.kind in ("conv", "bn")
+        bn = L.kind == "bn"
+        dt = K.F32 if (bn or cfg.act_dtype == "f32") else K.BF16
+        gt = K.F32 if (bn or cfg.grad_dtype == "f32") else K.BF16
+        out.append(K.make_layer(
+            {"conv": K.CONV2D, "bn": K.BATCHNORM}.get(L.kind, K.LINEAR), L.d_in, L.d_out, L.rows, L.has_bias,
+            act_dtype=dt, grad_dtype=gt, batch=L.batch if conv else 0, c_in=L.c_in if conv else 0,
+            height=L.h if conv else 0, width=L.w if conv else 0, k=L.k if conv else 0,
+            stride=L.stride if conv else 0, pad=L.pad if conv else 0,
+            factor_layout=K.FACTORS_PACKED if packed else K.FACTORS_FULL))
+    return out
+
+
+def test_workspace_size_every_workload(lib):
+    """Plans every workload at its full and its small size, with and without a
+    batch-norm layer after each convolution, in every mode and factor layout
+    it admits: the planner accepts each, and packed storage never needs more
+    workspace than whole storage."""
+    import dataclasses
+    import synth
+    for name in synth.CONFIG_NAMES:
+        for cfg in (synth.full_config(name), synth.small_config(name)):
+            variants = [cfg.layers]
+            if any(L.kind == "conv" for L in cfg.layers):
+                variants.append(synth.with_batchnorm(cfg.layers))
+            for layers in variants:
+                c = dataclasses.replace(cfg, layers=tuple(layers))
+                modes = [K.MODE_FULL] + ([K.MODE_DIAG] if c.act_dtype == "f32" and c.grad_dtype == "f32" else [])
+                for mode in modes:
+                    sizes = []
+                    for packed in ((False, True) if mode == K.MODE_FULL else (False,)):
+                        arr = K.layer_array(_descs(c, packed))
+                        out = ctypes.c_size_t(0)
+                        st = K.load().kfac_workspace_size(arr, len(layers), mode, ctypes.byref(out))
+                        assert st == K.KFAC_OK, (name, len(layers), mode, packed, K.status_string(st))
+                        assert out.value > 0 and out.value % 256 == 0
+                        sizes.append(out.value)
+                    assert sizes[-1] <= sizes[0], (name, mode, sizes)
