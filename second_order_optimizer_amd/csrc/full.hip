@@ -592,12 +592,16 @@ kfac_status_t launch_bias_col(std::vector<BcProb>& probs, int stage, const kfac_
   return KFAC_OK;
 }
 
+// row length of the preconditioning intermediate T: a multiple of 4 floats,
+// so that its rows can be loaded 16 bytes at a time
+inline int t_ld(int d_a) { return (d_a + 3) & ~3; }
+
 struct FullPlan {
   size_t ws_bytes = kFlagBytes;
   std::vector<RescaleSeg> rescale;   // per layer: its weight (KFAC_OPT_RESCALE)
   std::vector<float*> part;      // per layer and factor (2 li + which): split-K partials, or null
   std::vector<int> nsplit;       // per layer and factor
-  std::vector<float*> T;         // per layer, d_out x d_a
+  std::vector<float*> T;         // per layer, d_out x d_a, rows of t_ld(d_a) floats (16-byte aligned rows)
   std::vector<float*> tb;        // per layer: column d_in of T (bias-column layers), else null
   std::vector<float*> xcol;      // per layer and factor: fp32 convolution tensor as [rows, width], or null
   std::vector<int> xcol_ld;      // their row pitch (floats)
@@ -658,7 +662,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   }
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
-    P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * g.d_a * 4)));
+    P.T.push_back(reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * t_ld(g.d_a) * 4)));
     P.tb.push_back(bias_column_split(g) ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.d_out) * 4)) : nullptr);
   }
   for (int li = 0; li < n; ++li) {
@@ -1305,7 +1309,7 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     p.ldb = g.d_a;
     p.b_special = -1;
     p.C = P.T[li];
-    p.ldc = g.d_a;
+    p.ldc = t_ld(g.d_a);
     p.M = g.d_out;
     p.N = ncols;
     p.kb = 0;
@@ -1321,7 +1325,7 @@ kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams
     q.lda = g.d_out;
     q.a_special = -1;
     q.B = P.T[li];
-    q.ldb = g.d_a;
+    q.ldb = t_ld(g.d_a);
     q.b_special = -1;
     q.M = g.d_out;
     q.N = ncols;

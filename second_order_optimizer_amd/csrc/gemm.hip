@@ -175,6 +175,91 @@ __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti
   }
 }
 
+// Epilogue: accumulator r of block (si, sj) is C[row][col] with
+// row = i0 + wm + 32 si + 8 (r / 4) + 4 (lane / 32) + r % 4, col = j0 + wn + 32 sj + lane % 32.
+// r1a / r1b (EPI_STORE only, may be null): a rank-one term r1a[row] r1b[col]
+// added to the product before scaling (the bias column of A taken out of the
+// contraction).
+template <int EPI, typename C>
+__device__ __forceinline__ void gemm_epilogue(const GemmBatch& batch, const GemmProb& P, float* Cp,
+                                              f32x16 (&acc)[C::kBI][C::kBJ], int i0, int j0, int wm, int wn,
+                                              int lane, const float* __restrict__ r1a,
+                                              const float* __restrict__ r1b) {
+  // Read-modify-write epilogues first issue every read of a block row (from a
+  // clamped, always valid address), then compute and store: one memory round
+  // trip per block row instead of one per element.
+  // (the factor SYRK reads C in place: its EMA problems are few and the
+  // staging registers would cost the far more numerous split problems)
+  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE;
+  const bool ema = EPI == EPI_SYRK && P.nsplit == 1;
+  bool bad = false;
+  // block rows by a compile-time index: a runtime one would place acc in scratch
+  static_for<0, C::kBI>([&](auto si_c) {
+    constexpr int si = decltype(si_c)::value;
+    float c0v[C::kBJ][16], c1v[C::kBJ][16];
+    if (kReads) {
+#pragma unroll
+      for (int sj = 0; sj < C::kBJ; ++sj) {
+        const int col = j0 + wn + 32 * sj + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const bool in = row < P.M && col < P.N;
+          const int64_t idx = in ? static_cast<int64_t>(row) * P.ldc + col : 0;
+          if (EPI == EPI_UPDATE) {
+            const bool wcol = !in || col < P.d_in;
+            const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
+            c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
+            c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
+          } else {
+            c0v[sj][r] = Cp[idx];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int sj = 0; sj < C::kBJ; ++sj) {
+      const int col = j0 + wn + 32 * sj + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= P.M || col >= P.N) continue;
+        float v = acc[si][sj][r];
+        if (EPI == EPI_STORE && r1a != nullptr) v = fmaf(r1a[row], r1b[col], v);
+        const int64_t idx = static_cast<int64_t>(row) * P.ldc + col;
+        if (EPI == EPI_STORE) {
+          Cp[idx] = P.alpha * v;
+        } else if (EPI == EPI_SUB) {
+          Cp[idx] = c0v[sj][r] - P.alpha * v;
+        } else if (EPI == EPI_SYRK && !ema) {
+          Cp[idx] = P.alpha * v;
+        } else if (EPI == EPI_SYRK) {
+          if (row <= col) {
+            const int64_t u = P.c_packed ? packed_index(row, col, P.M) : idx;
+            const float o = P.beta != 0.f ? P.beta * Cp[u] + P.alpha * v : P.alpha * v;
+            Cp[u] = o;
+            if (row != col && !P.c_packed) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
+          }
+        } else if (EPI == EPI_UPDATE) {
+          const bool wcol = col < P.d_in;
+          float* wp = wcol ? P.W + static_cast<int64_t>(row) * P.d_in + col : P.Wb + row;
+          float* vp = wcol ? P.V + static_cast<int64_t>(row) * P.d_in + col : P.Vb + row;
+          const float w = c0v[sj][r];
+          const float d = fmaf(batch.sc.weight_decay, w, v);
+          const float vn = fmaf(batch.sc.momentum, c1v[sj][r], d);
+          const float wn2 = fmaf(-batch.sc.lr, vn, w);
+          *vp = vn;
+          *wp = wn2;
+          bad |= !(isfinite(vn) && isfinite(wn2));
+        }
+      }
+    }
+  });
+  if (EPI == EPI_UPDATE) {
+    if (__any(bad) && lane == 0) raise_flag(batch.sc.flags, KFAC_FLAG_NONFINITE);
+  }
+}
+
 template <int AMODE, int BMODE, int EPI, bool BIG>
 __device__ __forceinline__ void gemm_f32_body(const GemmBatch& batch) {
   constexpr int TK = EPI == EPI_SYRK ? kTileKSyrk : kTileKDeep;
@@ -288,80 +373,7 @@ __device__ __forceinline__ void gemm_f32_body(const GemmBatch& batch) {
   if (live) main_loop(std::true_type{});
   else main_loop(std::false_type{});
 
-  // epilogue: accumulator r of block (si, sj) is C[row][col] with
-  // row = i0 + wm + 32 si + 8 (r / 4) + 4 (lane / 32) + r % 4, col = j0 + wn + 32 sj + lane % 32.
-  // Read-modify-write epilogues first issue every read of a block row (from a
-  // clamped, always valid address), then compute and store: one memory round
-  // trip per block row instead of one per element.
-  // (the factor SYRK reads C in place: its EMA problems are few and the
-  // staging registers would cost the far more numerous split problems)
-  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE;
-  const bool ema = EPI == EPI_SYRK && P.nsplit == 1;
-  bool bad = false;
-  // block rows by a compile-time index: a runtime one would place acc in scratch
-  static_for<0, C::kBI>([&](auto si_c) {
-    constexpr int si = decltype(si_c)::value;
-    float c0v[C::kBJ][16], c1v[C::kBJ][16];
-    if (kReads) {
-#pragma unroll
-      for (int sj = 0; sj < C::kBJ; ++sj) {
-        const int col = j0 + wn + 32 * sj + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const bool in = row < P.M && col < P.N;
-          const int64_t idx = in ? static_cast<int64_t>(row) * P.ldc + col : 0;
-          if (EPI == EPI_UPDATE) {
-            const bool wcol = !in || col < P.d_in;
-            const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
-            c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
-            c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
-          } else {
-            c0v[sj][r] = Cp[idx];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int sj = 0; sj < C::kBJ; ++sj) {
-      const int col = j0 + wn + 32 * sj + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= P.M || col >= P.N) continue;
-        const float v = acc[si][sj][r];
-        const int64_t idx = static_cast<int64_t>(row) * P.ldc + col;
-        if (EPI == EPI_STORE) {
-          Cp[idx] = P.alpha * v;
-        } else if (EPI == EPI_SUB) {
-          Cp[idx] = c0v[sj][r] - P.alpha * v;
-        } else if (EPI == EPI_SYRK && !ema) {
-          Cp[idx] = P.alpha * v;
-        } else if (EPI == EPI_SYRK) {
-          if (row <= col) {
-            const int64_t u = P.c_packed ? packed_index(row, col, P.M) : idx;
-            const float o = P.beta != 0.f ? P.beta * Cp[u] + P.alpha * v : P.alpha * v;
-            Cp[u] = o;
-            if (row != col && !P.c_packed) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
-          }
-        } else if (EPI == EPI_UPDATE) {
-          const bool wcol = col < P.d_in;
-          float* wp = wcol ? P.W + static_cast<int64_t>(row) * P.d_in + col : P.Wb + row;
-          float* vp = wcol ? P.V + static_cast<int64_t>(row) * P.d_in + col : P.Vb + row;
-          const float w = c0v[sj][r];
-          const float d = fmaf(batch.sc.weight_decay, w, v);
-          const float vn = fmaf(batch.sc.momentum, c1v[sj][r], d);
-          const float wn2 = fmaf(-batch.sc.lr, vn, w);
-          *vp = vn;
-          *wp = wn2;
-          bad |= !(isfinite(vn) && isfinite(wn2));
-        }
-      }
-    }
-  });
-  if (EPI == EPI_UPDATE) {
-    if (__any(bad) && lane == 0) raise_flag(batch.sc.flags, KFAC_FLAG_NONFINITE);
-  }
+  gemm_epilogue<EPI, C>(batch, P, Cp, acc, i0, j0, wm, wn, lane, nullptr, nullptr);
 }
 
 template <int AMODE, int BMODE, int EPI, bool BIG>
@@ -376,6 +388,195 @@ __global__ void __launch_bounds__((Cfg<BIG, kTileKDeep>::kThreads)) gemm_f32_ker
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 gemm_f32_syrk_kernel(GemmBatch batch) {
   gemm_f32_body<OP_MN, OP_MN, EPI_SYRK, false>(batch);
+}
+
+// ---------------------------------------------------------------------------
+// The 256 x 256 kernel with direct-to-LDS operand loads, for whole-K problems
+// (the preconditioning products): K a multiple of 16 (a bias column of an
+// OP_K A, the last index of the contraction, is added in the epilogue as a
+// rank-one term), B in OP_MN layout, 16-byte aligned rows.  Each stage holds
+// 16 of K for both operands; a 4-slot LDS ring is filled by
+// buffer_load_dwordx4 ... lds (no registers, no LDS stores by the
+// wavefronts), three stages ahead of the one being multiplied, with one
+// barrier per stage.  LDS layouts:
+//   OP_MN operand  [k][256 + 4] (one load instruction per k row, the 4-float
+//                  pad keeps the two half-wave rows of a fragment read apart);
+//   OP_K A         [m][16], the four 16-byte chunks of row m stored at
+//                  position chunk ^ ((m >> 1) & 3) (the lane that loads a
+//                  position fetches the chunk that belongs there), so that
+//                  the 16-byte reads of 8 consecutive rows cover all banks.
+// Contraction order: at substep s (0..7) of a stage, lane half h takes
+// k = 8 h + s for both operands (any bijection is a valid order; this one
+// lets an OP_K lane read its 8 values of a stage with two 16-byte reads).
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDK = 16;                    // K per stage
+constexpr int kDNS = 4;                    // ring slots
+constexpr int kDRow = 256 + 4;             // OP_MN row (floats)
+constexpr int kDSlot = kDK * kDRow;        // floats per operand and slot (>= 256 x 16 for OP_K)
+
+// buffer resource over `bytes` bytes at `base` (reads past them return 0)
+__device__ inline i32x4_t buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{static_cast<int>(a & 0xffffffffu), static_cast<int>((a >> 32) & 0xffffu), static_cast<int>(bytes),
+                 0x00020000};
+}
+
+// 16 bytes per lane from byte offset `voff` of `rsrc` to LDS at lds + 16 lane
+__device__ inline void dma16(const void* lds, uint32_t voff, i32x4_t rsrc) {
+  const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// 4 bytes per lane from byte offset `voff` of `rsrc` to LDS at lds + 4 lane
+__device__ inline void dma4(const void* lds, uint32_t voff, i32x4_t rsrc) {
+  const uint32_t l = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64; its
+// bits 3:0 and 5:4 sit at 3:0 and 15:14 of the immediate)
+#define KFAC_GEMM_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+
+// B16: B rows start 16-byte aligned (ldb % 4 == 0) and load 16 bytes per
+// lane; otherwise 4 bytes per lane, four instructions per row
+template <int AMODE, int EPI, bool B16>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_f32_dma_kernel(GemmBatch batch) {
+  using C = Cfg<true, kTileKDeep>;
+  __shared__ __attribute__((aligned(16))) float ring[kDNS][2][kDSlot];
+  const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
+  int split, ti, tj;
+  tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
+  const int i0 = ti * 256, j0 = tj * 256;
+  const int kmain = P.a_special >= 0 ? P.a_special : P.ke;   // multiple of kDK
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int wm = (wid / C::kWavesN) * C::kWM, wn = (wid % C::kWavesN) * C::kWN;
+  const bool live = i0 + wm < P.M && j0 + wn < P.N;
+
+  // A spans K rows of lda floats (OP_MN) or M rows (OP_K); B K rows of ldb
+  const uint32_t a_bytes = static_cast<uint32_t>(
+      static_cast<uint64_t>(AMODE == OP_MN ? P.ke : P.M) * P.lda * 4);
+  const uint32_t b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(P.ke) * P.ldb * 4);
+  const i32x4_t ra = buf_rsrc(P.A, a_bytes), rb = buf_rsrc(P.B, b_bytes);
+  // this wavefront's two load instructions per operand and stage (q = 2 wid + u)
+  uint32_t a_off[2], b_off[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = 2 * wid + u;
+    if (AMODE == OP_MN) {
+      a_off[u] = static_cast<uint32_t>((static_cast<int64_t>(q) * P.lda + i0 + 4 * lane) * 4);
+    } else {
+      const int m = 16 * q + (lane >> 2);
+      const int c = (lane & 3) ^ ((m >> 1) & 3);
+      a_off[u] = static_cast<uint32_t>((static_cast<int64_t>(i0 + m) * P.lda + 4 * c) * 4);
+    }
+    b_off[u] = static_cast<uint32_t>((static_cast<int64_t>(q) * P.ldb + j0 + (B16 ? 4 : 1) * lane) * 4);
+  }
+  const uint32_t a_step = AMODE == OP_MN ? static_cast<uint32_t>(kDK * P.lda * 4) : kDK * 4;
+  const uint32_t b_step = static_cast<uint32_t>(kDK * P.ldb * 4);
+  const int nst = kmain / kDK;
+  auto issue = [&](int s, int slot) {
+    if (s >= nst) return;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = 2 * wid + u;
+      dma16(&ring[slot][0][AMODE == OP_MN ? q * kDRow : q * 256], a_off[u] + static_cast<uint32_t>(s) * a_step, ra);
+      if (B16) {
+        dma16(&ring[slot][1][q * kDRow], b_off[u] + static_cast<uint32_t>(s) * b_step, rb);
+      } else {
+#pragma unroll
+        for (int part = 0; part < 4; ++part)
+          dma4(&ring[slot][1][q * kDRow + 64 * part], b_off[u] + static_cast<uint32_t>(s) * b_step + 256 * part, rb);
+      }
+    }
+  };
+  constexpr int kLoads = B16 ? 4 : 10;   // load instructions per lane and stage
+
+  f32x16 acc[C::kBI][C::kBJ];
+#pragma unroll
+  for (int a = 0; a < C::kBI; ++a)
+#pragma unroll
+    for (int b = 0; b < C::kBJ; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int s = 0; s < kDNS - 1; ++s) issue(s, s);
+  int slot = 0;
+  for (int s = 0; s < nst; ++s) {
+    // this lane's loads of stage s have landed once at most those of the
+    // later stages already issued (kLoads per stage) remain
+    const int later = min(nst - 1 - s, kDNS - 2);
+    if (later >= 2) KFAC_GEMM_WAIT_VM(2 * kLoads);
+    else if (later == 1) KFAC_GEMM_WAIT_VM(kLoads);
+    else KFAC_GEMM_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    issue(s + kDNS - 1, slot == 0 ? kDNS - 1 : slot - 1);
+    if (live) {
+      const float* sa = ring[slot][0];
+      const float* sb = ring[slot][1];
+      float af[8][C::kBI];
+      if (AMODE == OP_K) {
+        // rows wm + 32 i + l32: chunks 2 h and 2 h + 1 hold k = 8 h .. 8 h + 7
+#pragma unroll
+        for (int i = 0; i < C::kBI; ++i) {
+          const int m = wm + 32 * i + l32;
+          const int sw = (m >> 1) & 3;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kDK + 4 * ((2 * h + cc) ^ sw));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) af[4 * cc + e][i] = v[e];
+          }
+        }
+      }
+      float bfr[2][C::kBJ], afr[2][C::kBI];
+      auto frag = [&](int st, float (&fa)[C::kBI], float (&fb)[C::kBJ]) {
+        const int kr = 8 * h + st;
+#pragma unroll
+        for (int j = 0; j < C::kBJ; ++j) fb[j] = sb[kr * kDRow + wn + 32 * j + l32];
+        if (AMODE == OP_MN) {
+#pragma unroll
+          for (int i = 0; i < C::kBI; ++i) fa[i] = sa[kr * kDRow + wm + 32 * i + l32];
+        }
+      };
+      frag(0, afr[0], bfr[0]);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int cur = st & 1;
+        if (st < 7) frag(st + 1, afr[cur ^ 1], bfr[cur ^ 1]);
+#pragma unroll
+        for (int i = 0; i < C::kBI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::kBJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(AMODE == OP_K ? af[st][i] : afr[cur][i], bfr[cur][j],
+                                                            acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AMODE == OP_K ? C::kBJ : C::kBI + C::kBJ, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kBI * C::kBJ, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this stage's reads are done before the next barrier
+    slot = slot == kDNS - 1 ? 0 : slot + 1;
+  }
+
+  const float* r1a = nullptr;
+  const float* r1b = nullptr;
+  if (EPI == EPI_STORE && P.a_special >= 0) {
+    r1a = P.A_extra;
+    r1b = static_cast<const float*>(P.B) + static_cast<int64_t>(P.a_special) * P.ldb;
+  }
+  gemm_epilogue<EPI, C>(batch, P, P.C, acc, i0, j0, wm, wn, lane, r1a, r1b);
 }
 
 template <int AM, int BM, int EPI>
@@ -406,6 +607,36 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
   return KFAC_ERR_UNSUPPORTED;
 }
 
+kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int epi, bool b16, hipStream_t s) {
+  if (am == OP_K && epi == EPI_STORE && b16)
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_K, EPI_STORE, true>), dim3(blocks), dim3(512), 0, s, b);
+  else if (am == OP_K && epi == EPI_STORE)
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_K, EPI_STORE, false>), dim3(blocks), dim3(512), 0, s, b);
+  else if (am == OP_MN && epi == EPI_UPDATE && b16)
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_MN, EPI_UPDATE, true>), dim3(blocks), dim3(512), 0, s, b);
+  else if (am == OP_MN && epi == EPI_UPDATE)
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_MN, EPI_UPDATE, false>), dim3(blocks), dim3(512), 0, s, b);
+  else
+    return KFAC_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+}
+
+// the direct-to-LDS kernel takes a problem when its layouts and epilogue have
+// an instantiation and the problem is one whole-K product it can load
+bool dma_eligible(const GemmProb& p, int amode, int bmode, int epi) {
+  if (bmode != OP_MN || !((amode == OP_K && epi == EPI_STORE) || (amode == OP_MN && epi == EPI_UPDATE))) return false;
+  if (p.nsplit > 1 || p.nbatch > 1 || p.tri != TRI_FULL || p.krange != KR_ALL || p.kb != 0 || p.b_special >= 0)
+    return false;
+  if (p.a_special >= 0 && !(amode == OP_K && p.a_special == p.ke - 1 && p.A_extra != nullptr)) return false;
+  const int kmain = p.a_special >= 0 ? p.a_special : p.ke;
+  if (kmain < kDK || kmain % kDK != 0) return false;
+  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.lda % 4 != 0 || !al16(p.A) || (reinterpret_cast<uintptr_t>(p.B) & 3) != 0) return false;
+  const uint64_t a_bytes = static_cast<uint64_t>(amode == OP_MN ? p.ke : p.M) * p.lda * 4;
+  const uint64_t b_bytes = static_cast<uint64_t>(p.ke) * p.ldb * 4;
+  return a_bytes < (uint64_t(1) << 32) && b_bytes < (uint64_t(1) << 32);
+}
+
 int tiles_for(const GemmProb& p, int bt) {
   const int tm = (p.M + bt - 1) / bt, tn = (p.N + bt - 1) / bt;
   const int per = p.tri == TRI_FULL ? tm * tn : tm * (tm + 1) / 2;
@@ -430,7 +661,7 @@ int64_t block_k(const GemmProb& p) {
 }
 
 kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
-                          hipStream_t stream, bool big) {
+                          hipStream_t stream, bool big, bool dma = false, bool b16 = false) {
   const int bt = big ? 2 * kTile : kTile;
   std::vector<GemmProb> ps;
   for (GemmProb p : probs) {
@@ -464,7 +695,8 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
   }
   for (size_t l = 0; l < nl; ++l) {
     batches[l].sc = sc;
-    kfac_status_t st = dispatch(batches[l], blocks[l], big, amode, bmode, epi, stream);
+    kfac_status_t st = dma ? dispatch_dma(batches[l], blocks[l], amode, epi, b16, stream)
+                           : dispatch(batches[l], blocks[l], big, amode, bmode, epi, stream);
     if (st != KFAC_OK) return st;
   }
   return KFAC_OK;
@@ -488,10 +720,20 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
     if (st != KFAC_OK) return st;
     return small.empty() ? KFAC_OK : launch_with(small, amode, bmode, epi, sc, stream, false);
   }
-  // 256 x 256 tiles when the launch still has at least two tiles per CU
+  // 256 x 256 tiles when the launch still has at least two tiles per CU;
+  // then the problems the direct-to-LDS kernel can load go to it
   int big_tiles = 0;
   for (const GemmProb& p : probs) big_tiles += tiles_for(p, 2 * kTile);
-  return launch_with(probs, amode, bmode, epi, sc, stream, big_tiles >= 512);
+  if (big_tiles < 512) return launch_with(probs, amode, bmode, epi, sc, stream, false);
+  std::vector<GemmProb> dma16, dma4, rest;
+  for (const GemmProb& p : probs) {
+    const bool b16 = p.ldb % 4 == 0 && (reinterpret_cast<uintptr_t>(p.B) & 15) == 0;
+    (dma_eligible(p, amode, bmode, epi) ? (b16 ? dma16 : dma4) : rest).push_back(p);
+  }
+  kfac_status_t st = dma16.empty() ? KFAC_OK : launch_with(dma16, amode, bmode, epi, sc, stream, true, true, true);
+  if (st == KFAC_OK && !dma4.empty()) st = launch_with(dma4, amode, bmode, epi, sc, stream, true, true, false);
+  if (st != KFAC_OK) return st;
+  return rest.empty() ? KFAC_OK : launch_with(rest, amode, bmode, epi, sc, stream, true);
 }
 
 }  // namespace kfac

@@ -310,6 +310,21 @@ def test_big_tile_gemms_lockstep(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
+def test_big_tile_ragged_lockstep(gpu_lib):
+    """Preconditioning launches of 576 256 x 256 tiles with ragged edges: 16
+    layers 1040 -> 1008 with a bias (the bias column is not split off: the
+    first product has 1041 columns and a contraction of 1040 + the bias index,
+    over rows of the inverse that are not 16-byte aligned; the second product's
+    rows 1008 end inside a tile) and 16 layers 1024 -> 1008 without one (rows
+    of the inverse 16-byte aligned), three steps against the oracle."""
+    L = []
+    for i in range(16):
+        L.append(synth.linear(f"odd{i}", 1040, 1008, 48, bias=True))
+        L.append(synth.linear(f"even{i}", 1024, 1008, 48, bias=False))
+    cfg = with_layers(synth.full_config("fc64"), L, steps=3, act_std=1.0, grad_std=1e-2, refresh_every=2)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
 def test_full_nonfinite_flag(gpu_lib):
     """A NaN in the weight gradient of a layer whose update runs in the GEMM
     epilogue, and separately in the bias gradient of a layer whose bias
