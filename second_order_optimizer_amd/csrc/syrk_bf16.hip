@@ -28,7 +28,7 @@ constexpr int kBK = 64;         // rows of X per stage
 constexpr int kLR = kBK + 8;    // LDS column length in bf16 (144 bytes)
 constexpr int kMaxProbs = 56;
 constexpr int kXcdRun = 16;           // tiles per XCD run (xcd_tile)
-constexpr int kXcdRunMaxTiles = 16;   // only for launches whose factor grids are at most this wide
+constexpr int kBand = 4;              // tile rows per band (band_tile)
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -49,23 +49,53 @@ struct Batch {
   Prob p[kMaxProbs];
   int32_t n;
   int32_t xcd_run;   // > 1: runs of this many consecutive tiles per XCD (see xcd_tile)
+  int32_t band;      // > 0: tiles ordered in bands of this many tile rows (see band_tile)
 };
 static_assert(sizeof(Batch) <= 4096, "kernel arguments");
 
 // Workgroups go to the 8 XCDs round-robin (workgroup w on XCD w % 8), so
-// consecutive tiles, which share their row panel of X, would each load it into
-// a different XCD's L2.  With runs of R, XCD x takes logical tiles
-// [x R, x R + R) of every group of 8 R (the groups advance together, keeping
-// the launch's longest-first order); a final partial group keeps the
-// identity.  Measured on the 24-block transformer stack (factor grids of at
-// most 16 tiles): factor phase 6.8 -> 6.1 ms with R = 16; with 64-tile grids
-// (the 16k pair) every run length was slightly slower, so those launches keep
-// the identity.
+// consecutive tiles would each load their panels of X into a different XCD's
+// L2.  With runs of R, XCD x takes logical tiles [x R, x R + R) of every
+// group of 8 R (the groups advance together, keeping the launch's order); a
+// final partial group keeps the identity.  Together with the band order
+// below (bands of 4 tile rows), the R = 16 tiles an XCD runs together form a
+// 4 x 4 block of a factor's tile grid: 4 row panels and 4 column panels of X
+// instead of 1 and 16.  Measured factor phases (random inputs): transformer
+// stack 7.32 -> 7.24 ms, 16k pair 9.15 -> 8.87 ms.
 __device__ inline int xcd_tile(int w, int n, int R) {
   if (R <= 1) return w;
   const int base = n / (8 * R) * (8 * R);
   if (w >= base) return w;
   return (w / 8 / R) * (8 * R) + (w % 8) * R + (w / 8) % R;
+}
+
+// Upper tile t of a T x T tile grid in band order: bands of H tile rows;
+// inside a band, column after column, the band's rows of each column.  A
+// run of consecutive tiles then spans a few row panels and a few column
+// panels of X (a 2-D block of the grid) instead of one row panel and many
+// column panels.
+__device__ inline void band_tile(int t, int T, int H, int& ti, int& tj) {
+  int r0 = 0;
+  for (;;) {
+    const int h = min(H, T - r0);
+    const int tri = h * (h + 1) / 2;
+    const int n = tri + (T - r0 - h) * h;
+    if (t < n) {
+      if (t < tri) {
+        int u = 0;
+        while ((u + 1) * (u + 2) / 2 <= t) ++u;
+        tj = r0 + u;
+        ti = r0 + t - u * (u + 1) / 2;
+      } else {
+        const int q = t - tri;
+        tj = r0 + h + q / h;
+        ti = r0 + q % h;
+      }
+      return;
+    }
+    t -= n;
+    r0 += h;
+  }
 }
 
 __device__ inline int find_prob(const Batch& b, int blk) {
@@ -303,9 +333,13 @@ syrk_bf16_dma_kernel(Batch batch) {
   const int blk = xcd_tile(blockIdx.x, gridDim.x, batch.xcd_run);
   const Prob& P = batch.p[find_prob(batch, blk)];
   int t = blk - P.blk_begin;
-  int ti = 0;
-  while (t >= P.tiles - ti) { t -= P.tiles - ti; ++ti; }
-  const int tj = ti + t;
+  int ti = 0, tj;
+  if (batch.band > 0) {
+    band_tile(t, P.tiles, batch.band, ti, tj);
+  } else {
+    while (t >= P.tiles - ti) { t -= P.tiles - ti; ++ti; }
+    tj = ti + t;
+  }
   const bool diag = ti == tj;
   const int i0 = ti * kBT, j0 = tj * kBT;
   const int tid = threadIdx.x;
@@ -598,9 +632,8 @@ kfac_status_t launch_syrk_bf16(const std::vector<SyrkBf16Prob>& probs, hipStream
           b.p[b.n++] = p;
         }
         if (b.n == 0) continue;
-        int max_tiles = 0;
-        for (int j = 0; j < b.n; ++j) max_tiles = std::max(max_tiles, b.p[j].tiles);
-        b.xcd_run = max_tiles <= kXcdRunMaxTiles ? kXcdRun : 1;
+        b.xcd_run = kXcdRun;
+        b.band = kBand;
         if (use_dma && b.p[0].packed) hipLaunchKernelGGL(syrk_bf16_dma_kernel<true>, dim3(blocks), dim3(512), 0, st, b);
         else if (use_dma) hipLaunchKernelGGL(syrk_bf16_dma_kernel<false>, dim3(blocks), dim3(512), 0, st, b);
         else hipLaunchKernelGGL(syrk_bf16_kernel, dim3(blocks), dim3(512), 0, st, b);
