@@ -391,17 +391,22 @@ gemm_f32_syrk_kernel(GemmBatch batch) {
 }
 
 // ---------------------------------------------------------------------------
-// The 256 x 256 kernel with direct-to-LDS operand loads, for whole-K problems
-// (the preconditioning products): K a multiple of 16 (a bias column of an
-// OP_K A, the last index of the contraction, is added in the epilogue as a
-// rank-one term), B in OP_MN layout, 16-byte aligned rows.  Each stage holds
+// The 256 x 256 kernel with direct-to-LDS operand loads.  Each stage holds
 // 16 of K for both operands; a 4-slot LDS ring is filled by
 // buffer_load_dwordx4 ... lds (no registers, no LDS stores by the
 // wavefronts), three stages ahead of the one being multiplied, with one
-// barrier per stage.  LDS layouts:
+// barrier per stage.  It takes the problems whose contraction range of every
+// tile is whole stages (K bounds multiples of 16; the bias column of an OP_K
+// A, the last index of a whole-K contraction, is added in the epilogue as a
+// rank-one term) and whose rows start 16-byte aligned (an OP_MN B may instead
+// load 4 bytes per lane, four instructions per row).  Each operand is read
+// through a buffer resource that ends at its last element, so the loads of
+// tile rows or columns past M or N stay inside the operand's rows (their
+// products land in outputs the epilogue drops) and loads past the end read 0.
+// LDS layouts:
 //   OP_MN operand  [k][256 + 4] (one load instruction per k row, the 4-float
 //                  pad keeps the two half-wave rows of a fragment read apart);
-//   OP_K A         [m][16], the four 16-byte chunks of row m stored at
+//   OP_K operand   [m][16], the four 16-byte chunks of row m stored at
 //                  position chunk ^ ((m >> 1) & 3) (the lane that loads a
 //                  position fetches the chunk that belongs there), so that
 //                  the 16-byte reads of 8 consecutive rows cover all banks.
@@ -416,11 +421,14 @@ constexpr int kDNS = 4;                    // ring slots
 constexpr int kDRow = 256 + 4;             // OP_MN row (floats)
 constexpr int kDSlot = kDK * kDRow;        // floats per operand and slot (>= 256 x 16 for OP_K)
 
-// buffer resource over `bytes` bytes at `base` (reads past them return 0)
+// buffer resource over `bytes` bytes at `base` (reads past them return 0);
+// the values are workgroup-uniform, read from the first lane so that the
+// resource sits in scalar registers
 __device__ inline i32x4_t buf_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4_t{static_cast<int>(a & 0xffffffffu), static_cast<int>((a >> 32) & 0xffffu), static_cast<int>(bytes),
-                 0x00020000};
+  return i32x4_t{__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu)),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
 }
 
 // 16 bytes per lane from byte offset `voff` of `rsrc` to LDS at lds + 16 lane
@@ -446,9 +454,15 @@ __device__ inline void dma4(const void* lds, uint32_t voff, i32x4_t rsrc) {
 #define KFAC_GEMM_WAIT_VM(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
 
-// B16: B rows start 16-byte aligned (ldb % 4 == 0) and load 16 bytes per
-// lane; otherwise 4 bytes per lane, four instructions per row
-template <int AMODE, int EPI, bool B16>
+// Bytes from an operand's first element to the end of its last one: `rows`
+// rows of `ld` floats of which the last is read up to column `cols`.
+__host__ __device__ inline uint64_t operand_extent(int64_t rows, int64_t ld, int64_t cols) {
+  return rows <= 0 ? 0 : static_cast<uint64_t>(((rows - 1) * ld + cols) * 4);
+}
+
+// B16: the OP_MN B loads 16 bytes per lane (rows 16-byte aligned); otherwise
+// 4 bytes per lane, four instructions per row.
+template <int AMODE, int BMODE, int EPI, bool B16>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_f32_dma_kernel(GemmBatch batch) {
   using C = Cfg<true, kTileKDeep>;
@@ -457,41 +471,59 @@ gemm_f32_dma_kernel(GemmBatch batch) {
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
   const int i0 = ti * 256, j0 = tj * 256;
-  const int kmain = P.a_special >= 0 ? P.a_special : P.ke;   // multiple of kDK
+  // the contraction of the whole problem (the bias index of A excluded) and
+  // of this tile
+  const int kend = P.a_special >= 0 ? P.a_special : P.ke;
+  int kb = P.kb, ke = kend;
+  if (P.krange == KR_FROM_DIAG) kb = max(kb, max(i0, j0));
+  else if (P.krange == KR_FROM_ROW) kb = max(kb, i0);
+  else if (P.krange == KR_TO_ROW) ke = min(ke, i0 + 256);
+  const float* Ab = static_cast<const float*>(P.A);
+  const float* Bb = static_cast<const float*>(P.B);
+  float* Cp = P.C;
+  if (P.nbatch > 1) {
+    const int64_t off = static_cast<int64_t>(split) * P.split_stride;
+    Ab += off;
+    Bb += off;
+    Cp += off;
+  }
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int wm = (wid / C::kWavesN) * C::kWM, wn = (wid % C::kWavesN) * C::kWN;
-  const bool live = i0 + wm < P.M && j0 + wn < P.N;
+  const bool live = i0 + wm < P.M && j0 + wn < P.N && !(P.tri == TRI_UPPER && ti == tj && wm >= wn + C::kWN);
 
-  // A spans K rows of lda floats (OP_MN) or M rows (OP_K); B K rows of ldb
-  const uint32_t a_bytes = static_cast<uint32_t>(
-      static_cast<uint64_t>(AMODE == OP_MN ? P.ke : P.M) * P.lda * 4);
-  const uint32_t b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(P.ke) * P.ldb * 4);
-  const i32x4_t ra = buf_rsrc(P.A, a_bytes), rb = buf_rsrc(P.B, b_bytes);
-  // this wavefront's two load instructions per operand and stage (q = 2 wid + u)
+  const i32x4_t ra = buf_rsrc(Ab, static_cast<uint32_t>(AMODE == OP_MN ? operand_extent(kend, P.lda, P.M)
+                                                                       : operand_extent(P.M, P.lda, kend)));
+  const i32x4_t rb = buf_rsrc(Bb, static_cast<uint32_t>(BMODE == OP_MN ? operand_extent(kend, P.ldb, P.N)
+                                                                       : operand_extent(P.N, P.ldb, kend)));
+  // this wavefront's load instructions of a stage: q = 2 wid + u (0..15) of
+  // each operand; an OP_MN instruction is row q of the stage, an OP_K one
+  // rows 16 q .. 16 q + 15 of the tile
+  auto op_off = [&](int mode, int ld, int t0, int q, int vec) -> uint32_t {
+    if (mode == OP_MN)
+      return static_cast<uint32_t>((static_cast<int64_t>(kb + q) * ld + t0 + vec * lane) * 4);
+    const int m = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ ((m >> 1) & 3);
+    return static_cast<uint32_t>((static_cast<int64_t>(t0 + m) * ld + kb + 4 * c) * 4);
+  };
   uint32_t a_off[2], b_off[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int q = 2 * wid + u;
-    if (AMODE == OP_MN) {
-      a_off[u] = static_cast<uint32_t>((static_cast<int64_t>(q) * P.lda + i0 + 4 * lane) * 4);
-    } else {
-      const int m = 16 * q + (lane >> 2);
-      const int c = (lane & 3) ^ ((m >> 1) & 3);
-      a_off[u] = static_cast<uint32_t>((static_cast<int64_t>(i0 + m) * P.lda + 4 * c) * 4);
-    }
-    b_off[u] = static_cast<uint32_t>((static_cast<int64_t>(q) * P.ldb + j0 + (B16 ? 4 : 1) * lane) * 4);
+    a_off[u] = op_off(AMODE, P.lda, i0, 2 * wid + u, 4);
+    b_off[u] = op_off(BMODE, P.ldb, j0, 2 * wid + u, B16 ? 4 : 1);
   }
   const uint32_t a_step = AMODE == OP_MN ? static_cast<uint32_t>(kDK * P.lda * 4) : kDK * 4;
-  const uint32_t b_step = static_cast<uint32_t>(kDK * P.ldb * 4);
-  const int nst = kmain / kDK;
+  const uint32_t b_step = BMODE == OP_MN ? static_cast<uint32_t>(kDK * P.ldb * 4) : kDK * 4;
+  const int nst = ke > kb ? (ke - kb) / kDK : 0;
   auto issue = [&](int s, int slot) {
     if (s >= nst) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = 2 * wid + u;
       dma16(&ring[slot][0][AMODE == OP_MN ? q * kDRow : q * 256], a_off[u] + static_cast<uint32_t>(s) * a_step, ra);
-      if (B16) {
+      if (BMODE == OP_K) {
+        dma16(&ring[slot][1][q * 256], b_off[u] + static_cast<uint32_t>(s) * b_step, rb);
+      } else if (B16) {
         dma16(&ring[slot][1][q * kDRow], b_off[u] + static_cast<uint32_t>(s) * b_step, rb);
       } else {
 #pragma unroll
@@ -500,7 +532,7 @@ gemm_f32_dma_kernel(GemmBatch batch) {
       }
     }
   };
-  constexpr int kLoads = B16 ? 4 : 10;   // load instructions per lane and stage
+  constexpr int kLoads = (BMODE == OP_MN && !B16) ? 10 : 4;   // load instructions per lane and stage
 
   f32x16 acc[C::kBI][C::kBJ];
 #pragma unroll
@@ -526,31 +558,47 @@ gemm_f32_dma_kernel(GemmBatch batch) {
     if (live) {
       const float* sa = ring[slot][0];
       const float* sb = ring[slot][1];
-      float af[8][C::kBI];
+      // OP_K operands: rows wm + 32 i + l32 (wn + 32 j + l32); chunks 2 h and
+      // 2 h + 1 hold k = 8 h .. 8 h + 7
+      float ak[8][C::kBI], bk[8][C::kBJ];
       if (AMODE == OP_K) {
-        // rows wm + 32 i + l32: chunks 2 h and 2 h + 1 hold k = 8 h .. 8 h + 7
 #pragma unroll
         for (int i = 0; i < C::kBI; ++i) {
           const int m = wm + 32 * i + l32;
-          const int sw = (m >> 1) & 3;
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kDK + 4 * ((2 * h + cc) ^ sw));
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kDK + 4 * ((2 * h + cc) ^ ((m >> 1) & 3)));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) af[4 * cc + e][i] = v[e];
+            for (int e = 0; e < 4; ++e) ak[4 * cc + e][i] = v[e];
           }
         }
       }
+      if (BMODE == OP_K) {
+#pragma unroll
+        for (int j = 0; j < C::kBJ; ++j) {
+          const int n = wn + 32 * j + l32;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sb + n * kDK + 4 * ((2 * h + cc) ^ ((n >> 1) & 3)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bk[4 * cc + e][j] = v[e];
+          }
+        }
+      }
+      // OP_MN operands: one float per block and substep, read a substep ahead
       float bfr[2][C::kBJ], afr[2][C::kBI];
       auto frag = [&](int st, float (&fa)[C::kBI], float (&fb)[C::kBJ]) {
         const int kr = 8 * h + st;
+        if (BMODE == OP_MN) {
 #pragma unroll
-        for (int j = 0; j < C::kBJ; ++j) fb[j] = sb[kr * kDRow + wn + 32 * j + l32];
+          for (int j = 0; j < C::kBJ; ++j) fb[j] = sb[kr * kDRow + wn + 32 * j + l32];
+        }
         if (AMODE == OP_MN) {
 #pragma unroll
           for (int i = 0; i < C::kBI; ++i) fa[i] = sa[kr * kDRow + wm + 32 * i + l32];
         }
       };
+      constexpr int kReads = (AMODE == OP_MN ? C::kBI : 0) + (BMODE == OP_MN ? C::kBJ : 0);
       frag(0, afr[0], bfr[0]);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
@@ -560,9 +608,10 @@ gemm_f32_dma_kernel(GemmBatch batch) {
         for (int i = 0; i < C::kBI; ++i)
 #pragma unroll
           for (int j = 0; j < C::kBJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(AMODE == OP_K ? af[st][i] : afr[cur][i], bfr[cur][j],
-                                                            acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, AMODE == OP_K ? C::kBJ : C::kBI + C::kBJ, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(AMODE == OP_K ? ak[st][i] : afr[cur][i],
+                                                            BMODE == OP_K ? bk[st][j] : bfr[cur][j], acc[i][j], 0, 0,
+                                                            0);
+        if (kReads > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, C::kBI * C::kBJ, 0);
       }
     }
@@ -574,9 +623,9 @@ gemm_f32_dma_kernel(GemmBatch batch) {
   const float* r1b = nullptr;
   if (EPI == EPI_STORE && P.a_special >= 0) {
     r1a = P.A_extra;
-    r1b = static_cast<const float*>(P.B) + static_cast<int64_t>(P.a_special) * P.ldb;
+    r1b = Bb + static_cast<int64_t>(P.a_special) * P.ldb;
   }
-  gemm_epilogue<EPI, C>(batch, P, P.C, acc, i0, j0, wm, wn, lane, r1a, r1b);
+  gemm_epilogue<EPI, C>(batch, P, Cp, acc, i0, j0, wm, wn, lane, r1a, r1b);
 }
 
 template <int AM, int BM, int EPI>
@@ -606,6 +655,10 @@ kfac_status_t dispatch(const GemmBatch& b, int blocks, bool big, int am, int bm,
 #undef KFAC_GEMM_CASE
   return KFAC_ERR_UNSUPPORTED;
 }
+
+// ---------------------------------------------------------------------------
+// The factor SYRK (upper 128 x 128 tiles of X^T X, X = [rows, d] row-major,
+// no virtual bias column) with direct-to-LDS loads: 4 wavefronts of 64 x 64,
 
 // ---------------------------------------------------------------------------
 // The factor SYRK (upper 128 x 128 tiles of X^T X, X = [rows, d] row-major,
@@ -729,24 +782,28 @@ gemm_f32_dma_syrk_kernel(GemmBatch batch) {
   gemm_epilogue<EPI_SYRK, C>(batch, P, Cp, acc, i0, j0, wm, wn, lane, nullptr, nullptr);
 }
 
-kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int epi, bool b16, hipStream_t s) {
-  if (epi == EPI_SYRK)
+kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int bm, int epi, bool b16, hipStream_t s) {
+  if (epi == EPI_SYRK) {
     hipLaunchKernelGGL(gemm_f32_dma_syrk_kernel, dim3(blocks), dim3(256), 0, s, b);
-  else if (am == OP_K && epi == EPI_STORE && b16)
-    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_K, EPI_STORE, true>), dim3(blocks), dim3(512), 0, s, b);
-  else if (am == OP_K && epi == EPI_STORE)
-    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_K, EPI_STORE, false>), dim3(blocks), dim3(512), 0, s, b);
-  else if (am == OP_MN && epi == EPI_UPDATE && b16)
-    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_MN, EPI_UPDATE, true>), dim3(blocks), dim3(512), 0, s, b);
-  else if (am == OP_MN && epi == EPI_UPDATE)
-    hipLaunchKernelGGL((gemm_f32_dma_kernel<OP_MN, EPI_UPDATE, false>), dim3(blocks), dim3(512), 0, s, b);
-  else
-    return KFAC_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+  }
+#define KFAC_DMA_CASE(A_, B_, E_, W_)                                                        \
+  if (am == A_ && bm == B_ && epi == E_ && b16 == W_) {                                      \
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<A_, B_, E_, W_>), dim3(blocks), dim3(512), 0, s, b); \
+    return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;                         \
+  }
+  KFAC_DMA_CASE(OP_K, OP_MN, EPI_STORE, true)      // preconditioning, [grad_w | grad_b] A_inv
+  KFAC_DMA_CASE(OP_K, OP_MN, EPI_STORE, false)
+  KFAC_DMA_CASE(OP_MN, OP_MN, EPI_UPDATE, true)    // preconditioning, G_inv T + update
+  KFAC_DMA_CASE(OP_K, OP_K, EPI_SUB, true)         // Cholesky trailing updates
+  KFAC_DMA_CASE(OP_MN, OP_K, EPI_STORE, true)      // triangular inverse
+  KFAC_DMA_CASE(OP_K, OP_K, EPI_STORE, true)
+  KFAC_DMA_CASE(OP_MN, OP_MN, EPI_STORE, true)     // Z^T Z
+  KFAC_DMA_CASE(OP_MN, OP_MN, EPI_SUB, true)
+#undef KFAC_DMA_CASE
+  return KFAC_ERR_UNSUPPORTED;
 }
 
-// the direct-to-LDS kernel takes a problem when its layouts and epilogue have
-// an instantiation and the problem is one whole-K product it can load
 // the direct-to-LDS factor SYRK: no virtual bias column, 16-byte aligned rows
 bool dma_syrk_eligible(const GemmProb& p) {
   if (p.A != p.B || p.lda != p.ldb || p.a_special >= 0 || p.b_special >= 0 || p.nbatch > 1 || p.tri != TRI_UPPER ||
@@ -756,18 +813,36 @@ bool dma_syrk_eligible(const GemmProb& p) {
   return static_cast<uint64_t>(p.ke) * p.lda * 4 < (uint64_t(1) << 32);
 }
 
-bool dma_eligible(const GemmProb& p, int amode, int bmode, int epi) {
-  if (bmode != OP_MN || !((amode == OP_K && epi == EPI_STORE) || (amode == OP_MN && epi == EPI_UPDATE))) return false;
-  if (p.nsplit > 1 || p.nbatch > 1 || p.tri != TRI_FULL || p.krange != KR_ALL || p.kb != 0 || p.b_special >= 0)
+// Whether the 256 x 256 direct-to-LDS kernel takes problem `p` (see the
+// kernel's comment); b16 is set to the OP_MN B load width it needs.
+bool dma_eligible(const GemmProb& p, int am, int bm, int epi, bool& b16) {
+  const bool combo = (am == OP_K && bm == OP_MN && epi == EPI_STORE) ||
+                     (am == OP_MN && bm == OP_MN && (epi == EPI_UPDATE || epi == EPI_STORE || epi == EPI_SUB)) ||
+                     (am == OP_K && bm == OP_K && (epi == EPI_SUB || epi == EPI_STORE)) ||
+                     (am == OP_MN && bm == OP_K && epi == EPI_STORE);
+  if (!combo || p.nsplit > 1 || p.b_special >= 0) return false;
+  if (p.a_special >= 0 && !(am == OP_K && epi == EPI_STORE && p.krange == KR_ALL && p.a_special == p.ke - 1 &&
+                            p.A_extra != nullptr))
     return false;
-  if (p.a_special >= 0 && !(amode == OP_K && p.a_special == p.ke - 1 && p.A_extra != nullptr)) return false;
-  const int kmain = p.a_special >= 0 ? p.a_special : p.ke;
-  if (kmain < kDK || kmain % kDK != 0) return false;
-  const auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-  if (p.lda % 4 != 0 || !al16(p.A) || (reinterpret_cast<uintptr_t>(p.B) & 3) != 0) return false;
-  const uint64_t a_bytes = static_cast<uint64_t>(amode == OP_MN ? p.ke : p.M) * p.lda * 4;
-  const uint64_t b_bytes = static_cast<uint64_t>(p.ke) * p.ldb * 4;
-  return a_bytes < (uint64_t(1) << 32) && b_bytes < (uint64_t(1) << 32);
+  const int kend = p.a_special >= 0 ? p.a_special : p.ke;
+  if (p.kb < 0 || p.kb % kDK != 0 || kend % kDK != 0 || kend <= p.kb) return false;
+  if (p.nbatch > 1 && p.split_stride % 4 != 0) return false;
+  const auto al = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; };
+  // 16-byte loads: aligned rows, and an operand's last element ends a 16-byte chunk
+  if (p.lda % 4 != 0 || !al(p.A, 16) || (am == OP_MN && p.M % 4 != 0)) return false;
+  if (bm == OP_K) {
+    if (p.ldb % 4 != 0 || !al(p.B, 16)) return false;
+    b16 = true;
+  } else if (p.ldb % 4 == 0 && al(p.B, 16) && p.N % 4 == 0) {
+    b16 = true;
+  } else if (am == OP_K && epi == EPI_STORE && al(p.B, 4)) {
+    b16 = false;
+  } else {
+    return false;
+  }
+  const uint64_t ea = am == OP_MN ? operand_extent(kend, p.lda, p.M) : operand_extent(p.M, p.lda, kend);
+  const uint64_t eb = bm == OP_MN ? operand_extent(kend, p.ldb, p.N) : operand_extent(p.N, p.ldb, kend);
+  return ea < (uint64_t(1) << 32) && eb < (uint64_t(1) << 32);
 }
 
 int tiles_for(const GemmProb& p, int bt) {
@@ -828,7 +903,7 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
   }
   for (size_t l = 0; l < nl; ++l) {
     batches[l].sc = sc;
-    kfac_status_t st = dma ? dispatch_dma(batches[l], blocks[l], amode, epi, b16, stream)
+    kfac_status_t st = dma ? dispatch_dma(batches[l], blocks[l], amode, bmode, epi, b16, stream)
                            : dispatch(batches[l], blocks[l], big, amode, bmode, epi, stream);
     if (st != KFAC_OK) return st;
   }
@@ -867,8 +942,8 @@ kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, in
   if (big_tiles < 512) return launch_with(probs, amode, bmode, epi, sc, stream, false);
   std::vector<GemmProb> dma16, dma4, rest;
   for (const GemmProb& p : probs) {
-    const bool b16 = p.ldb % 4 == 0 && (reinterpret_cast<uintptr_t>(p.B) & 15) == 0;
-    (dma_eligible(p, amode, bmode, epi) ? (b16 ? dma16 : dma4) : rest).push_back(p);
+    bool b16 = true;
+    (dma_eligible(p, amode, bmode, epi, b16) ? (b16 ? dma16 : dma4) : rest).push_back(p);
   }
   kfac_status_t st = dma16.empty() ? KFAC_OK : launch_with(dma16, amode, bmode, epi, sc, stream, true, true, true);
   if (st == KFAC_OK && !dma4.empty()) st = launch_with(dma4, amode, bmode, epi, sc, stream, true, true, false);
