@@ -407,9 +407,12 @@ gemm_f32_syrk_kernel(GemmBatch batch) {
 //   OP_MN operand  [k][256 + 4] (one load instruction per k row, the 4-float
 //                  pad keeps the two half-wave rows of a fragment read apart);
 //   OP_K operand   [m][16], the four 16-byte chunks of row m stored at
-//                  position chunk ^ ((m >> 1) & 3) (the lane that loads a
-//                  position fetches the chunk that belongs there), so that
-//                  the 16-byte reads of 8 consecutive rows cover all banks.
+//                  position chunk ^ kswz(m) (the lane that loads a position
+//                  fetches the chunk that belongs there), so that the 16-byte
+//                  reads of 8 consecutive rows, and of the 4 rows of 16
+//                  consecutive ones that share a 64-byte quarter of a
+//                  256-byte line, fall on distinct banks (with (m >> 1) & 3
+//                  alone the second group collided: SQ_LDS_BANK_CONFLICT).
 // Contraction order: at substep s (0..7) of a stage, lane half h takes
 // k = 8 h + s for both operands (any bijection is a valid order; this one
 // lets an OP_K lane read its 8 values of a stage with two 16-byte reads).
@@ -420,6 +423,9 @@ constexpr int kDK = 16;                    // K per stage
 constexpr int kDNS = 4;                    // ring slots
 constexpr int kDRow = 256 + 4;             // OP_MN row (floats)
 constexpr int kDSlot = kDK * kDRow;        // floats per operand and slot (>= 256 x 16 for OP_K)
+
+// chunk swizzle of row m of an OP_K stage (see above)
+__device__ inline int kswz(int m) { return ((m >> 1) ^ (m >> 2)) & 3; }
 
 // buffer resource over `bytes` bytes at `base` (reads past them return 0);
 // the values are workgroup-uniform, read from the first lane so that the
@@ -503,7 +509,7 @@ gemm_f32_dma_kernel(GemmBatch batch) {
     if (mode == OP_MN)
       return static_cast<uint32_t>((static_cast<int64_t>(kb + q) * ld + t0 + vec * lane) * 4);
     const int m = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ ((m >> 1) & 3);
+    const int c = (lane & 3) ^ kswz(m);
     return static_cast<uint32_t>((static_cast<int64_t>(t0 + m) * ld + kb + 4 * c) * 4);
   };
   uint32_t a_off[2], b_off[2];
@@ -567,7 +573,7 @@ gemm_f32_dma_kernel(GemmBatch batch) {
           const int m = wm + 32 * i + l32;
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kDK + 4 * ((2 * h + cc) ^ ((m >> 1) & 3)));
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kDK + 4 * ((2 * h + cc) ^ kswz(m)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) ak[4 * cc + e][i] = v[e];
           }
@@ -579,7 +585,7 @@ gemm_f32_dma_kernel(GemmBatch batch) {
           const int n = wn + 32 * j + l32;
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sb + n * kDK + 4 * ((2 * h + cc) ^ ((n >> 1) & 3)));
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sb + n * kDK + 4 * ((2 * h + cc) ^ kswz(n)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) bk[4 * cc + e][j] = v[e];
           }
@@ -804,8 +810,12 @@ kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int bm, int e
   return KFAC_ERR_UNSUPPORTED;
 }
 
-// the direct-to-LDS factor SYRK: no virtual bias column, 16-byte aligned rows
+// the direct-to-LDS factor SYRK: no virtual bias column, 16-byte aligned rows,
+// enough rows to fill its ring (a short problem stays in the launch of the
+// others: one launch instead of two)
+constexpr int kDmaSyrkMinRows = 512;
 bool dma_syrk_eligible(const GemmProb& p) {
+  if (p.ke - p.kb < kDmaSyrkMinRows) return false;
   if (p.A != p.B || p.lda != p.ldb || p.a_special >= 0 || p.b_special >= 0 || p.nbatch > 1 || p.tri != TRI_UPPER ||
       p.krange != KR_ALL || p.kb != 0 || p.M != p.N)
     return false;
