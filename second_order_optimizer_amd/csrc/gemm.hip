@@ -62,14 +62,25 @@ struct Cfg {
 // [m][k] rows for k-contiguous ones.
 __host__ __device__ constexpr bool k_major(int mode) { return mode == OP_K; }
 
-struct GemmBatch {
-  GemmProb p[kMaxGemmProbs];
+// A launch's problem table, passed as kernel arguments.  Launches of at most
+// kSmallCap problems (most launches of the Cholesky chain) take the small
+// table: HIP copies the whole argument block per launch into a kernel
+// argument pool of bounded size, and a refresh step of the 16k pair, with
+// about a thousand launches of 4 KB tables, exhausted it, so that the host
+// waited for the GPU to drain it (34.7 ms to enqueue one step).
+template <int CAP>
+struct GemmBatchT {
+  GemmProb p[CAP];
   int32_t n;
   GemmScalars sc;
 };
+using GemmBatch = GemmBatchT<kMaxGemmProbs>;
+constexpr int kSmallCap = 4;
+using GemmBatchSmall = GemmBatchT<kSmallCap>;
 static_assert(sizeof(GemmBatch) <= 4096, "kernel arguments");
 
-__device__ inline int find_prob(const GemmBatch& b, int blk) {
+template <typename Batch>
+__device__ inline int find_prob(const Batch& b, int blk) {
   int lo = 0, hi = b.n - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -180,8 +191,8 @@ __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti
 // r1a / r1b (EPI_STORE only, may be null): a rank-one term r1a[row] r1b[col]
 // added to the product before scaling (the bias column of A taken out of the
 // contraction).
-template <int EPI, typename C>
-__device__ __forceinline__ void gemm_epilogue(const GemmBatch& batch, const GemmProb& P, float* Cp,
+template <int EPI, typename C, typename Batch>
+__device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb& P, float* Cp,
                                               f32x16 (&acc)[C::kBI][C::kBJ], int i0, int j0, int wm, int wn,
                                               int lane, const float* __restrict__ r1a,
                                               const float* __restrict__ r1b) {
@@ -260,8 +271,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmBatch& batch, const Gemm
   }
 }
 
-template <int AMODE, int BMODE, int EPI, bool BIG>
-__device__ __forceinline__ void gemm_f32_body(const GemmBatch& batch) {
+template <int AMODE, int BMODE, int EPI, bool BIG, typename Batch>
+__device__ __forceinline__ void gemm_f32_body(const Batch& batch) {
   constexpr int TK = EPI == EPI_SYRK ? kTileKSyrk : kTileKDeep;
   using C = Cfg<BIG, TK>;
   __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
@@ -376,8 +387,8 @@ __device__ __forceinline__ void gemm_f32_body(const GemmBatch& batch) {
   gemm_epilogue<EPI, C>(batch, P, Cp, acc, i0, j0, wm, wn, lane, nullptr, nullptr);
 }
 
-template <int AMODE, int BMODE, int EPI, bool BIG>
-__global__ void __launch_bounds__((Cfg<BIG, kTileKDeep>::kThreads)) gemm_f32_kernel(GemmBatch batch) {
+template <int AMODE, int BMODE, int EPI, bool BIG, int CAP>
+__global__ void __launch_bounds__((Cfg<BIG, kTileKDeep>::kThreads)) gemm_f32_kernel(GemmBatchT<CAP> batch) {
   gemm_f32_body<AMODE, BMODE, EPI, BIG>(batch);
 }
 
@@ -637,11 +648,17 @@ gemm_f32_dma_kernel(GemmBatch batch) {
 template <int AM, int BM, int EPI>
 kfac_status_t launch_group(const GemmBatch& b, int blocks, bool big, hipStream_t s) {
   if (big) {
-    hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, true>), dim3(blocks), dim3(512), 0, s, b);
+    hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, true, kMaxGemmProbs>), dim3(blocks), dim3(512), 0, s, b);
   } else if constexpr (AM == OP_MN && BM == OP_MN && EPI == EPI_SYRK) {
     hipLaunchKernelGGL(gemm_f32_syrk_kernel, dim3(blocks), dim3(256), 0, s, b);
+  } else if (b.n <= kSmallCap) {
+    GemmBatchSmall t{};
+    for (int i = 0; i < b.n; ++i) t.p[i] = b.p[i];
+    t.n = b.n;
+    t.sc = b.sc;
+    hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, false, kSmallCap>), dim3(blocks), dim3(256), 0, s, t);
   } else {
-    hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, false>), dim3(blocks), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gemm_f32_kernel<AM, BM, EPI, false, kMaxGemmProbs>), dim3(blocks), dim3(256), 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
 }
