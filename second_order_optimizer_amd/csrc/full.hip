@@ -226,18 +226,12 @@ struct DMat {
   int32_t d;
   int32_t pad_;
 };
-template <int CAP>
-struct DiagTabT {
-  DMat m[CAP];
+struct DiagTab {
+  DMat m[kMaxDiagMats];
   int32_t n;
   int32_t k;
   uint32_t* flags;
 };
-using DiagTab = DiagTabT<kMaxDiagMats>;
-// launches of the chain's later steps hold few matrices: a small table keeps
-// the kernel arguments of the many per-step launches small
-constexpr int kSmallDiag = 8;
-using DiagTabSmall = DiagTabT<kSmallDiag>;
 
 // L = F + damping I from F's upper triangle (both triangles of L written),
 // Z = 0, fail = 0.  grid = (32 x 32 tiles, matrix); a lower tile (I > J) is
@@ -383,8 +377,7 @@ __device__ inline void factor_diag32(float* Ms, float* Zs, int c0, const DMat& M
   }
 }
 
-template <int CAP>
-__global__ void __launch_bounds__(256) chol_diag_kernel(DiagTabT<CAP> T) {
+__global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   __shared__ __attribute__((aligned(16))) float Ms[kNb * kLd];
   __shared__ __attribute__((aligned(16))) float Zs[kNb * kLd];
   __shared__ __attribute__((aligned(16))) float Ss[4][32 * kSd];
@@ -978,16 +971,8 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     D.flags = flags;
     for (size_t mi = 0; mi <= mats.size(); ++mi) {
       if (mi == mats.size() || D.n == kMaxDiagMats) {
-        if (D.n > kSmallDiag) {
-          hipLaunchKernelGGL(chol_diag_kernel<kMaxDiagMats>, dim3(D.n), dim3(256), 0, ds, D);
-          KFAC_HIP_TRY(hipGetLastError());
-        } else if (D.n > 0) {
-          DiagTabSmall t{};
-          for (int i = 0; i < D.n; ++i) t.m[i] = D.m[i];
-          t.n = D.n;
-          t.k = D.k;
-          t.flags = D.flags;
-          hipLaunchKernelGGL(chol_diag_kernel<kSmallDiag>, dim3(t.n), dim3(256), 0, ds, t);
+        if (D.n > 0) {
+          hipLaunchKernelGGL(chol_diag_kernel, dim3(D.n), dim3(256), 0, ds, D);
           KFAC_HIP_TRY(hipGetLastError());
         }
         D.n = 0;
