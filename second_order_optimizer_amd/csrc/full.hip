@@ -606,6 +606,7 @@ struct FullPlan {
   std::vector<float*> xcol;      // per layer and factor: fp32 convolution tensor as [rows, width], or null
   std::vector<int> xcol_ld;      // their row pitch (floats)
   std::vector<Mat> mats;         // inverse work per factor (2 layer + which)
+  std::vector<float*> W;         // per factor: Z^T Z, assembled while the Cholesky runs (upper triangle)
   // runs of equal-size factors whose work areas sit at a constant stride
   struct Group {
     int first;                   // index into mats of the lowest address
@@ -675,10 +676,11 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
       P.xcol.push_back(col ? reinterpret_cast<float*>(carve(static_cast<size_t>(g.rows) * ld * 4)) : nullptr);
     }
   }
-  // Cholesky work areas: one contiguous chunk per factor (L, Z, Dinv, fail),
+  // Cholesky work areas: one contiguous chunk per factor (L, Z, W, Dinv, fail),
   // factors of equal size side by side, so that the chunks of one size lie
   // at a constant stride and every size is one batched GEMM problem
   P.mats.resize(2 * static_cast<size_t>(n));
+  P.W.resize(P.mats.size());
   std::vector<int> order(P.mats.size());
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
@@ -699,6 +701,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
     start[i] = off;
     m.L = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
     m.Z = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
+    P.W[order[i]] = reinterpret_cast<float*>(carve(static_cast<size_t>(d) * d * 4));
     m.Dinv = reinterpret_cast<float*>(carve(nblk_of(d) * kNb * kNb * 4));
     m.fail = reinterpret_cast<int32_t*>(carve(4));
   }
@@ -842,7 +845,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
 }
 
 // The library's side streams for one caller stream on one device: the
-// Cholesky chain (s) and the assembly of finished inverses (f), with their
+// Cholesky chain (s) and the inverse assembly beside it (f), with their
 // events, at default priority, created at the first full step on that caller
 // stream and kept for the process.  Keying them by the caller's stream keeps
 // a step captured into a graph from pulling another stream's work into the
@@ -854,7 +857,7 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
 struct SideStream {
   std::mutex mu;
   hipStream_t s = nullptr;   // Cholesky inner chain
-  hipStream_t f = nullptr;   // inverse assembly of factors whose Cholesky is complete
+  hipStream_t f = nullptr;   // inverse assembly, as far as the chain allows
   hipEvent_t fork = nullptr, join = nullptr, fjoin = nullptr, main_done[2] = {nullptr, nullptr},
              side_done[2] = {nullptr, nullptr}, ufork = nullptr, ujoin = nullptr;
 };
@@ -1045,141 +1048,189 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (static_cast<int>(nblk_of(mats[g.first].d)) > k + 1) v.push_back(batched(panel_of(mats[g.first], k), g));
     return v.empty() ? KFAC_OK : launch_gemm(v, OP_K, OP_K, EPI_STORE, sc, ss);
   };
-  // The triangular inverse, Z^T Z and the output of the factors in `gs`
-  // (complete Cholesky factors), on stream fs.
-  auto finish = [&](const std::vector<const FullPlan::Group*>& gs, hipStream_t fs) -> kfac_status_t {
-    std::vector<Mat> ms;
-    int dm = 0;
-    for (const FullPlan::Group* g : gs)
-      for (int mi : g->members) {
-        ms.push_back(mats[mi]);
-        dm = std::max(dm, mats[mi].d);
-      }
-    // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
-    // inverted diagonal blocks; at level s (128, 256, ...) each pair of
-    // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
-    // (r0, r0) with r0 = c0 + s, gives the block between them:
-    //   Z21 = -Z22 (L21 Z11)   (L21 = rows r0.., columns c0.. of L).
-    // T^T = Z11^T L21^T is staged in L's strict upper triangle at (c0, r0),
-    // which no later step reads (the Z^T Z pass overwrites L).  Z11 is lower
-    // triangular, so a tile of T^T needs rows k >= its first row of Z11; Z22
-    // is lower triangular, so a tile of Z21 needs k up to its last row.  The
-    // full-size pairs of one matrix and level form one strided problem (all
-    // three operands move by 2 s (d + 1) floats from pair to pair), the last,
-    // shorter pair another; every matrix advances one level per two launches.
-    for (int s = kNb; s < dm; s *= 2) {
+  // The inverse of each factor is assembled on stream fs as far as its
+  // Cholesky factor allows: after outer panel K, rows and columns below
+  // R = 512 (K + 1) of L are final (later steps touch only rows and columns
+  // from R on), so every part of Z = L^-1 and of Z^T Z that needs nothing
+  // beyond them can run beside the remaining steps.
+  //
+  // Z = L^-1 by recursive doubling.  The diagonal 128-blocks of Z are the
+  // inverted diagonal blocks; at level s (128, 256, ...) each pair of
+  // neighbouring inverted s-blocks of a matrix, Z11 at (c0, c0) and Z22 at
+  // (r0, r0) with r0 = c0 + s, gives the block between them:
+  //   Z21 = -Z22 (L21 Z11)   (L21 = rows r0.., columns c0.. of L).
+  // T^T = Z11^T L21^T is staged in L's strict upper triangle at (c0, r0),
+  // which no step of the Cholesky reads or writes.  Z11 is lower triangular,
+  // so a tile of T^T needs rows k >= its first row of Z11; Z22 is lower
+  // triangular, so a tile of Z21 needs k up to its last row.  A pair needs
+  // L up to its end min(r0 + s, d): the pairs of a level become ready in
+  // order, and the ready ones not yet done form one strided problem (all
+  // three operands move by 2 s (d + 1) floats from pair to pair; the last,
+  // shorter pair is a problem of its own).  Levels run in increasing s, so a
+  // pair's own lower levels are done first.
+  //
+  // inverse = Z^T Z into W.  Z is lower triangular, so element (i, j) sums
+  // over rows k >= max(i, j).  Rows below P = 128 * 2^m <= R of Z are
+  // complete once R is reached (every pair that writes into them ends by P),
+  // so, when the total Z^T Z work is small against d_max, W takes Z's rows
+  // kLauRows at a time as they complete (no workgroup then runs the whole
+  // height, and the passes run beside the Cholesky); otherwise it takes all
+  // rows in one pass once the factor is complete (a pass of few rows would
+  // read and write the whole triangle for little work).
+  // Finally sym_reduce_kernel writes W's upper triangle, mirrored, into the
+  // inverse unless the factorisation failed.
+  struct Progress {
+    std::vector<int> pairs;   // per level: pairs done
+    int rows = 0;             // rows of Z already in W
+  };
+  std::vector<Progress> prog(groups.size());
+  double lau_flops = 0.0;
+  int d_all = 0;
+  for (const FullPlan::Group& g : groups) {
+    const int d = mats[g.first].d;
+    lau_flops += static_cast<double>(g.count) * d * d * d / 3.0;
+    d_all = std::max(d_all, d);
+  }
+  const bool by_rows = lau_flops < 67108864.0 * d_all;
+  // end of the next Z^T Z pass of a factor of size d whose rows below `done`
+  // are in W, once L is final below R (done itself when there is none)
+  auto lau_next = [&](int done, int R, int d) -> int {
+    if (done >= d) return done;
+    if (R >= d) return by_rows ? std::min(d, done + kLauRows) : d;
+    if (!by_rows) return done;                   // one pass once the factor is complete
+    int P2 = 0;                                  // rows of Z complete: 128 * 2^m <= R
+    for (int q = kNb; q <= R; q *= 2) P2 = q;
+    return done + kLauRows <= P2 ? done + kLauRows : done;
+  };
+  auto assemble = [&](int R, hipStream_t fs) -> kfac_status_t {
+    // every level's newly ready pairs, matrix by matrix
+    for (int s = kNb, lv = 0; s < d_all; s *= 2, ++lv) {
       std::vector<GemmProb> g1, g2;
-      for (const Mat& m : ms) {
-        const int d = m.d;
-        if (d <= s) continue;
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const FullPlan::Group& g = groups[gi];
+        const int d = mats[g.first].d;
+        if (d <= s || R <= 0) continue;
+        Progress& pr = prog[gi];
+        if (static_cast<int>(pr.pairs.size()) <= lv) pr.pairs.resize(lv + 1, 0);
+        const int Rm = std::min(R, d);
         const int npairs = (d - s + 2 * s - 1) / (2 * s);       // pairs with r0 = 2 p s + s < d
+        int ready = 0;
+        while (ready < npairs && std::min((2 * ready + 2) * s, d) <= Rm) ++ready;
         const int nfull = (d - 2 * s) >= 0 ? (d - 2 * s) / (2 * s) + 1 : 0;   // pairs with r0 + s <= d
-        for (int part = 0; part < 2; ++part) {
-          const int p0 = part == 0 ? 0 : nfull;
-          const int cnt = part == 0 ? nfull : npairs - nfull;
-          if (cnt <= 0) continue;
-          const int c0 = 2 * p0 * s, r0 = c0 + s;
-          const int m2 = part == 0 ? s : d - r0;
-          GemmProb p{};
-          p.A = m.Z + static_cast<int64_t>(c0) * d + c0;        // Z11, read as A[i][k] = Z11[k][i]
-          p.lda = d;
-          p.B = m.L + static_cast<int64_t>(r0) * d + c0;        // L21, read as B[k][j] = L21[j][k]
-          p.ldb = d;
-          p.C = m.L + static_cast<int64_t>(c0) * d + r0;        // T^T (s x m2) in L's upper triangle
-          p.ldc = d;
-          p.M = s;
-          p.N = m2;
-          p.kb = 0;
-          p.ke = s;
-          p.tri = TRI_FULL;
-          p.krange = KR_FROM_ROW;
-          p.a_special = p.b_special = -1;
-          p.alpha = 1.f;
-          p.nsplit = 1;
-          p.nbatch = static_cast<int16_t>(cnt);
-          p.split_stride = static_cast<int64_t>(2 * s) * (d + 1);
-          gemm_set_tiles(p);
-          g1.push_back(p);
-          GemmProb q = p;
-          q.A = m.Z + static_cast<int64_t>(r0) * d + r0;        // Z22
-          q.B = m.L + static_cast<int64_t>(c0) * d + r0;        // T[k][j] = T^T[j][k]
-          q.C = m.Z + static_cast<int64_t>(r0) * d + c0;        // Z21
-          q.M = m2;
-          q.N = s;
-          q.ke = m2;
-          q.krange = KR_TO_ROW;
-          q.alpha = -1.f;
-          gemm_set_tiles(q);
-          g2.push_back(q);
+        const int p_lo = pr.pairs[lv];
+        if (ready <= p_lo) continue;
+        pr.pairs[lv] = ready;
+        for (int mi : g.members) {
+          const Mat& m = mats[mi];
+          for (int part = 0; part < 2; ++part) {
+            const int p0 = part == 0 ? p_lo : std::max(p_lo, nfull);
+            const int p1 = part == 0 ? std::min(ready, nfull) : ready;
+            const int cnt = p1 - p0;
+            if (cnt <= 0) continue;
+            const int c0 = 2 * p0 * s, r0 = c0 + s;
+            const int m2 = part == 0 ? s : d - r0;
+            GemmProb p{};
+            p.A = m.Z + static_cast<int64_t>(c0) * d + c0;        // Z11, read as A[i][k] = Z11[k][i]
+            p.lda = d;
+            p.B = m.L + static_cast<int64_t>(r0) * d + c0;        // L21, read as B[k][j] = L21[j][k]
+            p.ldb = d;
+            p.C = m.L + static_cast<int64_t>(c0) * d + r0;        // T^T (s x m2) in L's upper triangle
+            p.ldc = d;
+            p.M = s;
+            p.N = m2;
+            p.kb = 0;
+            p.ke = s;
+            p.tri = TRI_FULL;
+            p.krange = KR_FROM_ROW;
+            p.a_special = p.b_special = -1;
+            p.alpha = 1.f;
+            p.nsplit = 1;
+            p.nbatch = static_cast<int16_t>(cnt);
+            p.split_stride = static_cast<int64_t>(2 * s) * (d + 1);
+            gemm_set_tiles(p);
+            g1.push_back(p);
+            GemmProb q = p;
+            q.A = m.Z + static_cast<int64_t>(r0) * d + r0;        // Z22
+            q.B = m.L + static_cast<int64_t>(c0) * d + r0;        // T[k][j] = T^T[j][k]
+            q.C = m.Z + static_cast<int64_t>(r0) * d + c0;        // Z21
+            q.M = m2;
+            q.N = s;
+            q.ke = m2;
+            q.krange = KR_TO_ROW;
+            q.alpha = -1.f;
+            gemm_set_tiles(q);
+            g2.push_back(q);
+          }
         }
       }
-      if (g1.empty()) break;
+      if (g1.empty()) continue;
       kfac_status_t r = launch_gemm(g1, OP_MN, OP_K, EPI_STORE, sc, fs);
       if (r != KFAC_OK) return r;
       r = launch_gemm(g2, OP_K, OP_K, EPI_STORE, sc, fs);
       if (r != KFAC_OK) return r;
     }
-    // inverse = Z^T Z.  Z is lower triangular, so element (i, j) sums over
-    // rows k >= max(i, j); the product goes into L (free once Z is complete;
-    // upper tiles only) and the reduce writes it, mirrored, into the inverse of
-    // every matrix that factored.  The top-left tile of the largest factor sums
-    // all of its d_max rows; when that one workgroup would take a large share
-    // of the whole product (total d^3 / 3 below 2^26 d_max flops: few large
-    // factors), the rows are taken kLauRows at a time (the first pass stores,
-    // later passes add) so that no workgroup runs the whole height.
-    double lau_flops = 0.0;
-    for (const Mat& m : ms) lau_flops += static_cast<double>(m.d) * m.d * m.d / 3.0;
-    const bool by_rows = lau_flops < 67108864.0 * dm;
-    const int rows_per_pass = by_rows ? kLauRows : dm;
-    for (int k0 = 0; k0 < dm; k0 += rows_per_pass) {
-      std::vector<GemmProb> lau;
-      for (const FullPlan::Group* gp : gs) {
-        const FullPlan::Group& g = *gp;
+    // Z^T Z passes over the rows of Z that are complete (the first stores,
+    // later ones add); factors of different groups share the launches
+    for (;;) {
+      std::vector<GemmProb> first, later;
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const FullPlan::Group& g = groups[gi];
         const Mat& m = mats[g.first];
-        if (m.d <= k0) continue;
+        const int d = m.d;
+        Progress& pr = prog[gi];
+        const int k1 = lau_next(pr.rows, R, d);
+        if (k1 <= pr.rows) continue;
         GemmProb p{};
         p.A = m.Z;
         p.B = m.Z;
-        p.lda = p.ldb = m.d;
-        p.C = m.L;
-        p.ldc = m.d;
-        p.M = p.N = m.d;
-        p.kb = k0;
-        p.ke = std::min(m.d, k0 + rows_per_pass);
+        p.lda = p.ldb = d;
+        p.C = P.W[g.first];
+        p.ldc = d;
+        p.M = p.N = d;
+        p.kb = pr.rows;
+        p.ke = k1;
         p.tri = TRI_UPPER;
         p.krange = KR_FROM_DIAG;
         p.a_special = p.b_special = -1;
         p.nsplit = 1;
-        p.alpha = k0 == 0 ? 1.f : -1.f;
+        p.alpha = pr.rows == 0 ? 1.f : -1.f;
         gemm_set_tiles(p);
-        lau.push_back(batched(p, g));
+        (pr.rows == 0 ? first : later).push_back(batched(p, g));
+        pr.rows = k1;
       }
-      kfac_status_t r =
-          launch_gemm(lau, OP_MN, OP_MN, k0 == 0 ? EPI_STORE : EPI_SUB, sc, fs, by_rows ? TILES_SMALL : TILES_AUTO);
+      if (first.empty() && later.empty()) break;
+      const int policy = by_rows ? TILES_SMALL : TILES_AUTO;
+      kfac_status_t r = first.empty() ? KFAC_OK : launch_gemm(first, OP_MN, OP_MN, EPI_STORE, sc, fs, policy);
+      if (r == KFAC_OK && !later.empty()) r = launch_gemm(later, OP_MN, OP_MN, EPI_SUB, sc, fs, policy);
       if (r != KFAC_OK) return r;
     }
+    // output of the factors complete at R
     std::vector<SymRedItem> out;
-    for (const Mat& m : ms) {
-      SymRedItem it{};
-      it.part = m.L;
-      it.F = m.Finv;
-      it.fail = m.fail;
-      it.d = m.d;
-      it.nsplit = 1;
-      it.alpha = 1.f;
-      it.beta = 0.f;
-      out.push_back(it);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const FullPlan::Group& g = groups[gi];
+      const int d = mats[g.first].d;
+      const int K = (static_cast<int>(nblk_of(d)) - 1) / kOuter;   // outer panel of its last block
+      if (R < d || (R - 1) / (kOuter * kNb) != K) continue;        // complete before this call: done then
+      for (int mi : g.members) {
+        SymRedItem it{};
+        it.part = P.W[mi];
+        it.F = mats[mi].Finv;
+        it.fail = mats[mi].fail;
+        it.d = d;
+        it.nsplit = 1;
+        it.alpha = 1.f;
+        it.beta = 0.f;
+        out.push_back(it);
+      }
     }
-    return launch_sym_reduce(out, fs);
+    return out.empty() ? KFAC_OK : launch_sym_reduce(out, fs);
   };
   if (nblk_max == 1) {
     // every factor is one diagonal block: no chain to overlap, so the same
     // launches run in order on the caller's stream (no fork, no events)
     r = diag_step(0, st);
     if (r != KFAC_OK) return r;
-    std::vector<const FullPlan::Group*> all;
-    for (const FullPlan::Group& g : groups) all.push_back(&g);
-    return finish(all, st);
+    return assemble(d_all, st);
   }
   hipStream_t fs = side->f;
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
@@ -1246,14 +1297,14 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r != KFAC_OK) return r;
     }
     KFAC_HIP_TRY(hipEventRecord(side->main_done[K & 1], st));
-    // factors whose last block is in outer panel K are complete: their
-    // inverse is assembled on a third stream beside the remaining steps
-    std::vector<const FullPlan::Group*> done;
-    for (const FullPlan::Group& g : groups)
-      if ((static_cast<int>(nblk_of(mats[g.first].d)) - 1) / kOuter == K) done.push_back(&g);
-    if (!done.empty()) {
+    // rows and columns of L below 512 (K + 1) are final: the inverse
+    // assembly of every factor still in progress goes as far as they allow,
+    // on a third stream beside the remaining steps
+    bool active = false;
+    for (const FullPlan::Group& g : groups) active = active || static_cast<int>(nblk_of(mats[g.first].d)) > k0;
+    if (active) {
       KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->side_done[K & 1], 0));
-      r = finish(done, fs);
+      r = assemble(k1 * kNb, fs);
       if (r != KFAC_OK) return r;
     }
   }
