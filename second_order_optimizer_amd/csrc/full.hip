@@ -634,6 +634,20 @@ bool fp32_factor(const kfac_layer_t& L, int which) {
   return (which == 0 ? L.act_dtype : L.grad_dtype) == KFAC_F32;
 }
 
+// an fp32 convolution factor whose rows the SYRK reads from the tensor in
+// place: the output gradient, and the input of a 1 x 1, stride-1, unpadded
+// convolution without a bias column (in both, row n is pixel n % HW of image
+// n / HW, the tensor being [B][d][HW])
+bool nchw_factor(const kfac_layer_t& L, int which) {
+  const LayerGeom g = geom_of(L);
+  if (!g.conv || !fp32_factor(L, which)) return false;
+  if (which == 0) {
+    if (g.bias || g.kh != 1 || g.kw != 1 || g.stride != 1 || g.pad != 0) return false;
+    return gemm_nchw_syrk_ok(L.a, g.rows, g.h * g.w, g.d_in);
+  }
+  return gemm_nchw_syrk_ok(L.g, g.rows, g.h_out * g.w_out, g.d_out);
+}
+
 FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool refresh) {
   FullPlan P;
   size_t off = kFlagBytes;
@@ -669,7 +683,7 @@ FullPlan plan_full(const kfac_layer_t* layers, int n, char* ws, int phases, bool
   for (int li = 0; li < n; ++li) {
     const LayerGeom g = geom_of(layers[li]);
     for (int which = 0; which < 2; ++which) {
-      const bool col = g.conv && fp32_factor(layers[li], which);
+      const bool col = g.conv && fp32_factor(layers[li], which) && !nchw_factor(layers[li], which);
       const int w = which == 0 ? g.d_in : g.d_out;
       const int ld = (w + 3) / 4 * 4;
       P.xcol_ld.push_back(col ? ld : 0);
@@ -780,6 +794,9 @@ kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparam
       p.a_special = p.b_special = special;
       if (!g.conv) {
         p.lda = p.ldb = which == 0 ? g.d_in : g.d_out;
+      } else if (nchw_factor(L, which)) {
+        p.lda = p.ldb = which == 0 ? g.h * g.w : g.h_out * g.w_out;
+        p.nchw = 1;
       } else {
         // the convolution tensor as rows first (im2col of the input; the
         // output gradient transposed), then the same SYRK as a linear layer's

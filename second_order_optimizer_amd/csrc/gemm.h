@@ -61,7 +61,8 @@ struct GemmProb {
   uint8_t krange;         // GemmKRange
   uint8_t a_vec, b_vec;   // set by the launcher: 16-byte loads allowed (ld % 4 == 0, aligned base)
   uint8_t c_packed;       // EPI_SYRK with nsplit == 1: C is a packed upper triangle of an M x M matrix
-  uint8_t pad_;
+  uint8_t nchw;           // EPI_SYRK with A == B: X is a convolution tensor [K / lda][M][lda] read in
+                          // place (row k of X: pixel k % lda of image k / lda); see gemm_nchw_syrk_ok
   float alpha, beta;
 };
 
@@ -69,6 +70,11 @@ struct GemmScalars {
   float lr, momentum, weight_decay;
   uint32_t* flags;
 };
+
+// Whether the factor SYRK can read X = the convolution tensor [rows / hw][d][hw]
+// at `X` in place (as rows of d pixels values, GemmProb::nchw) instead of as
+// materialised rows.
+bool gemm_nchw_syrk_ok(const void* X, int64_t rows, int hw, int d);
 
 // Number of workgroups one problem needs.
 int gemm_blocks(const GemmProb& p);

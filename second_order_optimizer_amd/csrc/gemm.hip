@@ -701,6 +701,11 @@ constexpr int kSNS = 3;                    // ring slots (three workgroups per C
 constexpr int kSPair = 2 * 128 + 4;        // a row pair (floats)
 constexpr int kSSlot = (kSK / 2) * kSPair; // floats per operand and slot
 
+// NCHW: X is a convolution tensor [B][d][HW] read in place (row k of X is
+// pixel k % HW of image k / HW: X[k][i] at (k / HW) d HW + i HW + k % HW,
+// lda = HW, a multiple of 16 so that no stage spans two images); its stages
+// sit in LDS as the OP_K operand of the 256 x 256 kernel ([m][16], swizzled).
+template <bool NCHW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 gemm_f32_dma_syrk_kernel(GemmBatch batch) {
   using C = Cfg<false, kTileKSyrk>;
@@ -723,30 +728,46 @@ gemm_f32_dma_syrk_kernel(GemmBatch batch) {
   const int wm = (wid / C::kWavesN) * C::kWM, wn = (wid % C::kWavesN) * C::kWN;
   const bool live = i0 + wm < P.M && j0 + wn < P.N && !(diag && wm >= wn + C::kWN);
 
-  // X: rows [0, P.ke) of lda floats; rows past them read as zero
-  const i32x4_t rx = buf_rsrc(P.A, static_cast<uint32_t>(static_cast<uint64_t>(P.ke) * P.lda * 4));
+  // X: rows [0, P.ke) of lda floats (NCHW: ke / HW images of d HW floats);
+  // reads past them return zero
+  const i32x4_t rx = buf_rsrc(P.A, static_cast<uint32_t>(static_cast<uint64_t>(P.ke) * (NCHW ? P.M : P.lda) * 4));
   const int nops = diag ? 1 : 2;
-  // load instruction q = 2 wid + u (0..7) of an operand: rows 2 q, 2 q + 1 of the stage
+  // load instruction q = 2 wid + u (0..7) of an operand: rows 2 q, 2 q + 1 of
+  // the stage (NCHW: tile rows 16 q .. 16 q + 15, 16 pixels each)
   uint32_t off[2][2];
 #pragma unroll
   for (int op = 0; op < 2; ++op)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = 2 * wid + u;
-      const int row = 2 * q + (lane >> 5);
-      off[op][u] = static_cast<uint32_t>(
-          (static_cast<int64_t>(kb + row) * P.lda + (op ? j0 : i0) + 4 * (lane & 31)) * 4);
+      if (NCHW) {
+        const int m = 16 * q + (lane >> 2);
+        const int c = (lane & 3) ^ kswz(m);
+        off[op][u] = static_cast<uint32_t>((static_cast<int64_t>((op ? j0 : i0) + m) * P.lda + 4 * c) * 4);
+      } else {
+        const int row = 2 * q + (lane >> 5);
+        off[op][u] = static_cast<uint32_t>(
+            (static_cast<int64_t>(kb + row) * P.lda + (op ? j0 : i0) + 4 * (lane & 31)) * 4);
+      }
     }
   const uint32_t step = static_cast<uint32_t>(kSK * P.lda * 4);
   const int nst = (ke - kb + kSK - 1) / kSK;
+  // byte offset of stage s (NCHW: image and first pixel of its rows)
+  auto stage_off = [&](int s) -> uint32_t {
+    if (!NCHW) return static_cast<uint32_t>(s) * step;
+    const int k0 = kb + s * kSK;
+    const int img = k0 / P.lda;
+    return static_cast<uint32_t>((static_cast<int64_t>(img) * P.M * P.lda + (k0 - img * P.lda)) * 4);
+  };
   auto issue = [&](int s, int slot) {
     if (s >= nst) return;
+    const uint32_t so = stage_off(s);
 #pragma unroll
     for (int op = 0; op < 2; ++op) {
       if (op >= nops) break;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        dma16(&ring[slot][op][(2 * wid + u) * kSPair], off[op][u] + static_cast<uint32_t>(s) * step, rx);
+        dma16(&ring[slot][op][(2 * wid + u) * (NCHW ? 256 : kSPair)], off[op][u] + so, rx);
     }
   };
 
@@ -773,7 +794,41 @@ gemm_f32_dma_syrk_kernel(GemmBatch batch) {
     }
     __builtin_amdgcn_s_barrier();
     issue(s + kSNS - 1, slot == 0 ? kSNS - 1 : slot - 1);
-    if (live) {
+    if (live && NCHW) {
+      const float* sa = ring[slot][0];
+      const float* sb = diag ? sa : ring[slot][1];
+      // rows wm + 32 i + l32 (wn + 32 j + l32): chunks 2 h and 2 h + 1 hold
+      // the stage's k = 8 h .. 8 h + 7
+      float ak[8][C::kBI], bk[8][C::kBJ];
+#pragma unroll
+      for (int i = 0; i < C::kBI; ++i) {
+        const int m = wm + 32 * i + l32;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sa + m * kSK + 4 * ((2 * h + cc) ^ kswz(m)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ak[4 * cc + e][i] = v[e];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C::kBJ; ++j) {
+        const int n = wn + 32 * j + l32;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sb + n * kSK + 4 * ((2 * h + cc) ^ kswz(n)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bk[4 * cc + e][j] = v[e];
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+#pragma unroll
+        for (int i = 0; i < C::kBI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::kBJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ak[st][i], bk[st][j], acc[i][j], 0, 0, 0);
+      }
+    } else if (live) {
       const float* sa = ring[slot][0];
       const float* sb = diag ? sa : ring[slot][1];
       float afr[2][C::kBI], bfr[2][C::kBJ];
@@ -807,7 +862,8 @@ gemm_f32_dma_syrk_kernel(GemmBatch batch) {
 
 kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int bm, int epi, bool b16, hipStream_t s) {
   if (epi == EPI_SYRK) {
-    hipLaunchKernelGGL(gemm_f32_dma_syrk_kernel, dim3(blocks), dim3(256), 0, s, b);
+    if (b.p[0].nchw) hipLaunchKernelGGL(gemm_f32_dma_syrk_kernel<true>, dim3(blocks), dim3(256), 0, s, b);
+    else hipLaunchKernelGGL(gemm_f32_dma_syrk_kernel<false>, dim3(blocks), dim3(256), 0, s, b);
     return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
   }
 #define KFAC_DMA_CASE(A_, B_, E_, W_)                                                        \
@@ -832,6 +888,7 @@ kfac_status_t dispatch_dma(const GemmBatch& b, int blocks, int am, int bm, int e
 // others: one launch instead of two)
 constexpr int kDmaSyrkMinRows = 512;
 bool dma_syrk_eligible(const GemmProb& p) {
+  if (p.nchw) return true;   // planned with gemm_nchw_syrk_ok
   if (p.ke - p.kb < kDmaSyrkMinRows) return false;
   if (p.A != p.B || p.lda != p.ldb || p.a_special >= 0 || p.b_special >= 0 || p.nbatch > 1 || p.tri != TRI_UPPER ||
       p.krange != KR_ALL || p.kb != 0 || p.M != p.N)
@@ -879,6 +936,12 @@ int tiles_for(const GemmProb& p, int bt) {
 }
 
 }  // namespace
+
+bool gemm_nchw_syrk_ok(const void* X, int64_t rows, int hw, int d) {
+  return hw > 0 && hw % kSK == 0 && rows % hw == 0 && rows >= kDmaSyrkMinRows && d > 0 &&
+         (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+         (static_cast<uint64_t>(rows) * d + static_cast<uint64_t>(128) * hw) * 4 < (uint64_t(1) << 32);
+}
 
 void gemm_set_tiles(GemmProb& p) {
   p.tiles_m = (p.M + kTile - 1) / kTile;
@@ -942,9 +1005,10 @@ kfac_status_t launch_with(std::vector<GemmProb>& probs, int amode, int bmode, in
 kfac_status_t launch_gemm(std::vector<GemmProb>& probs, int amode, int bmode, int epi, const GemmScalars& sc,
                           hipStream_t stream, int policy) {
   if (policy == TILES_SMALL && epi == EPI_SYRK && amode == OP_MN && bmode == OP_MN) {
-    std::vector<GemmProb> dma, rest;
-    for (const GemmProb& p : probs) (dma_syrk_eligible(p) ? dma : rest).push_back(p);
+    std::vector<GemmProb> dma, nchw, rest;
+    for (const GemmProb& p : probs) (p.nchw ? nchw : dma_syrk_eligible(p) ? dma : rest).push_back(p);
     kfac_status_t st = dma.empty() ? KFAC_OK : launch_with(dma, amode, bmode, epi, sc, stream, false, true);
+    if (st == KFAC_OK && !nchw.empty()) st = launch_with(nchw, amode, bmode, epi, sc, stream, false, true);
     if (st != KFAC_OK) return st;
     return rest.empty() ? KFAC_OK : launch_with(rest, amode, bmode, epi, sc, stream, false);
   }

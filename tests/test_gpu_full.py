@@ -325,6 +325,23 @@ def test_big_tile_ragged_lockstep(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
+def test_conv_factors_read_in_place(gpu_lib):
+    """Convolution factors whose SYRK reads the NCHW tensor in place: the
+    input of 1 x 1 stride-1 convolutions (8 x 8 and 16 x 16 planes, channel
+    counts that end inside a tile) and the output gradients of 3 x 3
+    convolutions with 16 x 16 output planes, at 1,024-4,096 rows (row splits),
+    next to the same kinds that are laid out as rows first (a strided 1 x 1
+    convolution, 10 x 10 planes); 3 steps against the oracle."""
+    L = [synth.conv("pw8", 96, 130, 1, 1, 0, 16, 8),
+         synth.conv("pw16", 64, 200, 1, 1, 0, 16, 16),
+         synth.conv("c3", 40, 72, 3, 1, 1, 4, 16),
+         synth.conv("c3s", 24, 64, 3, 2, 1, 4, 32),
+         synth.conv("pw_s2", 48, 80, 1, 2, 0, 4, 16),
+         synth.conv("pw10", 56, 90, 1, 1, 0, 8, 10)]
+    cfg = with_layers(synth.small_config("resnet50_kfac"), L, steps=3)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
+
+
 def test_full_nonfinite_flag(gpu_lib):
     """A NaN in the weight gradient of a layer whose update runs in the GEMM
     epilogue, and separately in the bias gradient of a layer whose bias
