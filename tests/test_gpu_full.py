@@ -185,18 +185,22 @@ def test_bf16_factor_row_chunks(gpu_lib):
     assert e <= 2e-2
 
 
-def test_graph_replays_match_eager(gpu_lib):
+@pytest.mark.parametrize("extra", [0, 24])
+def test_graph_replays_match_eager(gpu_lib, extra):
     """One full step (factors; the two-level Cholesky with its far updates
-    and the early inverse assembly on the library's side streams; update)
+    and the inverse assembly on the library's side streams; update)
     captured in a HIP graph through torch.cuda.graph on ResNet-50 layer kinds
     (factors of up to 9 Cholesky blocks, three outer panels) plus a biased
     256-input layer (its bias column on the side stream beside the update
-    GEMMs); three replays, each followed by eager work and a synchronisation,
-    match three eager steps on the same inputs bitwise."""
+    GEMMs), and with 24 more small layers (more problems than one launch's
+    table holds: every GEMM kind in several launches); three replays, each
+    followed by eager work and a synchronisation, match three eager steps on
+    the same inputs bitwise."""
     import torch
     from second_order_optimizer_amd.stack import KfacStack
     base = synth.small_config("resnet50_kfac")
-    cfg = with_layers(base, list(base.layers) + [synth.linear("fc_split", 256, 96, 32, bias=True)])
+    more = [synth.linear(f"small{i}", 48, 40, 16, bias=(i % 2 == 0)) for i in range(extra)]
+    cfg = with_layers(base, list(base.layers) + [synth.linear("fc_split", 256, 96, 32, bias=True)] + more)
     H = KfacStack.hparams(synth.hparams(cfg), refresh=True)
 
     def make():
