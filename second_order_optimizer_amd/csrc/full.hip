@@ -1203,7 +1203,9 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
         p.lda = p.ldb = d;
         p.C = P.W[g.first];
         p.ldc = d;
-        p.M = p.N = d;
+        // the first pass stores every tile of W (zero where its rows add
+        // nothing); a later pass adds only into the leading k1 x k1 block
+        p.M = p.N = pr.rows == 0 ? d : k1;
         p.kb = pr.rows;
         p.ke = k1;
         p.tri = TRI_UPPER;
@@ -1216,6 +1218,8 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
         pr.rows = k1;
       }
       if (first.empty() && later.empty()) break;
+      // (128 x 128 tiles for the passes of kLauRows rows: they run beside the
+      // Cholesky chain, whose kernels need room on the CUs)
       const int policy = by_rows ? TILES_SMALL : TILES_AUTO;
       kfac_status_t r = first.empty() ? KFAC_OK : launch_gemm(first, OP_MN, OP_MN, EPI_STORE, sc, fs, policy);
       if (r == KFAC_OK && !later.empty()) r = launch_gemm(later, OP_MN, OP_MN, EPI_SUB, sc, fs, policy);
