@@ -1,16 +1,21 @@
-// Batched fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
-//
-// Two tile shapes, picked per launch: 128 x 128 tiles on 256 threads (4
-// wavefronts of 64 x 64 = 2 x 2 MFMA 32 x 32 blocks) for small problem sets,
-// 256 x 256 tiles on 512 threads (8 wavefronts of 128 x 64 = 4 x 2 blocks)
-// when there are at least two such tiles per CU.  K advances 16 at a time:
-// the next A/B slabs are fetched into registers while the current ones,
-// staged in LDS as [k][m] rows (m contiguous, padded), feed the MFMAs.  fp32
-// in, fp32 accumulate, fp32 out.
-//
+// Batched fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32), fp32 in,
+// fp32 accumulate, fp32 out.  Three kernels:
+//   gemm_f32_kernel           register-staged: the next stage's A/B slabs are
+//                             fetched into registers while the current ones,
+//                             staged in LDS, feed the MFMAs; 128 x 128 tiles on
+//                             256 threads (4 wavefronts of 2 x 2 MFMA 32 x 32
+//                             blocks) or 256 x 256 tiles on 512 threads (8
+//                             wavefronts of 4 x 2 blocks) when a launch has at
+//                             least two such tiles per CU; every problem kind;
+//   gemm_f32_dma_kernel       256 x 256 tiles with direct-to-LDS loads
+//                             (buffer_load ... lds into a 4-slot ring), for the
+//                             large launches whose problems it can load;
+//   gemm_f32_dma_syrk_kernel  the factor SYRK on 128 x 128 tiles with the same
+//                             loader, from row-major X or from a convolution
+//                             tensor read in place.
 // One launch runs a table of independent problems (layers, matrices, K
-// splits); each workgroup finds its problem by binary search over the
-// table's block offsets.
+// splits, batches); each workgroup finds its problem by binary search over
+// the table's block offsets.
 #include "gemm.h"
 
 #include <algorithm>
