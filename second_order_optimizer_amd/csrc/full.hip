@@ -330,50 +330,96 @@ __device__ inline void tile_store(float* S, int ld, int r0, int c0, const f32x16
 
 // Wavefront-level factorization of the 32 x 32 diagonal sub-block at (c0, c0)
 // of Ms; writes the factor into Ms and its inverse into Zs at the same place.
-__device__ inline void factor_diag32(float* Ms, float* Zs, int c0, const DMat& M, uint32_t* flags, int lane) {
+// Step j is a rank-1 update by u = column j of the (symmetric) remaining
+// block, which every lane needs whole.  Lane r holds row j of column r, which
+// is u_r by symmetry, so the lanes exchange u through the 64 floats at Us:
+// each writes its entry, then all read it back with broadcast 16-byte reads
+// (no cross-lane register moves).
+__device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, float* Zs, float* Us, int c0,
+                                                                   const DMat& M, uint32_t* flags, int lane) {
   const int c = lane & 31;
   const bool xl = lane >= 32;
   float v[32];
 #pragma unroll
   for (int r = 0; r < 32; ++r) v[r] = xl ? (r == c ? 1.f : 0.f) : Ms[(c0 + r) * kLd + c0 + c];
-  float pv[32];
-  float dmine = 1.f;
+  Us[lane] = v[0];   // (the X lanes' entries, Us[32..63], are never read)
+  __builtin_amdgcn_wave_barrier();
+  // u_q .. u_31 (the aligned quads from q on) as last written
+  auto gather = [&](float* u, int q0) {
+#pragma unroll
+    for (int q = q0 / 4; q < 8; ++q) {
+      const f32x4 t4 = *reinterpret_cast<const f32x4*>(Us + 4 * q);
+      u[4 * q] = t4.x;
+      u[4 * q + 1] = t4.y;
+      u[4 * q + 2] = t4.z;
+      u[4 * q + 3] = t4.w;
+    }
+  };
+  float dmine = 1.f;   // this lane's pivot (lane c: d_c)
   bool bad = false;
-  // no branch inside the loop: the scheduler may start step j + 1 while
-  // step j's remaining updates issue
+  float ua[32], ub[32];
+  gather(ua, 0);
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), j));
+    float* u = (j & 1) ? ub : ua;    // this step's u (the pivot is u_j)
+    float* un = (j & 1) ? ua : ub;   // the next step's
+    float piv = u[j];
     const bool ok = piv > 0.f && isfinite(piv);
     bad = bad || !ok;
     piv = ok ? piv : 1.f;
-    pv[j] = piv;
     if (c == j) dmine = piv;
     const float inv = __builtin_amdgcn_rcpf(piv);
-    // A lanes: columns c > j take the rank-1 update (row j of column c is
-    // B_jc = B_cj); finished columns keep their multipliers.  X lanes: row
+    // u_j's quad also brought the entries before it, which are not needed:
+    // held until here (their load has landed with u_j), their registers are
+    // not handed to this step's updates while the load is still in flight
+    // (which would make the updates wait for it)
+#pragma unroll
+    for (int r = 4 * (j / 4); r < j; ++r) asm volatile("" ::"v"(u[r]));
+    // A lanes: columns c > j take the update (row j of column c is
+    // B_jc = u_c); finished columns keep their multipliers.  X lanes: row
     // operation on the whole row.
     const float t = (xl || c > j) ? v[j] * inv : 0.f;
-    // the whole column first (independent broadcasts), then the updates
-    float col[32];
+    if (j + 1 < 32) {
+      // the next step's u first, so that its round trip through LDS
+      // overlaps the rest of this step
+      v[j + 1] = fmaf(-u[j + 1], t, v[j + 1]);
+      Us[lane] = v[j + 1];
+      __builtin_amdgcn_wave_barrier();
+      gather(un, j + 1);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the rest of the step's updates, each held to this step: left to
+    // itself, the compiler defers every update to its first use and keeps
+    // all earlier steps' u in registers
 #pragma unroll
-    for (int r = j + 1; r < 32; ++r) col[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), j));
-#pragma unroll
-    for (int r = j + 1; r < 32; ++r) v[r] = fmaf(-col[r], t, v[r]);
+    for (int r = j + 2; r < 32; ++r) {
+      v[r] = fmaf(-u[r], t, v[r]);
+      asm volatile("" : "+v"(v[r]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (bad && lane == 0 && *M.fail == 0) {
     *M.fail = 1;
     raise_flag(flags, KFAC_FLAG_NOT_PD);
   }
+  // scales: lane c computes sqrt(d_c) and 1 / sqrt(d_c) for pivot c (its
+  // own, dmine) and shares the latter through Us, so the X lanes' row scales
+  // cost one division per lane instead of 32 in a row
+  const float s = sqrtf(dmine), is = 1.0f / s;
+  Us[lane] = is;
+  __builtin_amdgcn_wave_barrier();
+  float rs[32];
+  gather(rs, 0);
+  __builtin_amdgcn_wave_barrier();
   if (!xl) {
     // L_rc = B_rc / sqrt(d_c) below the diagonal, sqrt(d_c) on it
-    const float s = sqrtf(dmine), is = 1.0f / s;
 #pragma unroll
     for (int r = 0; r < 32; ++r) Ms[(c0 + r) * kLd + c0 + c] = r > c ? v[r] * is : (r == c ? s : 0.f);
   } else {
     // (L^-1)_rc = X_rc / sqrt(d_r)
 #pragma unroll
-    for (int r = 0; r < 32; ++r) Zs[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * (1.0f / sqrtf(pv[r])) : 0.f;
+    for (int r = 0; r < 32; ++r) Zs[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * rs[r] : 0.f;
   }
 }
 
@@ -381,6 +427,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   __shared__ __attribute__((aligned(16))) float Ms[kNb * kLd];
   __shared__ __attribute__((aligned(16))) float Zs[kNb * kLd];
   __shared__ __attribute__((aligned(16))) float Ss[4][32 * kSd];
+  __shared__ __attribute__((aligned(16))) float Us[64];
   const DMat& M = T.m[blockIdx.x];
   const int d = M.d, k = T.k;
   const int nblk = (d + kNb - 1) / kNb;
@@ -391,22 +438,45 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   float* Lg = M.L + static_cast<int64_t>(r0) * d + r0;
 
   // symmetric working block from the lower triangle; identity beyond bk.
-  // Thread t reads column t % 128 of rows t / 128 + 2 i, 32 loads in flight.
-  const int lc = tid & (kNb - 1), lr = tid >> 7;
-  for (int i0 = 0; i0 < kNb / 2; i0 += 32) {
-    float vals[32];
+  // With d a multiple of 4 (16-byte rows), thread t reads quad t % 32 of
+  // rows t / 32 + 8 i, all 16 loads in flight; otherwise column t % 128 of
+  // rows t / 128 + 2 i, 32 loads at a time.
+  const bool vec = (d & 3) == 0;
+  auto put = [&](int r, int c, float v) {   // (r, c), c <= r, and its mirror
+    const float x = r < bk ? v : (r == c ? 1.f : 0.f);
+    Ms[r * kLd + c] = x;
+    Ms[c * kLd + r] = x;
+  };
+  if (vec) {
+    const int q = tid & 31, rr = tid >> 5;
+    f32x4 vals[16];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int r = lr + 2 * (i0 + u);
-      vals[u] = (r < bk && lc <= r) ? Lg[static_cast<int64_t>(r) * d + lc] : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const int r = rr + 8 * i;
+      vals[i] = (r < bk && 4 * q <= r) ? *reinterpret_cast<const f32x4*>(Lg + static_cast<int64_t>(r) * d + 4 * q)
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int r = lr + 2 * (i0 + u);
-      if (lc > r) continue;
-      const float v = r < bk ? vals[u] : (r == lc ? 1.f : 0.f);
-      Ms[r * kLd + lc] = v;
-      Ms[lc * kLd + r] = v;
+    for (int i = 0; i < 16; ++i) {
+      const int r = rr + 8 * i;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e <= r) put(r, 4 * q + e, vals[i][e]);
+    }
+  } else {
+    const int lc = tid & (kNb - 1), lr = tid >> 7;
+    for (int i0 = 0; i0 < kNb / 2; i0 += 32) {
+      float vals[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int r = lr + 2 * (i0 + u);
+        vals[u] = (r < bk && lc <= r) ? Lg[static_cast<int64_t>(r) * d + lc] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int r = lr + 2 * (i0 + u);
+        if (lc <= r) put(r, lc, vals[u]);
+      }
     }
   }
   __syncthreads();
@@ -417,7 +487,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   const int np = (bk + 31) / 32;
   for (int p = 0; p < np; ++p) {
     const int c0 = 32 * p;
-    if (wid == 0) factor_diag32(Ms, Zs, c0, M, T.flags, lane);
+    if (wid == 0) factor_diag32(Ms, Zs, Us, c0, M, T.flags, lane);
     __syncthreads();
     // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
     if (wid < np - 1 - p) {
@@ -456,16 +526,33 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   }
 
   // write back Dinv[k] and Z_kk (L_kk itself is not read again: the panel
-  // below it is formed with Dinv[k])
+  // below it is formed with Dinv[k]); thread t writes quad t % 32 of rows
+  // t / 32 + 8 i (bk is a multiple of 4 when d is)
   float* D = M.Dinv + static_cast<int64_t>(k) * kNb * kNb;
   float* Zg = M.Z + static_cast<int64_t>(r0) * d + r0;
-#pragma unroll 8
-  for (int e = tid; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e - (e / kNb) * kNb;
-    const bool in = r < bk && c < bk;
-    const float z = c <= r ? Zs[r * kLd + c] : 0.f;
-    D[e] = in ? z : 0.f;
-    if (in) Zg[static_cast<int64_t>(r) * d + c] = z;
+  {
+    const int q = tid & 31, rr = tid >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = rr + 8 * i;
+      f32x4 z;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * q + e;
+        z[e] = (c <= r && r < bk && c < bk) ? Zs[r * kLd + c] : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(D + r * kNb + 4 * q) = z;
+      if (r < bk) {
+        float* zr = Zg + static_cast<int64_t>(r) * d + 4 * q;
+        if (vec) {
+          if (4 * q < bk) *reinterpret_cast<f32x4*>(zr) = z;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q + e < bk) zr[e] = z[e];
+        }
+      }
+    }
   }
 }
 
