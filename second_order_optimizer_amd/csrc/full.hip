@@ -233,40 +233,55 @@ struct DiagTab {
   uint32_t* flags;
 };
 
-// L = F + damping I from F's upper triangle (both triangles of L written),
-// Z = 0, fail = 0.  grid = (32 x 32 tiles, matrix); a lower tile (I > J) is
-// read from F's upper tile (J, I) row by row and transposed through LDS.
+// L = F + damping I (lower triangle) from F's upper triangle, fail = 0, and
+// zeros in Z's strict upper triangle within 256 of the diagonal.  Nothing
+// reads L's upper triangle (the triangular inverse stages its products
+// there), Z's lower triangle is written whole by the inverse, and the tiles
+// of the inverse's products that straddle the diagonal (at most 256 wide)
+// read Z's upper entries in that band only.  grid = (32 x 32 tiles, matrix);
+// a lower tile (I > J) is read from F's upper tile (J, I) row by row and
+// transposed through LDS.  T.k selects the tiles: 0 all, 1 the columns of the
+// first outer panel of L (what the first inner steps need), 2 the rest.
+constexpr int kInitSplit = kOuter * kNb;   // the first outer panel's columns
 __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
   __shared__ float t[32][33];
   const Mat& M = T.m[blockIdx.y];
   const int d = M.d;
   const int nt = (d + 31) / 32;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *M.fail = 0;
+  if (T.k != 2 && blockIdx.x == 0 && threadIdx.x == 0) *M.fail = 0;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
     const int I = tile / nt, J = tile - (tile / nt) * nt;
-    const bool lower = I > J;
-    const int sr = (lower ? J : I) * 32, sc = (lower ? I : J) * 32;   // source tile in the upper triangle
-    __syncthreads();
-    for (int r = ty; r < 32; r += 8) {
-      const int i = sr + r, j = sc + tx;
-      // only upper entries are used (a diagonal tile mirrors its upper part)
-      float v = 0.f;
-      if (i < d && j < d && i <= j) v = M.F[M.packed ? packed_index(i, j, d) : static_cast<int64_t>(i) * d + j];
-      t[r][tx] = v;
+    const bool first = J * 32 < kInitSplit;
+    const bool fill_l = I >= J && (T.k == 0 || (T.k == 1) == first);
+    const bool zero_z = I <= J && I / 8 == J / 8 && T.k != 1;   // (same 256-block)
+    if (!fill_l && !zero_z) continue;   // (uniform across the workgroup)
+    if (fill_l) {
+      const bool lower = I > J;
+      const int sr = (lower ? J : I) * 32, sc = (lower ? I : J) * 32;   // source tile in the upper triangle
+      __syncthreads();
+      for (int r = ty; r < 32; r += 8) {
+        const int i = sr + r, j = sc + tx;
+        // only upper entries are used (a diagonal tile mirrors its upper part)
+        float v = 0.f;
+        if (i < d && j < d && i <= j) v = M.F[M.packed ? packed_index(i, j, d) : static_cast<int64_t>(i) * d + j];
+        t[r][tx] = v;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int r = ty; r < 32; r += 8) {
       const int i = I * 32 + r, j = J * 32 + tx;
       if (i >= d || j >= d) continue;
-      float v;
-      if (lower) v = t[tx][r];
-      else if (I == J) v = t[min(r, tx)][max(r, tx)];   // diagonal tile: mirror its upper part
-      else v = t[r][tx];
-      if (i == j) v += T.damping;
       const int64_t e = static_cast<int64_t>(i) * d + j;
-      M.L[e] = v;
-      M.Z[e] = 0.f;
+      if (i >= j) {
+        if (fill_l) {
+          float v = I > J ? t[tx][r] : t[min(r, tx)][max(r, tx)];   // diagonal tile: mirror its upper part
+          if (i == j) v += T.damping;
+          M.L[e] = v;
+        }
+      } else if (zero_z) {
+        M.Z[e] = 0.f;
+      }
     }
   }
 }
@@ -1051,11 +1066,15 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     }
     return T.n > 0 ? fn(T) : KFAC_OK;
   };
-  kfac_status_t r = tables([](const Mat&) { return true; }, 0, [&](MatTab& T) {
-    hipLaunchKernelGGL(chol_init_kernel, dim3(2048, T.n), dim3(256), 0, st, T);
-    return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
-  });
-  if (r != KFAC_OK) return r;
+  // L = F + damping I (part 0: all of it; 1: the first outer panel's
+  // columns; 2: the rest)
+  auto init = [&](int part) {
+    return tables([](const Mat&) { return true; }, part, [&](MatTab& T) {
+      hipLaunchKernelGGL(chol_init_kernel, dim3(2048, T.n), dim3(256), 0, st, T);
+      return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+    });
+  };
+  kfac_status_t r;
   // Blocked right-looking Cholesky in two levels.  Inner step k factors
   // diagonal block k (chol_diag) and forms the panel L_ik = M_ik Dinv_k^T
   // below it.  Blocks are grouped kOuter at a time into outer panels; the
@@ -1336,11 +1355,18 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   if (nblk_max == 1) {
     // every factor is one diagonal block: no chain to overlap, so the same
     // launches run in order on the caller's stream (no fork, no events)
-    r = diag_step(0, st);
+    r = init(0);
+    if (r == KFAC_OK) r = diag_step(0, st);
     if (r != KFAC_OK) return r;
     return assemble(d_all, st);
   }
   hipStream_t fs = side->f;
+  // the chain starts once the first outer panel is initialised; the rest of
+  // L (and Z's band) follows on the caller's stream beside it, ahead of the
+  // first far update there (main_done[1] for the first F_next and the
+  // assembly)
+  r = init(1);
+  if (r != KFAC_OK) return r;
   KFAC_HIP_TRY(hipEventRecord(side->fork, st));
   const int nouter = (nblk_max + kOuter - 1) / kOuter;
   // everything between the fork and the join; an error inside still reaches
@@ -1349,12 +1375,15 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   auto chain = [&]() -> kfac_status_t {
   KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->fork, 0));
   KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->fork, 0));
-  kfac_status_t r;
+  kfac_status_t r = init(2);
+  if (r != KFAC_OK) return r;
+  KFAC_HIP_TRY(hipEventRecord(side->main_done[1], st));
   for (int K = 0; K < nouter; ++K) {
     const int k0 = K * kOuter, k1 = k0 + kOuter;   // blocks of outer panel K
     // second stream: F_next(K - 1) after F_rest(K - 2), then the inner steps
     if (K > 0) {
-      if (K > 1) KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[K & 1], 0));
+      // (K = 1: the initialisation of the rest; later: F_rest(K - 2))
+      KFAC_HIP_TRY(hipStreamWaitEvent(ss, side->main_done[K & 1], 0));
       std::vector<GemmProb> fn;
       for (const FullPlan::Group& g : groups) {
         const Mat& m = mats[g.first];
@@ -1411,6 +1440,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     bool active = false;
     for (const FullPlan::Group& g : groups) active = active || static_cast<int>(nblk_of(mats[g.first].d)) > k0;
     if (active) {
+      if (K == 0) KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->main_done[1], 0));   // Z's band
       KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->side_done[K & 1], 0));
       r = assemble(k1 * kNb, fs);
       if (r != KFAC_OK) return r;
