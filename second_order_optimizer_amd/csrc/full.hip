@@ -291,20 +291,22 @@ __global__ void __launch_bounds__(256) chol_init_kernel(MatTab T) {
 // blocked by 32 columns with the whole block in LDS.  Per 32-column panel:
 //  - wavefront 0 factors the 32 x 32 diagonal sub-block in registers: lane c
 //    holds column c of the sub-block, lane 32 + c column c of an identity;
-//    elimination is sqrt-free (row r -= (B_rj / B_jj) row j, column j
-//    broadcast from lane j by v_readlane), which yields D^-1/2-scaled forms
-//    of both L (columns) and L^-1 (rows);
+//    elimination is sqrt-free (row r -= (B_rj / B_jj) row j), which yields
+//    D^-1/2-scaled forms of both L (columns) and L^-1 (rows);
 //  - the sub-diagonal panel L_qp = M_qp Z_pp^T and the trailing update
 //    M_ij -= L_ip L_jp^T run on MFMA, one 32 x 32 tile per wavefront.
 // The off-diagonal blocks of the inverse follow by rows,
-// Z_ij = -Z_ii sum_{j<=m<i} L_im Z_mj, also on MFMA.  The inverse goes to
-// Dinv[k] and to Z's diagonal block; L_kk itself is not written back (later
-// steps use only its inverse).  A pivot that is not positive (or not finite)
+// Z_ij = -Z_ii sum_{j<=m<i} L_im Z_mj, also on MFMA.  One 128 x 128 array
+// holds everything (66 KB of LDS, so that the workgroup fits on a CU beside a
+// 128 x 128 GEMM workgroup): L's off-diagonal blocks below the diagonal, Z's
+// diagonal blocks in place of L's (which no later step reads: the panel below
+// a block is formed with its inverse), and Z's off-diagonal blocks transposed
+// above the diagonal.  The inverse goes to Dinv[k] and to Z's diagonal block;
+// L_kk is not written back.  A pivot that is not positive (or not finite)
 // marks the matrix failed, raises KFAC_FLAG_NOT_PD and is replaced by 1 so the
 // remaining steps stay finite; a failed matrix's inverse is not written.
 // Rows and columns beyond a partial last block are an identity.
 constexpr int kLd = kNb + 1;   // LDS pitch: row and column walks hit distinct banks
-constexpr int kSd = 33;        // pitch of a wavefront's 32 x 32 staging tile
 
 __device__ inline f32x16 mfma32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -343,15 +345,21 @@ __device__ inline void tile_store(float* S, int ld, int r0, int c0, const f32x16
   for (int r = 0; r < 16; ++r) S[(r0 + acc_row(r, lane)) * ld + c0 + (lane & 31)] = sign * acc[r];
 }
 
+// the tile transposed: element (i, j) to S[(r0 + j) * ld + c0 + i]
+__device__ inline void tile_store_t(float* S, int ld, int r0, int c0, const f32x16& acc, float sign, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[(r0 + (lane & 31)) * ld + c0 + acc_row(r, lane)] = sign * acc[r];
+}
+
 // Wavefront-level factorization of the 32 x 32 diagonal sub-block at (c0, c0)
-// of Ms; writes the factor into Ms and its inverse into Zs at the same place.
+// of Ms; writes its inverse over it (the factor itself is not kept).
 // Step j is a rank-1 update by u = column j of the (symmetric) remaining
 // block, which every lane needs whole.  Lane r holds row j of column r, which
 // is u_r by symmetry, so the lanes exchange u through the 64 floats at Us:
 // each writes its entry, then all read it back with broadcast 16-byte reads
 // (no cross-lane register moves).
-__device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, float* Zs, float* Us, int c0,
-                                                                   const DMat& M, uint32_t* flags, int lane) {
+__device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, float* Us, int c0, const DMat& M,
+                                                                   uint32_t* flags, int lane) {
   const int c = lane & 31;
   const bool xl = lane >= 32;
   float v[32];
@@ -418,30 +426,22 @@ __device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, f
     *M.fail = 1;
     raise_flag(flags, KFAC_FLAG_NOT_PD);
   }
-  // scales: lane c computes sqrt(d_c) and 1 / sqrt(d_c) for pivot c (its
-  // own, dmine) and shares the latter through Us, so the X lanes' row scales
-  // cost one division per lane instead of 32 in a row
-  const float s = sqrtf(dmine), is = 1.0f / s;
-  Us[lane] = is;
+  // row scales 1 / sqrt(d_r): lane c computes its own pivot's (dmine) and
+  // shares it through Us, one division per lane instead of 32 in a row
+  Us[lane] = 1.0f / sqrtf(dmine);
   __builtin_amdgcn_wave_barrier();
   float rs[32];
   gather(rs, 0);
   __builtin_amdgcn_wave_barrier();
-  if (!xl) {
-    // L_rc = B_rc / sqrt(d_c) below the diagonal, sqrt(d_c) on it
-#pragma unroll
-    for (int r = 0; r < 32; ++r) Ms[(c0 + r) * kLd + c0 + c] = r > c ? v[r] * is : (r == c ? s : 0.f);
-  } else {
+  if (xl) {
     // (L^-1)_rc = X_rc / sqrt(d_r)
 #pragma unroll
-    for (int r = 0; r < 32; ++r) Zs[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * rs[r] : 0.f;
+    for (int r = 0; r < 32; ++r) Ms[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * rs[r] : 0.f;
   }
 }
 
 __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   __shared__ __attribute__((aligned(16))) float Ms[kNb * kLd];
-  __shared__ __attribute__((aligned(16))) float Zs[kNb * kLd];
-  __shared__ __attribute__((aligned(16))) float Ss[4][32 * kSd];
   __shared__ __attribute__((aligned(16))) float Us[64];
   const DMat& M = T.m[blockIdx.x];
   const int d = M.d, k = T.k;
@@ -502,13 +502,13 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   const int np = (bk + 31) / 32;
   for (int p = 0; p < np; ++p) {
     const int c0 = 32 * p;
-    if (wid == 0) factor_diag32(Ms, Zs, Us, c0, M, T.flags, lane);
+    if (wid == 0) factor_diag32(Ms, Us, c0, M, T.flags, lane);
     __syncthreads();
     // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
     if (wid < np - 1 - p) {
       const int q = p + 1 + wid;
       f32x16 acc = {};
-      mma_nt(acc, Ms, 32 * q, c0, Zs, c0, c0, 1.f, lane);
+      mma_nt(acc, Ms, 32 * q, c0, Ms, c0, c0, 1.f, lane);
       tile_store(Ms, kLd, 32 * q, c0, acc, 1.f, lane);
     }
     __syncthreads();
@@ -526,16 +526,20 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
     __syncthreads();
   }
 
-  // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj
+  // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj, with
+  // Z_mj (m > j) held transposed at block (j, m); the sum is staged, also
+  // transposed, at block (j, i), where Z_ij then goes (wavefront j alone
+  // touches that block in this row)
   for (int i = 1; i < np; ++i) {
     if (wid < i) {
       const int j = wid;
       f32x16 acc = {};
-      for (int m = j; m < i; ++m) mma_nn(acc, Ms, 32 * i, 32 * m, Zs, kLd, 32 * m, 32 * j, lane);
-      tile_store(Ss[wid], kSd, 0, 0, acc, 1.f, lane);
+      mma_nn(acc, Ms, 32 * i, 32 * j, Ms, kLd, 32 * j, 32 * j, lane);
+      for (int m = j + 1; m < i; ++m) mma_nt(acc, Ms, 32 * i, 32 * m, Ms, 32 * j, 32 * m, 1.f, lane);
+      tile_store_t(Ms, kLd, 32 * j, 32 * i, acc, 1.f, lane);
       f32x16 z = {};
-      mma_nn(z, Zs, 32 * i, 32 * i, Ss[wid], kSd, 0, 0, lane);
-      tile_store(Zs, kLd, 32 * i, 32 * j, z, -1.f, lane);
+      mma_nt(z, Ms, 32 * i, 32 * i, Ms, 32 * j, 32 * i, 1.f, lane);
+      tile_store_t(Ms, kLd, 32 * j, 32 * i, z, -1.f, lane);
     }
     __syncthreads();
   }
@@ -554,7 +558,8 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 4 * q + e;
-        z[e] = (c <= r && r < bk && c < bk) ? Zs[r * kLd + c] : 0.f;
+        // (an off-diagonal 32-block of Z is held transposed)
+        z[e] = (c <= r && r < bk && c < bk) ? Ms[(r >> 5) == (c >> 5) ? r * kLd + c : c * kLd + r] : 0.f;
       }
       *reinterpret_cast<f32x4*>(D + r * kNb + 4 * q) = z;
       if (r < bk) {
