@@ -299,9 +299,9 @@ __device__ inline uint32_t tap_mask(int x, int k, int pad, int stride, int n_out
 // for a single kernel row) along the columns, VEC consecutive pixels per
 // load; a pixel adds its value to every tap (kh, kw) of the item whose masks
 // say it lies in that tap's window.  Each pixel of S is read once per item.
-template <int K, int VEC>
+template <int K, int VEC, bool TABS>
 __device__ __forceinline__ void fin_window(const FinTask& T, int c, int kh0, int nk, int tix, int nthr,
-                                           const uint8_t* rowtab, const uint8_t* coltab, bool tabs,
+                                           const uint8_t* rowtab, const uint8_t* coltab,
                                            float (&acc)[fin_nkh(K) * K]) {
   constexpr int NKH = fin_nkh(K);
 #pragma unroll
@@ -326,11 +326,14 @@ __device__ __forceinline__ void fin_window(const FinTask& T, int c, int kh0, int
   // lane position (row i, load column x), stepped by nthr loads without division
   const int di = nthr / wv, dx = nthr - (nthr / wv) * wv;
   int i = tix / wv, x = tix - (tix / wv) * wv;
-  for (int q0 = tix; q0 < nld; q0 += 8 * nthr) {
-    float v[8][VEC];
-    int hh[8], ww[8];
+  // (8 loads in flight with the tables; the rare path without them, which
+  // computes every tap mask, takes one at a time to stay small)
+  constexpr int NL = TABS ? 8 : 1;
+  for (int q0 = tix; q0 < nld; q0 += NL * nthr) {
+    float v[NL][VEC];
+    int hh[NL], ww[NL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NL; ++u) {
       const bool ok = q0 + u * nthr < nld;
       hh[u] = ok ? hfirst + i * hstep : -1;
       ww[u] = x * VEC;
@@ -351,12 +354,12 @@ __device__ __forceinline__ void fin_window(const FinTask& T, int c, int kh0, int
       if (x >= wv) { x -= wv; ++i; }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NL; ++u) {
       if (hh[u] < 0) continue;
-      const uint32_t rm = (tabs ? rowtab[hh[u]] : tap_mask(hh[u], K, T.pad, T.stride, T.Ho)) >> kh0 & rsel;
+      const uint32_t rm = (TABS ? rowtab[hh[u]] : tap_mask(hh[u], K, T.pad, T.stride, T.Ho)) >> kh0 & rsel;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const uint32_t cm = tabs ? coltab[ww[u] + e] : tap_mask(ww[u] + e, K, T.pad, T.stride, T.Wo);
+        const uint32_t cm = TABS ? coltab[ww[u] + e] : tap_mask(ww[u] + e, K, T.pad, T.stride, T.Wo);
 #pragma unroll
         for (int r = 0; r < NKH; ++r)
 #pragma unroll
@@ -387,9 +390,13 @@ __device__ __forceinline__ void fin_window_block(const FinTask& T, int b, float 
   const int c = item / groups, kh0 = (item - c * groups) * NKH, nk = min(NKH, K - kh0);
   float acc[NKH * K];
   if (item < items) {
+    // (the tap masks come from the LDS tables unless the plane is too wide for
+    // them; each body is compiled for one of the two, which keeps the code
+    // of the common one within the instruction cache)
     const bool vec4 = (T.W & 3) == 0;   // plane starts and rows 16-byte aligned (S is 256-byte aligned)
-    if (vec4) fin_window<K, 4>(T, c, kh0, nk, tix, nthr, rowtab, coltab, tabs, acc);
-    else fin_window<K, 1>(T, c, kh0, nk, tix, nthr, rowtab, coltab, tabs, acc);
+    if (!tabs) fin_window<K, 1, false>(T, c, kh0, nk, tix, nthr, rowtab, coltab, acc);
+    else if (vec4) fin_window<K, 4, true>(T, c, kh0, nk, tix, nthr, rowtab, coltab, acc);
+    else fin_window<K, 1, true>(T, c, kh0, nk, tix, nthr, rowtab, coltab, acc);
   } else {
 #pragma unroll
     for (int t = 0; t < NKH * K; ++t) acc[t] = 0.f;
