@@ -210,10 +210,21 @@ __global__ void __launch_bounds__(kColThreads) diag_colsq_kernel(ColTasks tasks)
   }
 }
 
+// Sum over the wavefront, returned to every lane: butterflies within rows of
+// 16 lanes by DPP moves (pairs, quads, half-row and row mirrors), then the
+// four row sums by lane reads; no LDS round trips.
+template <int CTRL>
+__device__ inline float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_mov<0xb1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4e>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  const auto lane_v = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (lane_v(0) + lane_v(16)) + (lane_v(32) + lane_v(48));
 }
 
 __global__ void __launch_bounds__(kBnThreads) diag_bn_kernel(BnTasks tasks) {
