@@ -296,11 +296,15 @@ __global__ void __launch_bounds__(kBnThreads) diag_bn_kernel(BnTasks tasks) {
 // Bit t of the result is set when input row (or column) x is reached by
 // kernel row (column) t from some output position: x = o * stride + t - pad
 // with 0 <= o < n_out.
+// (y = o * stride exactly when t = (x + pad) mod stride, mod stride; one
+// division per call)
 __device__ inline uint32_t tap_mask(int x, int k, int pad, int stride, int n_out) {
+  const int base = x + pad;
+  const int64_t lim = static_cast<int64_t>(n_out) * stride;   // o < n_out
   uint32_t m = 0;
-  for (int t = 0; t < k; ++t) {
-    const int y = x + pad - t;
-    if (y >= 0 && y % stride == 0 && y / stride < n_out) m |= 1u << t;
+  for (int t = base % stride; t < k; t += stride) {
+    const int y = base - t;
+    if (y >= 0 && y < lim) m |= 1u << t;
   }
   return m;
 }
