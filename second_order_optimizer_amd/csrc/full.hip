@@ -1210,6 +1210,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   struct Progress {
     std::vector<int> pairs;   // per level: pairs done
     int rows = 0;             // rows of Z already in W
+    bool out = false;         // the inverse has been written
   };
   std::vector<Progress> prog(groups.size());
   double lau_flops = 0.0;
@@ -1336,13 +1337,13 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
       if (r == KFAC_OK && !later.empty()) r = launch_gemm(later, OP_MN, OP_MN, EPI_SUB, sc, fs, policy);
       if (r != KFAC_OK) return r;
     }
-    // output of the factors complete at R
+    // output of the factors complete at R (not yet written)
     std::vector<SymRedItem> out;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const FullPlan::Group& g = groups[gi];
       const int d = mats[g.first].d;
-      const int K = (static_cast<int>(nblk_of(d)) - 1) / kOuter;   // outer panel of its last block
-      if (R < d || (R - 1) / (kOuter * kNb) != K) continue;        // complete before this call: done then
+      if (R < d || prog[gi].out) continue;
+      prog[gi].out = true;
       for (int mi : g.members) {
         SymRedItem it{};
         it.part = P.W[mi];
@@ -1383,6 +1384,7 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   kfac_status_t r = init(2);
   if (r != KFAC_OK) return r;
   KFAC_HIP_TRY(hipEventRecord(side->main_done[1], st));
+  KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->main_done[1], 0));   // Z's band, before any assembly
   for (int K = 0; K < nouter; ++K) {
     const int k0 = K * kOuter, k1 = k0 + kOuter;   // blocks of outer panel K
     // second stream: F_next(K - 1) after F_rest(K - 2), then the inner steps
@@ -1441,11 +1443,12 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     KFAC_HIP_TRY(hipEventRecord(side->main_done[K & 1], st));
     // rows and columns of L below 512 (K + 1) are final: the inverse
     // assembly of every factor still in progress goes as far as they allow,
-    // on a third stream beside the remaining steps
+    // on a third stream beside the remaining steps, every second outer panel
+    // (fewer, larger launches: that stream is the last to finish, and its
+    // small launches cost their latency whatever their size)
     bool active = false;
     for (const FullPlan::Group& g : groups) active = active || static_cast<int>(nblk_of(mats[g.first].d)) > k0;
-    if (active) {
-      if (K == 0) KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->main_done[1], 0));   // Z's band
+    if (active && (K % 2 == 1 || K == nouter - 1)) {
       KFAC_HIP_TRY(hipStreamWaitEvent(fs, side->side_done[K & 1], 0));
       r = assemble(k1 * kNb, fs);
       if (r != KFAC_OK) return r;
