@@ -372,7 +372,8 @@ def _function_text(src, name):
     return src[m.start():]
 
 
-A7_KERNELS = ("diag_colsq_kernel", "wave_sum", "tap_mask", "fin_window", "fin_window_block", "diag_finish_kernel")
+A7_KERNELS = ("diag_colsq_kernel", "dpp_mov", "wave_sum", "tap_mask", "fin_window", "fin_window_block",
+              "diag_finish_kernel")
 
 
 def a7_source_sha256():
