@@ -341,9 +341,12 @@ __device__ __forceinline__ void fin_window(const FinTask& T, int c, int kh0, int
   // lane position (row i, load column x), stepped by nthr loads without division
   const int di = nthr / wv, dx = nthr - (nthr / wv) * wv;
   int i = tix / wv, x = tix - (tix / wv) * wv;
-  // (8 loads in flight with the tables; the rare path without them, which
-  // computes every tap mask, takes one at a time to stay small)
-  constexpr int NL = TABS ? 8 : 1;
+  // (2 loads in flight with the tables: 47 VGPRs, so 8 wavefronts per SIMD
+  // and twice the resident workgroups of 8 loads in flight (86 VGPRs), which
+  // the launch's ~2.7 rounds of short workgroups need more (19.3 -> 17.2 us);
+  // the rare path without tables, which computes every tap mask, takes one
+  // load at a time to stay small)
+  constexpr int NL = TABS ? 2 : 1;
   for (int q0 = tix; q0 < nld; q0 += NL * nthr) {
     float v[NL][VEC];
     int hh[NL], ww[NL];
