@@ -88,7 +88,7 @@ struct FinTasks {
 };
 
 constexpr int kUpdThreads = 256;
-constexpr int kUpdUnroll = 4;
+constexpr int kUpdUnroll = 2;   // float4 groups per thread (50 VGPRs: 8 wavefronts per SIMD)
 constexpr int kUpdPerBlock = kUpdThreads * 4 * kUpdUnroll;
 constexpr int kMaxSegs = 48;
 
