@@ -730,10 +730,18 @@ size_t nblk_of(int d) { return (d + kNb - 1) / kNb; }
 // contracts about kSplitRows rows, so a launch holds many workgroups of
 // similar length and tall factors (a stem convolution's 401,408 rows) do not
 // serialise it; sym_reduce_kernel adds the partial products in split order.
+// A factor of at most 4 tiles is split into pieces of 32 or more rows (up to
+// 8): its few workgroups would otherwise each run the whole contraction as
+// one serial chain of stages (FC 64 -> 32 at batch 128: factor phase 37 ->
+// 23-31 us).
 constexpr int64_t kSplitRows = 2048;
 
-int syrk_splits(int, int64_t rows) {
-  if (rows < 2 * kSplitRows) return 1;
+int syrk_splits(int d, int64_t rows) {
+  if (rows < 2 * kSplitRows) {
+    const int64_t t = (d + 127) / 128;
+    if (t * (t + 1) / 2 <= 4 && rows >= 64) return static_cast<int>(std::min<int64_t>(8, rows / 32));
+    return 1;
+  }
   return static_cast<int>(std::min<int64_t>(128, (rows + kSplitRows - 1) / kSplitRows));
 }
 

@@ -203,17 +203,20 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
                                               const float* __restrict__ r1b) {
   // Read-modify-write epilogues first issue every read of a block row (from a
   // clamped, always valid address), then compute and store: one memory round
-  // trip per block row instead of one per element.
-  // (the factor SYRK reads C in place: its EMA problems are few and the
-  // staging registers would cost the far more numerous split problems)
-  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE;
+  // trip per block row instead of one per element (a read after a store to
+  // the same array is not moved ahead of it, so reads issued element by
+  // element would each wait a full round trip).  The factor SYRK reads the
+  // old factor only for its EMA (one row split, beta != 0): upper elements,
+  // at their packed or whole position.
   const bool ema = EPI == EPI_SYRK && P.nsplit == 1;
+  const bool ema_read = ema && P.beta != 0.f;
+  constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE || EPI == EPI_SYRK;
   bool bad = false;
   // block rows by a compile-time index: a runtime one would place acc in scratch
   static_for<0, C::kBI>([&](auto si_c) {
     constexpr int si = decltype(si_c)::value;
     float c0v[C::kBJ][16], c1v[C::kBJ][16];
-    if (kReads) {
+    if (kReads && (EPI != EPI_SYRK || ema_read)) {
 #pragma unroll
       for (int sj = 0; sj < C::kBJ; ++sj) {
         const int col = j0 + wn + 32 * sj + (lane & 31);
@@ -227,6 +230,9 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
             const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
             c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
             c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
+          } else if (EPI == EPI_SYRK) {
+            const bool up = in && row <= col;
+            c0v[sj][r] = Cp[!up ? 0 : P.c_packed ? packed_index(row, col, P.M) : idx];
           } else {
             c0v[sj][r] = Cp[idx];
           }
@@ -252,7 +258,7 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
         } else if (EPI == EPI_SYRK) {
           if (row <= col) {
             const int64_t u = P.c_packed ? packed_index(row, col, P.M) : idx;
-            const float o = P.beta != 0.f ? P.beta * Cp[u] + P.alpha * v : P.alpha * v;
+            const float o = ema_read ? P.beta * c0v[sj][r] + P.alpha * v : P.alpha * v;
             Cp[u] = o;
             if (row != col && !P.c_packed) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
