@@ -332,6 +332,15 @@ __device__ inline void mma_nn(f32x16& acc, const float* X, int ar, int ac, const
   }
 }
 
+// acc += A^T B with A = X[ar.., ac..], B = Y[br.., bc..] (32 x 32 each, pitch kLd)
+__device__ inline void mma_tn(f32x16& acc, const float* X, int ar, int ac, const float* Y, int br, int bc, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 32; kk += 2) {
+    const int k = kk + (lane >> 5);
+    acc = mfma32(X[(ar + k) * kLd + ac + (lane & 31)], Y[(br + k) * kLd + bc + (lane & 31)], acc);
+  }
+}
+
 // accumulator r of lane l is element (8 (r/4) + 4 (l/32) + r%4, l%32) of the tile
 __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
@@ -358,7 +367,7 @@ __device__ inline void tile_store_t(float* S, int ld, int r0, int c0, const f32x
 // is u_r by symmetry, so the lanes exchange u through the 64 floats at Us:
 // each writes its entry, then all read it back with broadcast 16-byte reads
 // (no cross-lane register moves).
-__device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, float* Us, int c0, const DMat& M,
+__device__ __attribute__((always_inline)) inline bool factor_diag32(float* Ms, float* Us, int c0, int32_t* fail,
                                                                    uint32_t* flags, int lane) {
   const int c = lane & 31;
   const bool xl = lane >= 32;
@@ -422,8 +431,8 @@ __device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, f
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (bad && lane == 0 && *M.fail == 0) {
-    *M.fail = 1;
+  if (bad && lane == 0 && *fail == 0) {
+    *fail = 1;
     raise_flag(flags, KFAC_FLAG_NOT_PD);
   }
   // row scales 1 / sqrt(d_r): lane c computes its own pivot's (dmine) and
@@ -437,6 +446,67 @@ __device__ __attribute__((always_inline)) inline void factor_diag32(float* Ms, f
     // (L^-1)_rc = X_rc / sqrt(d_r)
 #pragma unroll
     for (int r = 0; r < 32; ++r) Ms[(c0 + r) * kLd + c0 + c] = r >= c ? v[r] * rs[r] : 0.f;
+  }
+  return bad;   // (the same in every lane: all of them read the same pivots)
+}
+
+// Cholesky and inverse of the symmetric working block in Ms (pitch kLd; bk
+// rows and columns hold the matrix, the rest an identity), by 32-column
+// sub-blocks; on return Ms holds Z = L^-1 with its diagonal blocks in place
+// (zero above their diagonal) and its off-diagonal blocks transposed above
+// the diagonal.  A failed pivot also sets *sbad (in LDS; when not null).
+// Returns with the workgroup synchronised.
+__device__ __forceinline__ void factor_invert_block(float* Ms, float* Us, int bk, int32_t* fail, uint32_t* flags,
+                                                    int* sbad, int lane, int wid) {
+  // Only the first np 32-column sub-blocks hold the factor (bk rows); the
+  // rest of the working block is identity, is never read by them and is not
+  // written out, so a ragged last block skips it.
+  const int np = (bk + 31) / 32;
+  for (int p = 0; p < np; ++p) {
+    const int c0 = 32 * p;
+    if (wid == 0) {
+      const bool bad = factor_diag32(Ms, Us, c0, fail, flags, lane);
+      if (bad && sbad != nullptr && lane == 0) *sbad = 1;
+    }
+    __syncthreads();
+    // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
+    if (wid < np - 1 - p) {
+      const int q = p + 1 + wid;
+      f32x16 acc = {};
+      mma_nt(acc, Ms, 32 * q, c0, Ms, c0, c0, 1.f, lane);
+      tile_store(Ms, kLd, 32 * q, c0, acc, 1.f, lane);
+    }
+    __syncthreads();
+    // trailing lower tiles (ib, jb), p < jb <= ib: M_ij -= L_ip L_jp^T
+    const int nr = np - 1 - p;
+    for (int t = wid; t < nr * (nr + 1) / 2; t += 4) {
+      int ib = 0, u = t;
+      while (u > ib) { u -= ib + 1; ++ib; }
+      const int I = 32 * (p + 1 + ib), J = 32 * (p + 1 + u);
+      f32x16 acc;
+      tile_load(acc, Ms, kLd, I, J, lane);
+      mma_nt(acc, Ms, I, c0, Ms, J, c0, -1.f, lane);
+      tile_store(Ms, kLd, I, J, acc, 1.f, lane);
+    }
+    __syncthreads();
+  }
+
+  // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj, with
+  // Z_mj (m > j) held transposed at block (j, m); the sum is staged, also
+  // transposed, at block (j, i), where Z_ij then goes (wavefront j alone
+  // touches that block in this row)
+  for (int i = 1; i < np; ++i) {
+    if (wid < i) {
+      const int j = wid;
+      f32x16 acc = {};
+      mma_nn(acc, Ms, 32 * i, 32 * j, Ms, kLd, 32 * j, 32 * j, lane);
+      for (int m = j + 1; m < i; ++m) mma_nt(acc, Ms, 32 * i, 32 * m, Ms, 32 * j, 32 * m, 1.f, lane);
+      tile_store_t(Ms, kLd, 32 * j, 32 * i, acc, 1.f, lane);
+      f32x16 z = {};
+      mma_nt(z, Ms, 32 * i, 32 * i, Ms, 32 * j, 32 * i, 1.f, lane);
+      tile_store_t(Ms, kLd, 32 * j, 32 * i, z, -1.f, lane);
+    }
+    __syncthreads();
   }
 }
 
@@ -496,53 +566,7 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
   }
   __syncthreads();
 
-  // Only the first np 32-column sub-blocks hold the factor (bk rows); the
-  // rest of the working block is identity, is never read by them and is not
-  // written out, so a ragged last block skips it.
-  const int np = (bk + 31) / 32;
-  for (int p = 0; p < np; ++p) {
-    const int c0 = 32 * p;
-    if (wid == 0) factor_diag32(Ms, Us, c0, M, T.flags, lane);
-    __syncthreads();
-    // panel below the diagonal sub-block: L_qp = M_qp Z_pp^T
-    if (wid < np - 1 - p) {
-      const int q = p + 1 + wid;
-      f32x16 acc = {};
-      mma_nt(acc, Ms, 32 * q, c0, Ms, c0, c0, 1.f, lane);
-      tile_store(Ms, kLd, 32 * q, c0, acc, 1.f, lane);
-    }
-    __syncthreads();
-    // trailing lower tiles (ib, jb), p < jb <= ib: M_ij -= L_ip L_jp^T
-    const int nr = np - 1 - p;
-    for (int t = wid; t < nr * (nr + 1) / 2; t += 4) {
-      int ib = 0, u = t;
-      while (u > ib) { u -= ib + 1; ++ib; }
-      const int I = 32 * (p + 1 + ib), J = 32 * (p + 1 + u);
-      f32x16 acc;
-      tile_load(acc, Ms, kLd, I, J, lane);
-      mma_nt(acc, Ms, I, c0, Ms, J, c0, -1.f, lane);
-      tile_store(Ms, kLd, I, J, acc, 1.f, lane);
-    }
-    __syncthreads();
-  }
-
-  // inverse by block rows: Z_ij = -Z_ii sum_{j <= m < i} L_im Z_mj, with
-  // Z_mj (m > j) held transposed at block (j, m); the sum is staged, also
-  // transposed, at block (j, i), where Z_ij then goes (wavefront j alone
-  // touches that block in this row)
-  for (int i = 1; i < np; ++i) {
-    if (wid < i) {
-      const int j = wid;
-      f32x16 acc = {};
-      mma_nn(acc, Ms, 32 * i, 32 * j, Ms, kLd, 32 * j, 32 * j, lane);
-      for (int m = j + 1; m < i; ++m) mma_nt(acc, Ms, 32 * i, 32 * m, Ms, 32 * j, 32 * m, 1.f, lane);
-      tile_store_t(Ms, kLd, 32 * j, 32 * i, acc, 1.f, lane);
-      f32x16 z = {};
-      mma_nt(z, Ms, 32 * i, 32 * i, Ms, 32 * j, 32 * i, 1.f, lane);
-      tile_store_t(Ms, kLd, 32 * j, 32 * i, z, -1.f, lane);
-    }
-    __syncthreads();
-  }
+  factor_invert_block(Ms, Us, bk, M.fail, T.flags, nullptr, lane, wid);
 
   // write back Dinv[k] and Z_kk (L_kk itself is not read again: the panel
   // below it is formed with Dinv[k]); thread t writes quad t % 32 of rows
@@ -573,6 +597,86 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(DiagTab T) {
         }
       }
     }
+  }
+}
+
+// A factor of at most 128 rows and columns in one launch: the working block
+// is F's upper triangle plus the damping on the diagonal (read directly, no
+// separate initialisation), factored and inverted as above, and the damped
+// inverse (L L^T)^-1 = Z^T Z formed on MFMA from Ms's Z and written whole
+// (both triangles) unless a pivot failed.  One workgroup per factor.  With
+// 32-blocks Z_ab of Z (block row a, block column b) and m >= max(a, b):
+// W_ab = sum_m Z_ma^T Z_mb, where for a <= b the term m = b is Z_ab'^T Z_bb
+// (a < b: Z_ba^T is the stored block (a, b); a = b: the diagonal block
+// itself, transposed) and every m > b is (stored (a, m)) (stored (b, m))^T.
+__global__ void __launch_bounds__(256) chol_small_kernel(MatTab T) {
+  __shared__ __attribute__((aligned(16))) float Ms[kNb * kLd];
+  __shared__ __attribute__((aligned(16))) float Us[64];
+  __shared__ int sbad;
+  const Mat& M = T.m[blockIdx.x];
+  const int d = M.d;   // <= kNb
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid == 0) {
+    *M.fail = 0;
+    sbad = 0;
+  }
+  for (int e = tid; e < kNb * kLd; e += 256) Ms[e] = (e / kLd == e % kLd) ? 1.f : 0.f;
+  __syncthreads();
+  // upper elements (r, c), c >= r, mirrored; 32 loads in flight per thread
+  const int ne = d * d;
+  for (int e0 = 0; e0 < ne; e0 += 32 * 256) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int r = e / d, c = e - r * d;
+      const bool up = e < ne && c >= r;
+      v[u] = up ? M.F[M.packed ? packed_index(r, c, d) : static_cast<int64_t>(e)] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int r = e / d, c = e - r * d;
+      if (e < ne && c >= r) {
+        const float x = r == c ? v[u] + T.damping : v[u];
+        Ms[r * kLd + c] = x;
+        Ms[c * kLd + r] = x;
+      }
+    }
+  }
+  __syncthreads();
+  factor_invert_block(Ms, Us, d, M.fail, T.flags, &sbad, lane, wid);
+
+  // W's upper 32-blocks (a, b), b-major: at most 10, so 3 per wavefront
+  const int np = (d + 31) / 32;
+  const int nw = np * (np + 1) / 2;
+  f32x16 w[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int t = wid + 4 * s;
+    w[s] = f32x16{};
+    if (t >= nw) continue;
+    int b = 0, a = t;
+    while (a > b) { a -= b + 1; ++b; }
+    if (a == b) mma_tn(w[s], Ms, 32 * b, 32 * b, Ms, 32 * b, 32 * b, lane);
+    else mma_nn(w[s], Ms, 32 * a, 32 * b, Ms, kLd, 32 * b, 32 * b, lane);
+    for (int m = b + 1; m < np; ++m) mma_nt(w[s], Ms, 32 * a, 32 * m, Ms, 32 * b, 32 * m, 1.f, lane);
+  }
+  __syncthreads();   // every read of Z done: W replaces it in Ms
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int t = wid + 4 * s;
+    if (t >= nw) continue;
+    int b = 0, a = t;
+    while (a > b) { a -= b + 1; ++b; }
+    tile_store(Ms, kLd, 32 * a, 32 * b, w[s], 1.f, lane);
+    if (a != b) tile_store_t(Ms, kLd, 32 * b, 32 * a, w[s], 1.f, lane);
+  }
+  __syncthreads();
+  if (sbad != 0) return;   // a failed factor keeps its previous inverse
+  for (int e = tid; e < ne; e += 256) {
+    const int r = e / d, c = e - r * d;
+    M.Finv[e] = Ms[r * kLd + c];
   }
 }
 
@@ -1367,12 +1471,12 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
     return out.empty() ? KFAC_OK : launch_sym_reduce(out, fs);
   };
   if (nblk_max == 1) {
-    // every factor is one diagonal block: no chain to overlap, so the same
-    // launches run in order on the caller's stream (no fork, no events)
-    r = init(0);
-    if (r == KFAC_OK) r = diag_step(0, st);
-    if (r != KFAC_OK) return r;
-    return assemble(d_all, st);
+    // every factor is one diagonal block: one launch per kMaxMats factors
+    // reads, factors, inverts and writes them (no chain, no fork, no events)
+    return tables([](const Mat&) { return true; }, 0, [&](MatTab& T) {
+      hipLaunchKernelGGL(chol_small_kernel, dim3(T.n), dim3(256), 0, st, T);
+      return hipGetLastError() == hipSuccess ? KFAC_OK : KFAC_ERR_HIP;
+    });
   }
   hipStream_t fs = side->f;
   // the chain starts once the first outer panel is initialised; the rest of
