@@ -1576,8 +1576,188 @@ kfac_status_t invert_phase(const kfac_hparams_t& hp, const FullPlan& P, uint32_t
   return joined ? KFAC_OK : KFAC_ERR_HIP;
 }
 
+// Preconditioning and update of layers with d_out <= 128 and d_a <= 128, one
+// workgroup per layer: [grad_w | grad_b] and A_inv into LDS together, T =
+// their product on MFMA (kept in LDS), G_inv in, P = G_inv T on MFMA, then the
+// update of the GEMM path's fused epilogue (D = P + wd W; V = mu V + D;
+// W -= lr V, the bias column included; a non-finite result raises
+// KFAC_FLAG_NONFINITE).  Used when every layer of the step is that small: the
+// two GEMM launches would otherwise each run a serial chain of stages per
+// layer.  Both LDS arrays are zero outside the matrices, so the 32-blocks
+// that straddle d_out or d_a contract over zeros.
+constexpr int kMaxSmallUpd = 40;
+struct SmallUpd {
+  const float* gw;     // grad_w [d_out][d_in]
+  const float* gb;     // grad_b [d_out], null without a bias
+  const float* Ainv;   // [d_a][d_a]
+  const float* Ginv;   // [d_out][d_out]
+  float* W;
+  float* b;
+  float* V;
+  float* Vb;
+  int32_t d_out, d_in;
+};
+struct SmallUpdTab {
+  SmallUpd u[kMaxSmallUpd];
+  int32_t n;
+  float lr, momentum, weight_decay;
+  uint32_t* flags;
+};
+static_assert(sizeof(SmallUpdTab) <= 4096, "kernel arguments");
+
+__global__ void __launch_bounds__(256) precond_small_kernel(SmallUpdTab T) {
+  __shared__ __attribute__((aligned(16))) float X[kNb * kLd];   // [grad_w | grad_b], then T
+  __shared__ __attribute__((aligned(16))) float Y[kNb * kLd];   // A_inv, then G_inv
+  const SmallUpd& U = T.u[blockIdx.x];
+  const int mo = U.d_out, di = U.d_in, da = di + (U.gb != nullptr ? 1 : 0);
+  if (mo <= 0 || da <= 0) return;   // (uniform: nothing to update)
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nbi = (mo + 31) / 32, nbj = (da + 31) / 32;
+  for (int e = tid; e < kNb * kLd; e += 256) {
+    X[e] = 0.f;
+    Y[e] = 0.f;
+  }
+  __syncthreads();
+  // [grad_w | grad_b] (mo x da) and A_inv (da x da), 32 loads in flight per thread
+  const int n1 = mo * da, n12 = n1 + da * da;
+  for (int e0 = 0; e0 < n12; e0 += 32 * 256) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int f = e < n1 ? e : e - n1;
+      const int r = f / da, c = f - r * da;
+      const float* src = e < n1 ? (c < di ? U.gw + static_cast<int64_t>(r) * di + c : U.gb + r) : U.Ainv + f;
+      v[u] = e < n12 ? *src : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int f = e < n1 ? e : e - n1;
+      const int r = f / da, c = f - r * da;
+      if (e < n12) (e < n1 ? X : Y)[r * kLd + c] = v[u];
+    }
+  }
+  __syncthreads();
+  // T = [grad_w | grad_b] A_inv: (mo x da) blocks, at most 16, 4 per wavefront
+  const int nt = nbi * nbj;
+  f32x16 acc[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int t = wid + 4 * s;
+    acc[s] = f32x16{};
+    if (t >= nt) continue;
+    const int i = t / nbj, j = t - (t / nbj) * nbj;
+    for (int kb = 0; kb < nbj; ++kb) mma_nn(acc[s], X, 32 * i, 32 * kb, Y, kLd, 32 * kb, 32 * j, lane);
+  }
+  __syncthreads();   // every read of X and Y done
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int t = wid + 4 * s;
+    if (t >= nt) continue;
+    const int i = t / nbj, j = t - (t / nbj) * nbj;
+    tile_store(X, kLd, 32 * i, 32 * j, acc[s], 1.f, lane);
+  }
+  // G_inv over the blocks that P reads (rows and columns below 32 nbi; zero
+  // beyond mo, where A_inv's entries were)
+  const int gw = 32 * nbi, ng = gw * gw;
+  for (int e0 = 0; e0 < ng; e0 += 32 * 256) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int r = e / gw, c = e - r * gw;
+      v[u] = (e < ng && r < mo && c < mo) ? U.Ginv[r * mo + c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + u * 256 + tid;
+      const int r = e / gw, c = e - r * gw;
+      if (e < ng) Y[r * kLd + c] = v[u];
+    }
+  }
+  __syncthreads();
+  // P = G_inv T, then the update, block by block (reads of a block issued together)
+  bool bad = false;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int t = wid + 4 * s;
+    if (t >= nt) continue;
+    const int i = t / nbj, j = t - (t / nbj) * nbj;
+    f32x16 pacc = {};
+    for (int kb = 0; kb < nbi; ++kb) mma_nn(pacc, Y, 32 * i, 32 * kb, X, kLd, 32 * kb, 32 * j, lane);
+    const int col = 32 * j + (lane & 31);
+    float w0[16], v0[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * i + acc_row(r, lane);
+      const bool in = row < mo && col < da;
+      const int64_t e = static_cast<int64_t>(row) * di + col;
+      // (outside the layer: the first weight, or the first bias when d_in = 0)
+      const bool wsel = in ? col < di : di > 0;
+      const int64_t off = in ? (col < di ? e : row) : 0;
+      w0[r] = (wsel ? U.W : U.b)[off];
+      v0[r] = (wsel ? U.V : U.Vb)[off];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * i + acc_row(r, lane);
+      if (row >= mo || col >= da) continue;
+      const float d = fmaf(T.weight_decay, w0[r], pacc[r]);
+      const float vn = fmaf(T.momentum, v0[r], d);
+      const float wn = fmaf(-T.lr, vn, w0[r]);
+      if (col < di) {
+        U.V[static_cast<int64_t>(row) * di + col] = vn;
+        U.W[static_cast<int64_t>(row) * di + col] = wn;
+      } else {
+        U.Vb[row] = vn;
+        U.b[row] = wn;
+      }
+      bad |= !(isfinite(vn) && isfinite(wn));
+    }
+  }
+  if (__any(bad) && lane == 0) raise_flag(T.flags, KFAC_FLAG_NONFINITE);
+}
+
 kfac_status_t update_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                            uint32_t* flags, hipStream_t st, SideStream* side) {
+  // every layer within one 128 x 128 block: one workgroup per layer
+  bool small = n > 0;
+  for (int li = 0; li < n && small; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    small = g.d_out <= kNb && g.d_a <= kNb;
+  }
+  if (small) {
+    SmallUpdTab T{};
+    T.lr = hp.lr;
+    T.momentum = hp.momentum;
+    T.weight_decay = hp.weight_decay;
+    T.flags = flags;
+    for (int li = 0; li <= n; ++li) {
+      if (li == n || T.n == kMaxSmallUpd) {
+        if (T.n > 0) {
+          hipLaunchKernelGGL(precond_small_kernel, dim3(T.n), dim3(256), 0, st, T);
+          KFAC_HIP_TRY(hipGetLastError());
+        }
+        T.n = 0;
+        if (li == n) break;
+      }
+      const kfac_layer_t& L = layers[li];
+      const LayerGeom g = geom_of(L);
+      SmallUpd& u = T.u[T.n++];
+      u.gw = L.grad_w;
+      u.gb = g.bias ? L.grad_b : nullptr;
+      u.Ainv = L.A_inv;
+      u.Ginv = L.G_inv;
+      u.W = L.w;
+      u.b = L.b;
+      u.V = L.mom_w;
+      u.Vb = L.mom_b;
+      u.d_out = g.d_out;
+      u.d_in = g.d_in;
+    }
+    return KFAC_OK;
+  }
   std::vector<GemmProb> g1, g2;
   std::vector<BcProb> b0, b1;
   auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
