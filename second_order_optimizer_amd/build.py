@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops off: plain fp32 vector code, no packed-fp32 instructions.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+             "-Wall", "-Werror=uninitialized", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
 def _run(cmd, verbose):

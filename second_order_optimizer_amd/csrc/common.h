@@ -29,6 +29,17 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Sets `bits` in the workspace flag word.  Called by one lane.
 __device__ inline void raise_flag(uint32_t* flags, uint32_t bits) { atomicOr(flags, bits); }
 
+// A (workgroup-uniform) kernel-argument value held in a scalar register for
+// the rest of the kernel.  The compiler otherwise treats argument loads as
+// free to repeat and re-reads a table entry's fields at each use, each read
+// waited for on its own: a serial chain of scalar-memory round trips, most
+// costly in epilogues, where every wavefront of a workgroup runs it at once.
+template <typename T>
+__device__ inline T arg_reg(T v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
 // Packed upper-triangle storage of a symmetric d x d factor: element (i, j),
 // i <= j, at i d - i (i - 1) / 2 + (j - i) (rows of the upper triangle one
 // after the other).

@@ -974,9 +974,158 @@ kfac_status_t launch_sym_reduce(const std::vector<SymRedItem>& items, hipStream_
 // launch), then every fp32 factor of the stack in batched row-major SYRK
 // launches (direct EMA, or split rows summed by the batched reduce
 // afterwards), and the bf16 factors on the bf16 SYRK.
+// Factor and EMA of fp32 linear-layer factors at most 128 wide, one
+// workgroup per factor: X (plus the bias layer's constant-1 column, 1 on real
+// rows only) goes through LDS in chunks of kSmallRows rows, the next chunk's
+// loads in flight while the current one is contracted; each wavefront owns
+// whole upper 32-blocks of X^T X (at most 10, so 3 each) and runs every row
+// for them, so no partial sums are combined; then F <- beta F + alpha X^T X
+// on the upper triangle (mirrored, or packed).  Used when every factor of the
+// step qualifies: the general path's split SYRK and reduction are two
+// launches whose workgroups each walk a chain of stages.
+constexpr int kMaxSmallSyrk = 48;
+constexpr int kSmallRows = 64;                // rows of X per chunk
+constexpr int kSmallPitch = kNb + 4;          // LDS row of a chunk (floats)
+constexpr int64_t kSmallMaxRows = 8192;       // one workgroup contracts every row
+struct SmallSyrk {
+  const float* X;    // [rows][w] row-major
+  float* F;          // d x d (d = w + bias), whole or packed upper triangle
+  int32_t rows, w, bias, packed;
+  float alpha, beta;
+};
+struct SmallSyrkTab {
+  SmallSyrk s[kMaxSmallSyrk];
+  int32_t n;
+};
+static_assert(sizeof(SmallSyrkTab) <= 4096, "kernel arguments");
+
+__global__ void __launch_bounds__(256) syrk_small_kernel(SmallSyrkTab T) {
+  __shared__ __attribute__((aligned(16))) float Xs[kSmallRows * kSmallPitch];
+  // the table entry read once, kept in registers
+  const SmallSyrk& S = T.s[blockIdx.x];
+  const float* X = arg_reg(S.X);
+  float* F = arg_reg(S.F);
+  const int w = arg_reg(S.w), bias = arg_reg(S.bias), rows = arg_reg(S.rows), packed = arg_reg(S.packed);
+  const float alpha = arg_reg(S.alpha), beta = arg_reg(S.beta);
+  const int d = w + bias;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nb = (d + 31) / 32, nu = nb * (nb + 1) / 2;
+  // this wavefront's blocks (a, b), a <= b, b-major: t = wid, wid + 4, wid + 8
+  int ba[3], bb[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    int b = 0, a = wid + 4 * s;
+    while (a > b) { a -= b + 1; ++b; }
+    ba[s] = a;
+    bb[s] = b;
+  }
+  f32x16 acc[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) acc[s] = f32x16{};
+  // chunk loads: thread t takes column t % 128 of chunk rows t / 128 + 2 u
+  constexpr int kPer = kSmallRows / 2;   // 32
+  const int cc = tid & (kNb - 1), rr = tid >> 7;
+  float v[kPer];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = r0 + rr + 2 * u;
+      v[u] = (cc < w && r < rows) ? X[static_cast<int64_t>(r) * w + cc] : 0.f;
+    }
+  };
+  const int nch = (rows + kSmallRows - 1) / kSmallRows;
+  load(0);
+  for (int ch = 0; ch < nch; ++ch) {
+    const int r0 = ch * kSmallRows;
+    __syncthreads();   // the previous chunk is no longer read
+    // columns up to the last 32-block: X, the bias column (1 on real rows), zeros
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = rr + 2 * u;
+      const float one = (bias && cc == w && r0 + r < rows) ? 1.f : 0.f;
+      if (cc < 32 * nb) Xs[r * kSmallPitch + cc] = cc < w ? v[u] : one;
+    }
+    __syncthreads();
+    if (ch + 1 < nch) load(r0 + kSmallRows);
+    // every row pair of the chunk (rows past the end are zero)
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      if (wid + 4 * s >= nu) continue;
+      const int ca = 32 * ba[s] + (lane & 31), cb = 32 * bb[s] + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < kSmallRows; kk += 2) {
+        const int k = kk + (lane >> 5);
+        acc[s] = mfma32(Xs[k * kSmallPitch + ca], Xs[k * kSmallPitch + cb], acc[s]);
+      }
+    }
+  }
+  // F <- beta F + alpha acc on the upper triangle; a block's reads issued together
+  const bool rd = beta != 0.f;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (wid + 4 * s >= nu) continue;
+    const int col = 32 * bb[s] + (lane & 31);
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * ba[s] + acc_row(r, lane);
+      const bool up = row <= col && col < d;
+      const int64_t f = !up ? 0 : packed ? packed_index(row, col, d) : static_cast<int64_t>(row) * d + col;
+      o[r] = rd ? F[f] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * ba[s] + acc_row(r, lane);
+      if (row > col || col >= d) continue;
+      const float x = rd ? beta * o[r] + alpha * acc[s][r] : alpha * acc[s][r];
+      if (packed) {
+        F[packed_index(row, col, d)] = x;
+      } else {
+        F[static_cast<int64_t>(row) * d + col] = x;
+        if (row != col) F[static_cast<int64_t>(col) * d + row] = x;
+      }
+    }
+  }
+}
+
 kfac_status_t factors_phase(const kfac_layer_t* layers, int n, const kfac_hparams_t& hp, const FullPlan& P,
                             hipStream_t st) {
   const float eps = hp.ema_decay;
+  // every factor fp32, of a linear layer and at most 128 wide: one workgroup per factor
+  bool small = n > 0;
+  for (int li = 0; li < n && small; ++li) {
+    const LayerGeom g = geom_of(layers[li]);
+    small = !g.conv && g.d_a <= kNb && g.d_out <= kNb && g.rows <= kSmallMaxRows &&
+            fp32_factor(layers[li], 0) && fp32_factor(layers[li], 1);
+  }
+  if (small) {
+    SmallSyrkTab T{};
+    for (int li = 0; li < n; ++li) {
+      const kfac_layer_t& L = layers[li];
+      const LayerGeom g = geom_of(L);
+      for (int which = 0; which < 2; ++which) {
+        if (T.n == kMaxSmallSyrk) {
+          hipLaunchKernelGGL(syrk_small_kernel, dim3(T.n), dim3(256), 0, st, T);
+          KFAC_HIP_TRY(hipGetLastError());
+          T.n = 0;
+        }
+        SmallSyrk& q = T.s[T.n++];
+        q.X = static_cast<const float*>(which == 0 ? L.a : L.g);
+        q.F = which == 0 ? L.A : L.G;
+        q.rows = static_cast<int32_t>(g.rows);
+        q.w = which == 0 ? g.d_in : g.d_out;
+        q.bias = which == 0 && g.bias ? 1 : 0;
+        q.packed = g.packed ? 1 : 0;
+        q.alpha = (1.0f - eps) / static_cast<float>(g.rows);
+        q.beta = eps;
+      }
+    }
+    if (T.n > 0) {
+      hipLaunchKernelGGL(syrk_small_kernel, dim3(T.n), dim3(256), 0, st, T);
+      KFAC_HIP_TRY(hipGetLastError());
+    }
+    return KFAC_OK;
+  }
   std::vector<GemmProb> probs;
   std::vector<SymRedItem> reds;
   std::vector<SyrkBf16Prob> bf16;

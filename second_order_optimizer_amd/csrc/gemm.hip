@@ -170,6 +170,51 @@ __device__ inline void store_slab(float* __restrict__ s, const SlabRegs<BIG, TK>
   }
 }
 
+// The problem entry a workgroup works on, read once from the kernel arguments
+// and kept in scalar registers (see arg_reg).  The fused-update kernels read
+// it in place: any copy of the entry pushes their 256 x 256 instantiation past
+// 256 VGPRs (68 bytes of scratch per lane).
+template <int EPI>
+__device__ inline std::conditional_t<EPI == EPI_UPDATE, const GemmProb&, GemmProb> prob_regs(const GemmProb& P) {
+  if constexpr (EPI == EPI_UPDATE) return P;
+  else {
+  GemmProb q;
+  q.A = arg_reg(P.A);
+  q.B = arg_reg(P.B);
+  q.C = arg_reg(P.C);
+  q.A_extra = arg_reg(P.A_extra);
+  q.W = arg_reg(P.W);
+  q.Wb = arg_reg(P.Wb);
+  q.V = arg_reg(P.V);
+  q.Vb = arg_reg(P.Vb);
+  q.split_stride = arg_reg(P.split_stride);
+  q.lda = arg_reg(P.lda);
+  q.ldb = arg_reg(P.ldb);
+  q.ldc = arg_reg(P.ldc);
+  q.M = arg_reg(P.M);
+  q.N = arg_reg(P.N);
+  q.kb = arg_reg(P.kb);
+  q.ke = arg_reg(P.ke);
+  q.tiles_m = arg_reg(P.tiles_m);
+  q.tiles_n = arg_reg(P.tiles_n);
+  q.a_special = arg_reg(P.a_special);
+  q.b_special = arg_reg(P.b_special);
+  q.d_in = arg_reg(P.d_in);
+  q.nsplit = arg_reg(P.nsplit);
+  q.blk_begin = arg_reg(P.blk_begin);
+  q.nbatch = static_cast<int16_t>(arg_reg(static_cast<int32_t>(P.nbatch)));
+  q.tri = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.tri)));
+  q.krange = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.krange)));
+  q.a_vec = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.a_vec)));
+  q.b_vec = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.b_vec)));
+  q.c_packed = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.c_packed)));
+  q.nchw = static_cast<uint8_t>(arg_reg(static_cast<uint32_t>(P.nchw)));
+  q.alpha = arg_reg(P.alpha);
+  q.beta = arg_reg(P.beta);
+  return q;
+  }
+}
+
 __device__ inline void tile_coords(const GemmProb& P, int t, int& split, int& ti, int& tj) {
   int per;
   if (P.tri == TRI_FULL) per = P.tiles_m * P.tiles_n;
@@ -210,8 +255,55 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
   // at their packed or whole position.
   const bool ema = EPI == EPI_SYRK && P.nsplit == 1;
   const bool ema_read = ema && P.beta != 0.f;
+  const float wd = batch.sc.weight_decay, mom = batch.sc.momentum, lr = batch.sc.lr;
+  // the update's targets and extent, read once here (after the main loop, so
+  // that they hold no registers there)
+  float* const uW = EPI == EPI_UPDATE ? arg_reg(P.W) : nullptr;
+  float* const uWb = EPI == EPI_UPDATE ? arg_reg(P.Wb) : nullptr;
+  float* const uV = EPI == EPI_UPDATE ? arg_reg(P.V) : nullptr;
+  float* const uVb = EPI == EPI_UPDATE ? arg_reg(P.Vb) : nullptr;
+  const int ud_in = EPI == EPI_UPDATE ? arg_reg(P.d_in) : 0;
+  const int uM = EPI == EPI_UPDATE ? arg_reg(P.M) : P.M;
+  const int uN = EPI == EPI_UPDATE ? arg_reg(P.N) : P.N;
   constexpr bool kReads = EPI == EPI_SUB || EPI == EPI_UPDATE || EPI == EPI_SYRK;
   bool bad = false;
+  if constexpr (EPI == EPI_UPDATE) {
+    // one 32 x 32 block at a time (its 32 reads together): staging a whole
+    // block row would take this epilogue past 256 VGPRs
+    static_for<0, C::kBI>([&](auto si_c) {
+      constexpr int si = decltype(si_c)::value;
+#pragma unroll
+      for (int sj = 0; sj < C::kBJ; ++sj) {
+        const int col = j0 + wn + 32 * sj + (lane & 31);
+        float w0[16], v0[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const bool in = row < uM && col < uN;
+          const bool wcol = !in || col < ud_in;
+          const int64_t e = in ? static_cast<int64_t>(row) * ud_in + col : 0;
+          w0[r] = wcol ? uW[e] : uWb[row];
+          v0[r] = wcol ? uV[e] : uVb[row];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= uM || col >= uN) continue;
+          const bool wcol = col < ud_in;
+          float* wp = wcol ? uW + static_cast<int64_t>(row) * ud_in + col : uWb + row;
+          float* vp = wcol ? uV + static_cast<int64_t>(row) * ud_in + col : uVb + row;
+          const float d = fmaf(wd, w0[r], acc[si][sj][r]);
+          const float vn = fmaf(mom, v0[r], d);
+          const float wn2 = fmaf(-lr, vn, w0[r]);
+          *vp = vn;
+          *wp = wn2;
+          bad |= !(isfinite(vn) && isfinite(wn2));
+        }
+      }
+    });
+    if (__any(bad) && lane == 0) raise_flag(batch.sc.flags, KFAC_FLAG_NONFINITE);
+    return;
+  }
   // block rows by a compile-time index: a runtime one would place acc in scratch
   static_for<0, C::kBI>([&](auto si_c) {
     constexpr int si = decltype(si_c)::value;
@@ -223,13 +315,13 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const bool in = row < P.M && col < P.N;
+          const bool in = row < uM && col < uN;
           const int64_t idx = in ? static_cast<int64_t>(row) * P.ldc + col : 0;
           if (EPI == EPI_UPDATE) {
-            const bool wcol = !in || col < P.d_in;
-            const int64_t e = in ? static_cast<int64_t>(row) * P.d_in + col : 0;
-            c0v[sj][r] = wcol ? P.W[e] : P.Wb[row];
-            c1v[sj][r] = wcol ? P.V[e] : P.Vb[row];
+            const bool wcol = !in || col < ud_in;
+            const int64_t e = in ? static_cast<int64_t>(row) * ud_in + col : 0;
+            c0v[sj][r] = wcol ? uW[e] : uWb[row];
+            c1v[sj][r] = wcol ? uV[e] : uVb[row];
           } else if (EPI == EPI_SYRK) {
             const bool up = in && row <= col;
             c0v[sj][r] = Cp[!up ? 0 : P.c_packed ? packed_index(row, col, P.M) : idx];
@@ -245,7 +337,7 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + wm + 32 * si + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= P.M || col >= P.N) continue;
+        if (row >= uM || col >= uN) continue;
         float v = acc[si][sj][r];
         if (EPI == EPI_STORE && r1a != nullptr) v = fmaf(r1a[row], r1b[col], v);
         const int64_t idx = static_cast<int64_t>(row) * P.ldc + col;
@@ -263,13 +355,13 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
             if (row != col && !P.c_packed) Cp[static_cast<int64_t>(col) * P.ldc + row] = o;
           }
         } else if (EPI == EPI_UPDATE) {
-          const bool wcol = col < P.d_in;
-          float* wp = wcol ? P.W + static_cast<int64_t>(row) * P.d_in + col : P.Wb + row;
-          float* vp = wcol ? P.V + static_cast<int64_t>(row) * P.d_in + col : P.Vb + row;
+          const bool wcol = col < ud_in;
+          float* wp = wcol ? uW + static_cast<int64_t>(row) * ud_in + col : uWb + row;
+          float* vp = wcol ? uV + static_cast<int64_t>(row) * ud_in + col : uVb + row;
           const float w = c0v[sj][r];
-          const float d = fmaf(batch.sc.weight_decay, w, v);
-          const float vn = fmaf(batch.sc.momentum, c1v[sj][r], d);
-          const float wn2 = fmaf(-batch.sc.lr, vn, w);
+          const float d = fmaf(wd, w, v);
+          const float vn = fmaf(mom, c1v[sj][r], d);
+          const float wn2 = fmaf(-lr, vn, w);
           *vp = vn;
           *wp = wn2;
           bad |= !(isfinite(vn) && isfinite(wn2));
@@ -288,6 +380,8 @@ __device__ __forceinline__ void gemm_f32_body(const Batch& batch) {
   using C = Cfg<BIG, TK>;
   __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
   __shared__ __attribute__((aligned(16))) float sB[2][C::kSlab];
+  // (read in place: a register-held entry measured 25-40% slower here, in
+  // these kernels' latency-bound inverse launches)
   const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
@@ -495,7 +589,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 gemm_f32_dma_kernel(GemmBatch batch) {
   using C = Cfg<true, kTileKDeep>;
   __shared__ __attribute__((aligned(16))) float ring[kDNS][2][kDSlot];
-  const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
+  const auto& P = prob_regs<EPI>(batch.p[find_prob(batch, blockIdx.x)]);
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
   const int i0 = ti * 256, j0 = tj * 256;
@@ -721,7 +815,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))
 gemm_f32_dma_syrk_kernel(GemmBatch batch) {
   using C = Cfg<false, kTileKSyrk>;
   __shared__ __attribute__((aligned(16))) float ring[kSNS][2][kSSlot];
-  const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
+  const auto& P = prob_regs<EPI_SYRK>(batch.p[find_prob(batch, blockIdx.x)]);
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
   const int i0 = ti * 128, j0 = tj * 128;

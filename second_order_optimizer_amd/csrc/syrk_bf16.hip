@@ -98,6 +98,24 @@ __device__ inline void band_tile(int t, int T, int H, int& ti, int& tj) {
   }
 }
 
+// A problem entry read once from the kernel arguments and kept in scalar
+// registers (see arg_reg).
+__device__ inline Prob prob_regs(const Prob& P) {
+  Prob q;
+  q.X = arg_reg(P.X);
+  q.F = arg_reg(P.F);
+  q.rows = arg_reg(P.rows);
+  q.width = arg_reg(P.width);
+  q.bias = arg_reg(P.bias);
+  q.ldf = arg_reg(P.ldf);
+  q.tiles = arg_reg(P.tiles);
+  q.blk_begin = arg_reg(P.blk_begin);
+  q.packed = arg_reg(P.packed);
+  q.alpha = arg_reg(P.alpha);
+  q.beta = arg_reg(P.beta);
+  return q;
+}
+
 __device__ inline int find_prob(const Batch& b, int blk) {
   int lo = 0, hi = b.n - 1;
   while (lo < hi) {
@@ -138,7 +156,7 @@ __device__ inline void store_t(unsigned short* __restrict__ s, const u16x8 (&v)[
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 syrk_bf16_kernel(Batch batch) {
   __shared__ __attribute__((aligned(16))) unsigned short sX[2][2][kBT * kLR];
-  const Prob& P = batch.p[find_prob(batch, blockIdx.x)];
+  const Prob P = prob_regs(batch.p[find_prob(batch, blockIdx.x)]);
   int t = blockIdx.x - P.blk_begin;
   int ti = 0;
   while (t >= P.tiles - ti) { t -= P.tiles - ti; ++ti; }
@@ -331,7 +349,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 syrk_bf16_dma_kernel(Batch batch) {
   __shared__ __attribute__((aligned(16))) unsigned short ring[kNS][2][kOpElems];
   const int blk = xcd_tile(blockIdx.x, gridDim.x, batch.xcd_run);
-  const Prob& P = batch.p[find_prob(batch, blk)];
+  const Prob P = prob_regs(batch.p[find_prob(batch, blk)]);
   int t = blk - P.blk_begin;
   int ti = 0, tj;
   if (batch.band > 0) {
