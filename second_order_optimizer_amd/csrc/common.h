@@ -39,6 +39,16 @@ __device__ inline T arg_reg(T v) {
   asm volatile("" : "+s"(v));
   return v;
 }
+// Pointers come from global-memory arguments: that is restated after the
+// register pin (which hides it), so that accesses through them stay global
+// loads and stores rather than flat ones (a flat load also holds up every
+// wait for LDS reads until it returns).
+template <typename T>
+__device__ inline T* arg_reg(T* v) {
+  uint64_t u = reinterpret_cast<uint64_t>(v);
+  asm volatile("" : "+s"(u));
+  return (T*)reinterpret_cast<__attribute__((address_space(1))) T*>(u);
+}
 
 // Packed upper-triangle storage of a symmetric d x d factor: element (i, j),
 // i <= j, at i d - i (i - 1) / 2 + (j - i) (rows of the upper triangle one

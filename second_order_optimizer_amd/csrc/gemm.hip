@@ -380,9 +380,7 @@ __device__ __forceinline__ void gemm_f32_body(const Batch& batch) {
   using C = Cfg<BIG, TK>;
   __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
   __shared__ __attribute__((aligned(16))) float sB[2][C::kSlab];
-  // (read in place: a register-held entry measured 25-40% slower here, in
-  // these kernels' latency-bound inverse launches)
-  const GemmProb& P = batch.p[find_prob(batch, blockIdx.x)];
+  const auto& P = prob_regs<EPI>(batch.p[find_prob(batch, blockIdx.x)]);
   int split, ti, tj;
   tile_coords(P, blockIdx.x - P.blk_begin, split, ti, tj);
   const int i0 = ti * C::kBT, j0 = tj * C::kBT;
