@@ -1022,11 +1022,28 @@ __global__ void __launch_bounds__(256) syrk_small_kernel(SmallSyrkTab T) {
   f32x16 acc[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) acc[s] = f32x16{};
+  // A lone workgroup waits out every dependent memory round trip (several
+  // microseconds each), so everything that does not depend on the contraction
+  // is requested at the start: the old factor entries of this wavefront's
+  // blocks (for the EMA) and the first two chunks of X, into two register
+  // sets that then alternate.
+  const bool rd = beta != 0.f;
+  float o[3][16];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int col = 32 * bb[s] + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * ba[s] + acc_row(r, lane);
+      const bool up = wid + 4 * s < nu && row <= col && col < d;
+      const int64_t f = !up ? 0 : packed ? packed_index(row, col, d) : static_cast<int64_t>(row) * d + col;
+      o[s][r] = rd ? F[f] : 0.f;
+    }
+  }
   // chunk loads: thread t takes column t % 128 of chunk rows t / 128 + 2 u
   constexpr int kPer = kSmallRows / 2;   // 32
   const int cc = tid & (kNb - 1), rr = tid >> 7;
-  float v[kPer];
-  auto load = [&](int r0) {
+  auto load = [&](float (&v)[kPer], int r0) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int r = r0 + rr + 2 * u;
@@ -1034,8 +1051,9 @@ __global__ void __launch_bounds__(256) syrk_small_kernel(SmallSyrkTab T) {
     }
   };
   const int nch = (rows + kSmallRows - 1) / kSmallRows;
-  load(0);
-  for (int ch = 0; ch < nch; ++ch) {
+  // chunk ch from register set v: into LDS, the set refilled with chunk ch + 2,
+  // then every row pair of the chunk (rows past the end are zero)
+  auto step = [&](float (&v)[kPer], int ch) {
     const int r0 = ch * kSmallRows;
     __syncthreads();   // the previous chunk is no longer read
     // columns up to the last 32-block: X, the bias column (1 on real rows), zeros
@@ -1046,8 +1064,7 @@ __global__ void __launch_bounds__(256) syrk_small_kernel(SmallSyrkTab T) {
       if (cc < 32 * nb) Xs[r * kSmallPitch + cc] = cc < w ? v[u] : one;
     }
     __syncthreads();
-    if (ch + 1 < nch) load(r0 + kSmallRows);
-    // every row pair of the chunk (rows past the end are zero)
+    if (ch + 2 < nch) load(v, r0 + 2 * kSmallRows);
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
       if (wid + 4 * s >= nu) continue;
@@ -1058,26 +1075,24 @@ __global__ void __launch_bounds__(256) syrk_small_kernel(SmallSyrkTab T) {
         acc[s] = mfma32(Xs[k * kSmallPitch + ca], Xs[k * kSmallPitch + cb], acc[s]);
       }
     }
+  };
+  float va[kPer], vb[kPer];
+  load(va, 0);
+  if (nch > 1) load(vb, kSmallRows);
+  for (int ch = 0; ch < nch; ch += 2) {
+    step(va, ch);
+    if (ch + 1 < nch) step(vb, ch + 1);
   }
-  // F <- beta F + alpha acc on the upper triangle; a block's reads issued together
-  const bool rd = beta != 0.f;
+  // F <- beta F + alpha acc on the upper triangle
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
     if (wid + 4 * s >= nu) continue;
     const int col = 32 * bb[s] + (lane & 31);
-    float o[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 32 * ba[s] + acc_row(r, lane);
-      const bool up = row <= col && col < d;
-      const int64_t f = !up ? 0 : packed ? packed_index(row, col, d) : static_cast<int64_t>(row) * d + col;
-      o[r] = rd ? F[f] : 0.f;
-    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * ba[s] + acc_row(r, lane);
       if (row > col || col >= d) continue;
-      const float x = rd ? beta * o[r] + alpha * acc[s][r] : alpha * acc[s][r];
+      const float x = rd ? beta * o[s][r] + alpha * acc[s][r] : alpha * acc[s][r];
       if (packed) {
         F[packed_index(row, col, d)] = x;
       } else {
