@@ -68,6 +68,7 @@ struct GemmProb {
 
 struct GemmScalars {
   float lr, momentum, weight_decay;
+  int32_t prio;   // nonzero: the launch's wavefronts raise their issue priority
   uint32_t* flags;
 };
 

@@ -376,6 +376,7 @@ __device__ __forceinline__ void gemm_epilogue(const Batch& batch, const GemmProb
 
 template <int AMODE, int BMODE, int EPI, bool BIG, typename Batch>
 __device__ __forceinline__ void gemm_f32_body(const Batch& batch) {
+  if (batch.sc.prio) __builtin_amdgcn_s_setprio(3);
   constexpr int TK = EPI == EPI_SYRK ? kTileKSyrk : kTileKDeep;
   using C = Cfg<BIG, TK>;
   __shared__ __attribute__((aligned(16))) float sA[2][C::kSlab];
@@ -585,6 +586,7 @@ __host__ __device__ inline uint64_t operand_extent(int64_t rows, int64_t ld, int
 template <int AMODE, int BMODE, int EPI, bool B16>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_f32_dma_kernel(GemmBatch batch) {
+  if (batch.sc.prio) __builtin_amdgcn_s_setprio(3);
   using C = Cfg<true, kTileKDeep>;
   __shared__ __attribute__((aligned(16))) float ring[kDNS][2][kDSlot];
   const auto& P = prob_regs<EPI>(batch.p[find_prob(batch, blockIdx.x)]);
