@@ -50,6 +50,23 @@ def test_fp32_linear_split_k(gpu_lib):
     lockstep(cfg, cfg.steps, TOL32, FULL_KEYS)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_single_workgroup_paths(gpu_lib, packed):
+    """Steps whose layers all fit one 128-block take one workgroup per factor
+    (factor SYRK and EMA), per factor (the whole inverse) and per layer
+    (preconditioning and update).  Edge cases of those kernels: d = 128
+    exactly (ten upper 32-blocks, three per wavefront), 300 rows (five 64-row
+    chunks, the last partial: chunk pairs and an odd count), an odd row
+    count in the last chunk (77 rows), exactly one chunk (64 rows), widths
+    that are not multiples of 32, several factors and layers per launch,
+    and packed factor storage."""
+    L = [synth.linear("full_block", 127, 128, 300, bias=True),
+         synth.linear("odd_rows", 33, 97, 77, bias=False),
+         synth.linear("one_chunk", 5, 3, 64, bias=True)]
+    cfg = with_layers(synth.full_config("fc64"), L, steps=3, act_std=1.0, grad_std=1e-2)
+    lockstep(cfg, cfg.steps, TOL32, FULL_KEYS, packed=packed)
+
+
 def test_bias_column_layers(gpu_lib):
     """Biased layers whose d_in is a whole number of 128-wide tiles: the
     preconditioning GEMMs cover the weight columns and the bias column is two
