@@ -979,8 +979,8 @@ kfac_status_t launch_sym_reduce(const std::vector<SymRedItem>& items, hipStream_
 // afterwards), and the bf16 factors on the bf16 SYRK.
 // Factor and EMA of fp32 linear-layer factors at most 128 wide, one
 // workgroup per factor: X (plus the bias layer's constant-1 column, 1 on real
-// rows only) goes through LDS in chunks of kSmallRows rows, the next chunk's
-// loads in flight while the current one is contracted; each wavefront owns
+// rows only) goes through LDS in chunks of kSmallRows rows, the loads of the
+// next two chunks in flight while one is contracted; each wavefront owns
 // whole upper 32-blocks of X^T X (at most 10, so 3 each) and runs every row
 // for them, so no partial sums are combined; then F <- beta F + alpha X^T X
 // on the upper triangle (mirrored, or packed).  Used when every factor of the
